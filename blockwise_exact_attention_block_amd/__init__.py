@@ -1,0 +1,254 @@
+"""Ring-ordered blockwise exact attention on MI355X (gfx950).
+
+Thin Python binding of libringattn.so (declared in include/ringattn.h). Every call
+only checks and marshals arguments; all arithmetic runs in the library's HIP
+kernels on the current torch stream. PyTorch provides device memory and streams.
+There is no fallback: if the library is missing, every call raises.
+
+Entry points (same names as the C ABI without the ``ra_`` prefix):
+  ring_schedule    ring visiting order of one query partition (host only)
+  ring_attn_fwd    ring prefill over P KV blocks, running state in registers
+  block_attn_step  merge one KV block into a running fp32 (O, LSE) state
+  lse_merge        two-way merge of normalised partials
+  lse_merge_n      n-way merge of normalised partials
+  splitkv_decode   split-KV (pass-Q) decode: partials per chunk + reduction
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Tuple
+
+import torch
+
+__all__ = [
+    "RingAttnError", "library_path", "load_library", "abi_version", "ring_schedule",
+    "ring_attn_fwd", "block_attn_step", "init_state", "lse_merge", "lse_merge_n",
+    "splitkv_decode",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libringattn.so"
+_ABI_VERSION = 1
+RA_F32, RA_BF16 = 0, 1
+_STATUS = {0: "RA_OK", 1: "RA_EINVAL", 2: "RA_EUNSUPPORTED", 3: "RA_EHIP"}
+_KIND = {0: "skip", 1: "diag", 2: "full"}
+
+_lib = None
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _hip_runtimes_mapped() -> List[str]:
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+        return sorted(os.path.realpath(p) for p in paths)
+    except OSError:
+        return []
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libringattn.so (after torch, so it binds to the HIP runtime torch
+    already mapped). Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RingAttnError(3, f"{path} is missing: build it with "
+                               "`python -m blockwise_exact_attention_block_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, ll, f, ip = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "ra_abi_version": ([], i),
+        "ra_last_error": ([], ctypes.c_char_p),
+        "ra_ring_schedule": ([i, i, i, ip, ip], i),
+        "ra_ring_attn_fwd": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp], i),
+        "ra_block_attn_step": ([i, vp, ll, i, vp, vp, ll, i, i, i, i, i, i, f, i, vp, vp, vp], i),
+        "ra_lse_merge": ([ll, i, vp, vp, vp, vp, vp, vp, vp], i),
+        "ra_lse_merge_n": ([i, ll, i, i, vp, vp, vp, vp, vp], i),
+        "ra_splitkv_decode": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if lib.ra_abi_version() != _ABI_VERSION:
+        raise RingAttnError(2, f"library ABI {lib.ra_abi_version()} != binding ABI {_ABI_VERSION}")
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RingAttnError(3, "two HIP runtimes are mapped in this process: " + ", ".join(runtimes))
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().ra_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().ra_last_error().decode(errors="replace")
+        raise RingAttnError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise RingAttnError(2, f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise RingAttnError(1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise RingAttnError(1, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
+    """[(kv_block, kind)] for the P ring steps of query partition i (host only)."""
+    lib = load_library()
+    n = max(int(P), 1)
+    kv = (ctypes.c_int * n)()
+    kind = (ctypes.c_int * n)()
+    r = lib.ra_ring_schedule(int(P), int(i), int(bool(causal)), kv, kind)
+    if r < 0:
+        _check(-r)
+    return [(kv[s], _KIND[kind[s]]) for s in range(r)]
+
+
+def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, causal: bool,
+                  scale: Optional[float] = None, q_part0: int = 0,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Ring prefill. q [B,Hq,nq*Sp,Dqk] holds query partitions q_part0..q_part0+nq-1;
+    k [B,Hkv,P*Sp,Dqk] and v [B,Hkv,P*Sp,Dv] hold all P KV blocks. Returns
+    (o [B,Hq,nq*Sp,Dv] in q's dtype, lse [B,Hq,nq*Sp] fp32)."""
+    lib = load_library()
+    B, Hq, Sq, Dqk = q.shape
+    Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if Skv % P:
+        raise RingAttnError(1, f"KV length {Skv} is not P={P} equal blocks")
+    Sp = Skv // P
+    if Sq % Sp:
+        raise RingAttnError(1, f"query length {Sq} is not a whole number of partitions of {Sp}")
+    nq = Sq // Sp
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype or lse.dtype != torch.float32:
+        raise RingAttnError(1, "q, k, v, out must share one dtype and lse must be fp32")
+    _check(lib.ra_ring_attn_fwd(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                _dev(lse, "lse"), B, Hq, Hkv, Sp, int(P), int(q_part0), nq, Dqk, Dv,
+                                float(scale), int(bool(causal)), _stream(q)))
+    return out, lse
+
+
+def init_state(q: torch.Tensor, Dv: int):
+    """Empty running state for block_attn_step: O = 0 (fp32), LSE = -inf."""
+    B, Hq, Sq, _ = q.shape
+    o = torch.zeros((B, Hq, Sq, Dv), dtype=torch.float32, device=q.device)
+    lse = torch.full((B, Hq, Sq), float("-inf"), dtype=torch.float32, device=q.device)
+    return o, lse
+
+
+def block_attn_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, o_acc: torch.Tensor,
+                    lse_acc: torch.Tensor, *, q_pos0: int, k_pos0: int, causal: bool,
+                    scale: Optional[float] = None) -> None:
+    """Merge one KV block (keys at k_pos0..) into the running fp32 state of the
+    queries at q_pos0.., in place."""
+    lib = load_library()
+    B, Hq, Sq, Dqk = q.shape
+    Hkv, Sk, Dv = k_blk.shape[1], k_blk.shape[2], v_blk.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
+        raise RingAttnError(1, "running state must be fp32")
+    if k_blk.dtype != q.dtype or v_blk.dtype != q.dtype:
+        raise RingAttnError(1, "q, k_blk, v_blk must share one dtype")
+    if tuple(o_acc.shape) != (B, Hq, Sq, Dv) or tuple(lse_acc.shape) != (B, Hq, Sq):
+        raise RingAttnError(1, "running state shape does not match q / v_blk")
+    _check(lib.ra_block_attn_step(_dtype_code(q), _dev(q, "q"), int(q_pos0), Sq, _dev(k_blk, "k_blk"),
+                                  _dev(v_blk, "v_blk"), int(k_pos0), Sk, B, Hq, Hkv, Dqk, Dv, float(scale),
+                                  int(bool(causal)), _dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"),
+                                  _stream(q)))
+
+
+def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None):
+    """Two-way merge of normalised fp32 partials; o_* [..., Dv], lse_* [...]."""
+    lib = load_library()
+    Dv = o_a.shape[-1]
+    rows = lse_a.numel()
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    for t in (o_a, lse_a, o_b, lse_b, out, lse_out):
+        if t.dtype != torch.float32:
+            raise RingAttnError(1, "lse_merge works on fp32 tensors")
+    if o_b.shape != o_a.shape or lse_b.shape != lse_a.shape or o_a.numel() != rows * Dv:
+        raise RingAttnError(1, "shape mismatch")
+    _check(lib.ra_lse_merge(rows, Dv, _dev(o_a, "o_a"), _dev(lse_a, "lse_a"), _dev(o_b, "o_b"),
+                            _dev(lse_b, "lse_b"), _dev(out, "out"), _dev(lse_out, "lse_out"), _stream(o_a)))
+    return out, lse_out
+
+
+def lse_merge_n(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torch.float32):
+    """n-way merge along the partial axis: o_parts [..., n, Dv], lse_parts [..., n]."""
+    lib = load_library()
+    n, Dv = o_parts.shape[-2], o_parts.shape[-1]
+    lead = tuple(o_parts.shape[:-2])
+    rows = int(math.prod(lead))
+    if tuple(lse_parts.shape) != lead + (n,):
+        raise RingAttnError(1, "lse_parts shape must be o_parts.shape[:-1]")
+    o = torch.empty(lead + (Dv,), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty(lead, dtype=torch.float32, device=o_parts.device)
+    _check(lib.ra_lse_merge_n(_dtype_code(o), rows, n, Dv, _dev(o_parts, "o_parts"),
+                              _dev(lse_parts, "lse_parts"), _dev(o, "o"), _dev(lse, "lse"), _stream(o_parts)))
+    return o, lse
+
+
+def splitkv_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_splits: int,
+                   scale: Optional[float] = None):
+    """One query token per sequence: q [B,Hq,D], caches [B,Hkv,L,D]. Returns
+    (o_part [B,Hq,n,D] fp32, lse_part [B,Hq,n] fp32, o [B,Hq,D] q.dtype, lse [B,Hq] fp32)."""
+    lib = load_library()
+    B, Hq, Dqk = q.shape
+    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    dev = q.device
+    o_part = torch.empty((B, Hq, n_splits, Dv), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, Hq, n_splits), dtype=torch.float32, device=dev)
+    o = torch.empty((B, Hq, Dv), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise RingAttnError(1, "q and the caches must share one dtype")
+    _check(lib.ra_splitkv_decode(_dtype_code(q), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                 _dev(v_cache, "v_cache"), B, Hq, Hkv, L, Dqk, Dv, int(n_splits), float(scale),
+                                 _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(o, "o"),
+                                 _dev(lse, "lse"), _stream(q)))
+    return o_part, lse_part, o, lse

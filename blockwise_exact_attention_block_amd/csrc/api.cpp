@@ -1,0 +1,231 @@
+// C ABI of libringattn.so: argument validation, kernel dispatch, per-thread error
+// messages, and the host-side ring schedule. Every function validates all of its
+// arguments before it enqueues anything, so an error return has launched nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ringattn.h"
+#include "common.hpp"
+
+namespace ra {
+hipError_t prefill_bf16(const PrefillArgs& a, int dqk, int dv, int step_mode, hipStream_t st);
+hipError_t prefill_f32(const PrefillArgs& a, int dqk, int dv, int step_mode, hipStream_t st);
+hipError_t lse_merge2(long long rows, int Dv, const float* o_a, const float* lse_a, const float* o_b,
+                      const float* lse_b, float* o_out, float* lse_out, hipStream_t st);
+hipError_t lse_merge_n(int out_bf16, long long rows, int n, int Dv, const float* o_parts,
+                       const float* lse_parts, void* o_out, float* lse_out, hipStream_t st);
+hipError_t decode_partial_bf16(const DecodeArgs& a, int d, hipStream_t st);
+}  // namespace ra
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return RA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bf16_dims_ok(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+}
+bool f32_dims_ok(int dqk, int dv) { return (dqk == 64 || dqk == 128) && (dv == 64 || dv == 128); }
+
+// a per-(batch, head) slab must be addressable with 32-bit byte offsets
+constexpr long long kMaxSlabBytes = 0x7fffffffLL;
+
+int check_common(int dtype, int B, int Hq, int Hkv, int Dqk, int Dv, float scale) {
+  if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EINVAL, "dtype must be RA_F32 or RA_BF16");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0) return fail(RA_EINVAL, "B, Hq, Hkv must be positive");
+  if (Hq % Hkv != 0) return fail(RA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Dqk <= 0 || Dv <= 0) return fail(RA_EINVAL, "head dims must be positive");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  const bool dims = dtype == RA_BF16 ? bf16_dims_ok(Dqk, Dv) : f32_dims_ok(Dqk, Dv);
+  if (!dims)
+    return fail(RA_EUNSUPPORTED, "no %s kernel for (Dqk, Dv) = (%d, %d)", dtype == RA_BF16 ? "bf16" : "fp32",
+                Dqk, Dv);
+  return RA_OK;
+}
+
+int check_slab(long long rows, int d, int esize, const char* name) {
+  if (rows * (long long)d * esize > kMaxSlabBytes)
+    return fail(RA_EUNSUPPORTED, "%s: a per-head slab of %lld rows x %d exceeds 2^31 bytes", name, rows, d);
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+
+int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind) {
+  if (P <= 0 || i < 0 || i >= P || !kv_block || !kind) {
+    fail(RA_EINVAL, "ra_ring_schedule: need P > 0, 0 <= i < P and non-null outputs");
+    return -RA_EINVAL;
+  }
+  for (int s = 0; s < P; ++s) {
+    const int j = ((i - s) % P + P) % P;
+    kv_block[s] = j;
+    kind[s] = !causal ? 2 : (j > i ? 0 : (j == i ? 1 : 2));
+  }
+  ok();
+  return P;
+}
+
+int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv, float scale,
+                     int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(RA_EINVAL, "ra_ring_attn_fwd: null pointer");
+  if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
+  if (Sp <= 0 || P <= 0 || nq <= 0) return fail(RA_EINVAL, "Sp, P, nq must be positive");
+  if (q_part0 < 0 || (long long)q_part0 + nq > P)
+    return fail(RA_EINVAL, "query partitions %d..%d outside the ring of %d", q_part0, q_part0 + nq - 1, P);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  const int es = dtype == RA_BF16 ? 2 : 4;
+  const long long kv_rows = (long long)P * Sp, q_rows = (long long)nq * Sp;
+  if (int r = check_slab(kv_rows, Dqk > Dv ? Dqk : Dv, es, "k/v")) return r;
+  if (int r = check_slab(q_rows, Dqk > Dv ? Dqk : Dv, es, "q/o")) return r;
+  ra::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.q_rows = (int)q_rows;
+  a.kv_rows = (int)kv_rows;
+  a.Sp = Sp;
+  a.P = P;
+  a.q_part0 = q_part0;
+  a.nq = nq;
+  a.scale_log2 = scale * ra::kLog2e;
+  a.causal = causal ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = dtype == RA_BF16 ? ra::prefill_bf16(a, Dqk, Dv, 0, st) : ra::prefill_f32(a, Dqk, Dv, 0, st);
+  return hip_status(e, "ra_ring_attn_fwd launch");
+}
+
+int ra_block_attn_step(int dtype, const void* q, long long q_pos0, int Sq, const void* k_blk, const void* v_blk,
+                       long long k_pos0, int Sk, int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal,
+                       float* o_acc, float* lse_acc, void* stream) {
+  if (!q || !k_blk || !v_blk || !o_acc || !lse_acc) return fail(RA_EINVAL, "ra_block_attn_step: null pointer");
+  if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
+  if (Sq <= 0 || Sk <= 0) return fail(RA_EINVAL, "Sq and Sk must be positive");
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(RA_EINVAL, "positions must be non-negative");
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_acc) || !aligned16(lse_acc))
+    return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  const int es = dtype == RA_BF16 ? 2 : 4;
+  if (int r = check_slab(Sk, Dqk > Dv ? Dqk : Dv, es, "k/v")) return r;
+  if (int r = check_slab(Sq, Dqk > Dv ? Dqk : Dv, 4, "q/o_acc")) return r;
+  ra::PrefillArgs a{};
+  a.q = q;
+  a.k = k_blk;
+  a.v = v_blk;
+  a.o_acc = o_acc;
+  a.lse_acc = lse_acc;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.q_rows = Sq;
+  a.kv_rows = Sk;
+  a.q_pos0 = q_pos0;
+  a.k_pos0 = k_pos0;
+  a.Sk = Sk;
+  a.nq = 1;
+  a.P = 1;
+  a.scale_log2 = scale * ra::kLog2e;
+  a.causal = causal ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = dtype == RA_BF16 ? ra::prefill_bf16(a, Dqk, Dv, 1, st) : ra::prefill_f32(a, Dqk, Dv, 1, st);
+  return hip_status(e, "ra_block_attn_step launch");
+}
+
+int ra_lse_merge(long long rows, int Dv, const float* o_a, const float* lse_a, const float* o_b,
+                 const float* lse_b, float* o_out, float* lse_out, void* stream) {
+  if (rows < 0 || Dv <= 0 || Dv % 4) return fail(RA_EINVAL, "need rows >= 0 and Dv a positive multiple of 4");
+  if (rows == 0) return ok();
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return fail(RA_EINVAL, "ra_lse_merge: null pointer");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return fail(RA_EINVAL, "o pointers must be 16-byte aligned");
+  return hip_status(ra::lse_merge2(rows, Dv, o_a, lse_a, o_b, lse_b, o_out, lse_out, (hipStream_t)stream),
+                    "ra_lse_merge launch");
+}
+
+int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_parts, const float* lse_parts,
+                   void* o_out, float* lse_out, void* stream) {
+  if (out_dtype != RA_F32 && out_dtype != RA_BF16) return fail(RA_EINVAL, "out_dtype must be RA_F32 or RA_BF16");
+  if (rows < 0 || n <= 0 || Dv <= 0 || Dv % 4) return fail(RA_EINVAL, "need rows >= 0, n > 0, Dv a positive multiple of 4");
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(RA_EINVAL, "ra_lse_merge_n: null pointer");
+  return hip_status(ra::lse_merge_n(out_dtype == RA_BF16, rows, n, Dv, o_parts, lse_parts, o_out, lse_out,
+                                    (hipStream_t)stream),
+                    "ra_lse_merge_n launch");
+}
+
+int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
+                      int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part, void* o,
+                      float* lse, void* stream) {
+  if (!q || !k_cache || !v_cache || !o_part || !lse_part || !o || !lse)
+    return fail(RA_EINVAL, "ra_splitkv_decode: null pointer");
+  if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EINVAL, "dtype must be RA_F32 or RA_BF16");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || n_splits <= 0 || Dqk <= 0 || Dv <= 0)
+    return fail(RA_EINVAL, "sizes must be positive");
+  if (Hq % Hkv != 0) return fail(RA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (L % n_splits != 0) return fail(RA_EINVAL, "L (%d) must divide into n_splits (%d) equal chunks", L, n_splits);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) || !aligned16(o))
+    return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (dtype != RA_BF16 || Dqk != Dv || (Dqk != 64 && Dqk != 128) || Hq / Hkv > 16)
+    return fail(RA_EUNSUPPORTED, "split-KV decode supports bf16 with Dqk == Dv in {64, 128} and Hq/Hkv <= 16");
+  if (int r = check_slab(L, Dqk, 2, "k/v cache")) return r;
+  ra::DecodeArgs a{};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k_cache;
+  a.v = (const __bf16*)v_cache;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.L = L;
+  a.n_splits = n_splits;
+  a.Ls = L / n_splits;
+  a.scale_log2 = scale * ra::kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = ra::decode_partial_bf16(a, Dqk, st);
+  if (e != hipSuccess) return hip_status(e, "ra_splitkv_decode partial launch");
+  e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse, st);
+  return hip_status(e, "ra_splitkv_decode merge launch");
+}
+
+}  // extern "C"

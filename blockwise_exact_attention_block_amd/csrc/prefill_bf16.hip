@@ -1,0 +1,401 @@
+// bf16 blockwise exact attention for gfx950 (MI355X): ring prefill and single ring
+// step, on v_mfma_f32_32x32x16_bf16.
+//
+// What is computed: for every query row, exact softmax(scale * q K^T) V over the
+// visible keys of a sequence of KV blocks, visited one block at a time. Each KV tile
+// updates the row's running maximum and exp-sum, rescales the output accumulator
+// and adds the tile's contribution, so the result is the one-shot softmax
+// (page "AI 推理系列（十一）：Ring Attention 如何让多张 GPU 共同计算一条超长序列",
+// §"最容易被忽略的细节：不同 Block 的 Attention 结果不能直接相加"). In ring mode the
+// blocks are taken in ring order, block (i - s) mod P at step s, with causal block
+// skipping and an element-wise mask on the diagonal block only (same page, §"KV 在
+// Ring 中如何流动"). In step mode the running state arrives as a normalised fp32
+// output plus LSE and leaves in the same form (page "LLM长文本推理Ring Attention环形
+// 注意力机制实现与优化", §Ring Attention实现代码与通信重叠).
+//
+// Data flow per workgroup (NW waves, each owning NQ x 32 query rows):
+//   * Q rows of the wave are loaded once into VGPRs as the B operand of
+//     S^T = K Q^T, so each lane owns one query column of the score tile and the row
+//     maximum / sum are in-lane plus one exchange with the lane 32 apart.
+//   * K and V tiles of BK = 64 keys go HBM -> VGPR (raw buffer loads, prefetched
+//     two tiles ahead) -> LDS (double buffered, rows padded against bank conflicts).
+//   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
+//     (converted to bf16, round to nearest even). V^T operands come from the
+//     natural [key][d] LDS tile through ds_read_b64_tr_b16, with the key order
+//     inside each 16-key step matching the accumulator's row order.
+//   * The output accumulator O^T keeps one query per lane column, so rescaling by
+//     the running-max correction is a per-lane multiply.
+#include "common.hpp"
+
+namespace ra {
+
+enum { MODE_RING = 0, MODE_STEP = 1 };
+
+template <int DQK, int DV, int NQ, int NW>
+struct PCfg {
+  static constexpr int BK = 64;                       // keys per tile
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
+  static constexpr int KCH = BK * DQK / 8 / THREADS;  // 16-byte K chunks per thread per tile
+  static constexpr int VCH = BK * DV / 8 / THREADS;
+  // LDS rows are padded so that each lane's reads are a per-lane base plus a
+  // compile-time offset, and 8 (K) / 4 (V, transposed reads) consecutive rows fall
+  // on distinct banks.
+  static constexpr int KS = DQK + 8;
+  static constexpr int VS = DV + 16;
+  static constexpr int K_TILE = BK * KS;
+  static constexpr int V_TILE = BK * VS;
+  static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
+  static constexpr int MT = DV / 32;                  // 32-row output tiles along D_v
+  static_assert(KCH * THREADS * 8 == BK * DQK && VCH * THREADS * 8 == BK * DV, "tile split");
+};
+
+struct TileRef {
+  int row0;        // first key row of the tile inside the (b, kv head) slab
+  long long pos0;  // global token position of that key
+  int nvalid;      // keys of the tile that exist (<= BK)
+};
+
+template <int DQK, int DV, int NQ, int NW, int MODE>
+__global__ void __launch_bounds__(NW * 64)
+prefill_bf16_kernel(PrefillArgs a) {
+  using C = PCfg<DQK, DV, NQ, NW>;
+  constexpr int BK = C::BK;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][C::K_TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][C::V_TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  // Workgroup -> (batch, head, query partition, query tile). Workgroups of one head
+  // are consecutive so that the ones in flight together stream the same K/V
+  // (L2 / Infinity Cache reuse); inside a head the heaviest causal tiles go first.
+  const int tiles_per_head = (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
+  const int bh = blockIdx.x / tiles_per_head;
+  const int gt = tiles_per_head - 1 - (int)(blockIdx.x % tiles_per_head);
+  const int b = bh / a.Hq;
+  const int hq = bh - b * a.Hq;
+  const int g = hq / a.group;
+  int part = 0, qt = gt;
+  if (MODE == MODE_RING) {
+    part = gt / a.n_qtiles;
+    qt = gt - part * a.n_qtiles;
+  }
+
+  int row_base, row_end;
+  long long pos_base;
+  if (MODE == MODE_RING) {
+    row_base = part * a.Sp + qt * C::BQ;
+    row_end = part * a.Sp + a.Sp;
+    pos_base = (long long)(a.q_part0 + part) * a.Sp + qt * C::BQ;
+  } else {
+    row_base = qt * C::BQ;
+    row_end = a.q_rows;
+    pos_base = a.q_pos0 + row_base;
+  }
+  const int last_row = min(row_base + C::BQ, row_end) - 1;
+  const long long last_pos = pos_base + (last_row - row_base);
+
+  // Per-(batch, head) slabs as raw buffers: rows past the slab read as zero.
+  const size_t kvh = (size_t)(b * a.Hkv + g) * a.kv_rows;
+  const auto qrs = make_rsrc((const __bf16*)a.q + (size_t)bh * a.q_rows * DQK,
+                             (unsigned)((size_t)a.q_rows * DQK * 2));
+  const auto krs = make_rsrc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
+  const auto vrs = make_rsrc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
+
+  // ---- tile schedule -------------------------------------------------------------
+  int ntiles, n_first = 0, n_full = 0, ring_i = 0;
+  if (MODE == MODE_RING) {
+    ring_i = a.q_part0 + part;
+    n_full = (a.Sp + BK - 1) / BK;
+    if (a.causal) {
+      // the own (diagonal) block first, then blocks i-1 .. 0; blocks after i hold
+      // only future keys and are skipped
+      n_first = (last_row - part * a.Sp) / BK + 1;
+      ntiles = n_first + ring_i * n_full;
+    } else {
+      ntiles = a.P * n_full;
+    }
+  } else {
+    long long kmax = a.Sk;
+    if (a.causal) kmax = min(kmax, last_pos - a.k_pos0 + 1);
+    if (kmax <= 0) return;  // no key of this block is visible: state stays as it is
+    ntiles = (int)((kmax + BK - 1) / BK);
+  }
+  auto tile_ref = [&](int n) -> TileRef {
+    TileRef t;
+    if (MODE == MODE_RING) {
+      int j, tt;
+      if (a.causal) {
+        if (n < n_first) {
+          j = ring_i;
+          tt = n;
+        } else {
+          const int r = n - n_first;
+          const int s = 1 + r / n_full;
+          j = ring_i - s;
+          tt = r - (s - 1) * n_full;
+        }
+      } else {
+        const int s = n / n_full;
+        tt = n - s * n_full;
+        j = ring_i - s;
+        if (j < 0) j += a.P;
+      }
+      t.row0 = j * a.Sp + tt * BK;
+      t.pos0 = (long long)j * a.Sp + tt * BK;
+      t.nvalid = min(BK, a.Sp - tt * BK);
+    } else {
+      t.row0 = n * BK;
+      t.pos0 = a.k_pos0 + (long long)n * BK;
+      t.nvalid = min(BK, a.Sk - n * BK);
+    }
+    return t;
+  };
+
+  // ---- global -> register -> LDS staging ---------------------------------------
+  uint4 kr[C::KCH], vr[C::VCH];
+  auto load_tile = [&](int n) {
+    const TileRef t = tile_ref(n);
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int c = it * C::THREADS + tid;
+      const int row = c / (DQK / 8), col = c % (DQK / 8);
+      kr[it] = buf_load16(krs, (unsigned)((t.row0 + row) * DQK + col * 8) * 2u);
+    }
+#pragma unroll
+    for (int it = 0; it < C::VCH; ++it) {
+      const int c = it * C::THREADS + tid;
+      const int row = c / (DV / 8), col = c % (DV / 8);
+      vr[it] = buf_load16(vrs, (unsigned)((t.row0 + row) * DV + col * 8) * 2u);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int c = it * C::THREADS + tid;
+      const int row = c / (DQK / 8), col = c % (DQK / 8);
+      *(uint4*)&ks[buf][row * C::KS + col * 8] = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VCH; ++it) {
+      const int c = it * C::THREADS + tid;
+      const int row = c / (DV / 8), col = c % (DV / 8);
+      *(uint4*)&vs[buf][row * C::VS + col * 8] = vr[it];
+    }
+  };
+
+  // ---- stationary Q fragments and running state --------------------------------
+  const int wave_row0 = row_base + wave * NQ * 32;
+  const long long wave_pos0 = pos_base + wave * NQ * 32;
+  bf16x8 qf[NQ][C::DS];
+  float m[NQ], l[NQ];
+  f32x16 oacc[NQ][C::MT];
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    const int row = wave_row0 + nq * 32 + l32;
+    const bool valid = row < row_end;
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      qf[nq][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(row * DQK + 16 * s + 8 * h) * 2u));
+      // Keep the stationary Q fragments in AGPRs: MFMA reads its B operand from
+      // there directly, which leaves the VGPRs to the softmax working set.
+      asm volatile("" : "+a"(qf[nq][s]));
+    }
+    m[nq] = kNegInf;
+    l[nq] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) oacc[nq][mt] = f32x16{};
+    if (MODE == MODE_STEP && valid) {
+      // running state (O normalised, LSE) is the online state with m = LSE, l = 1
+      const size_t r = (size_t)bh * a.q_rows + row;
+      const float lin = a.lse_acc[r];
+      if (lin != kNegInf) {
+        m[nq] = lin * kLog2e;
+        l[nq] = h == 0 ? 1.f : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = *(const f32x4*)(a.o_acc + r * DV + 32 * mt + 8 * g4 + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[nq][mt][4 * g4 + e] = x[e];
+          }
+      }
+    }
+  }
+
+  // ---- one KV tile, consumed as BK/32 sub-tiles of 32 keys ----------------------
+  // Each sub-tile is a full online-softmax update (max, rescale, exp-sum, PV), which
+  // keeps only 32 keys of scores and probabilities live per query column.
+  const int gg = lane >> 4, L = lane & 15;
+  auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) {
+#pragma unroll
+    for (int kt = 0; kt < BK / 32; ++kt) {
+      f32x16 sacc[NQ];
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) sacc[nq] = f32x16{};
+      const int krow = kt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        const bf16x8 ka = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h];
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) sacc[nq] = mfma32(ka, qf[nq][s], sacc[nq]);
+      }
+      bf16x8 pb[NQ][2];
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) {
+        if (need_mask) {
+          // last visible key of the sub-tile for this lane's query, minus the lane's
+          // 4*h row offset, so each element compares a compile-time key offset
+          int lim = t.nvalid - 1 - kt * 32;
+          if (a.causal) {
+            const long long rel = wave_pos0 + nq * 32 + l32 - (t.pos0 + kt * 32);
+            lim = (int)min((long long)lim, max(rel, -1LL));
+          }
+          lim -= 4 * h;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key_off = 8 * (i >> 2) + (i & 3);
+            sacc[nq][i] = key_off <= lim ? sacc[nq][i] : kNegInf;
+          }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nq][i]);
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mnew = fmaxf(m[nq], mx * a.scale_log2);
+        const float muse = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = exp2_hw(m[nq] - muse);
+        m[nq] = mnew;
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_hw(fmaf(sacc[nq][i], a.scale_log2, -muse));
+          sacc[nq][i] = p;
+          rs += p;
+        }
+        l[nq] = l[nq] * alpha + rs;
+        // alpha is exactly 1 unless this lane's running max grew: skip the rescale
+        // when that holds for the whole wave
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) oacc[nq][mt] *= alpha;
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          f32x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = sacc[nq][8 * t2 + e];
+          pb[nq][t2] = to_bf16x8(x);
+        }
+      }
+      // O^T += V^T P^T over the sub-tile's two 16-key MFMA steps. Step t2 holds,
+      // in lane half h, keys 16*t2 + 4*h + {0..3} and 16*t2 + 8 + 4*h + {0..3}
+      // (the accumulator rows of S^T). 16-lane group gg reads those keys for
+      // columns 32*mt + 16*(gg%2) + 0..15 of the V tile, transposed.
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x4 half2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            half2[x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
+          }
+          const bf16x8 va = cat(half2[0], half2[1]);
+#pragma unroll
+          for (int nq = 0; nq < NQ; ++nq) oacc[nq][mt] = mfma32(va, pb[nq][t2], oacc[nq][mt]);
+        }
+      }
+    }
+  };
+
+  // ---- pipelined tile loop -------------------------------------------------------
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (ntiles > 1) load_tile(1);
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    const TileRef t = tile_ref(n);
+    const long long wave_pos1 = wave_pos0 + NQ * 32 - 1;
+    const bool skip = a.causal && t.pos0 > wave_pos1;
+    const bool need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
+    if (!skip) compute_tile(buf, t, need_mask);
+    // the output accumulators live in AGPRs across iterations (MFMA reads and
+    // writes them there; only the rare rescale touches them with VALU)
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) asm volatile("" : "+a"(oacc[nq][mt]));
+    if (n + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      if (n + 2 < ntiles) load_tile(n + 2);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ------------------------------------------------------------------
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    const float lt = l[nq] + shfl_xor_f(l[nq], 32);
+    const int row = wave_row0 + nq * 32 + l32;
+    if (row < row_end) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? (m[nq] + log2_hw(lt)) * kLn2 : kNegInf;
+      const size_t r = (size_t)bh * a.q_rows + row;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[nq][mt][4 * g4 + e] * inv;
+          const int d = 32 * mt + 8 * g4 + 4 * h;
+          if (MODE == MODE_RING)
+            *(bf16x4*)((__bf16*)a.o + r * DV + d) = to_bf16x4(x);
+          else
+            *(f32x4*)(a.o_acc + r * DV + d) = x;
+        }
+      if (h == 0) {
+        if (MODE == MODE_RING)
+          a.lse[r] = lse;
+        else
+          a.lse_acc[r] = lse;
+      }
+    }
+  }
+}
+
+template <int DQK, int DV, int MODE>
+static hipError_t launch_one(PrefillArgs a, hipStream_t st) {
+  constexpr int NQ = 2, NW = 4;
+  using C = PCfg<DQK, DV, NQ, NW>;
+  int rows_per_part = MODE == MODE_RING ? a.Sp : a.q_rows;
+  a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;
+  const long long tiles = (long long)a.B * a.Hq * (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE>), dim3((unsigned)tiles),
+                     dim3(C::THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+// Returns hipErrorInvalidValue when no kernel instance covers (dqk, dv).
+hipError_t prefill_bf16(const PrefillArgs& a, int dqk, int dv, int step_mode, hipStream_t st) {
+  if (dqk == 128 && dv == 128)
+    return step_mode ? launch_one<128, 128, MODE_STEP>(a, st) : launch_one<128, 128, MODE_RING>(a, st);
+  if (dqk == 64 && dv == 64)
+    return step_mode ? launch_one<64, 64, MODE_STEP>(a, st) : launch_one<64, 64, MODE_RING>(a, st);
+  if (dqk == 192 && dv == 128)
+    return step_mode ? launch_one<192, 128, MODE_STEP>(a, st) : launch_one<192, 128, MODE_RING>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

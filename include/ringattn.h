@@ -1,0 +1,150 @@
+/*
+ * ringattn.h — C ABI of the MI355X (gfx950) ring-ordered blockwise exact attention
+ * library (libringattn.so).
+ *
+ * What it computes. For a query block and a sequence of KV blocks, exact
+ * O = softmax(scale * Q K^T) V and the per-row log-sum-exp of the scaled scores,
+ * built one KV block at a time: each block updates a per-row running maximum and
+ * exp-sum, rescales the output accumulator and merges the block's contribution,
+ * so the result equals one-shot attention.
+ *   [RING] page "AI 推理系列（十一）：Ring Attention 如何让多张 GPU 共同计算一条超长序列",
+ *          §"KV 在 Ring 中如何流动" (ring order) and §"最容易被忽略的细节：不同 Block 的
+ *          Attention 结果不能直接相加" (running max / sum / rescale / merge).
+ *   [IMPL] page "LLM长文本推理Ring Attention环形注意力机制实现与优化",
+ *          §"Ring Attention实现代码与通信重叠" (lse state, initial out = 0, lse = -inf,
+ *          the rescale weights of the old output and the block output).
+ *   [CH]   page "长上下文的第一性挑战", §挑战 1 eq. lc-ch-attention (definition),
+ *          §KV 是 Decode 阶段的隐性瓶颈 (decode reads the whole KV cache once).
+ *   [CPEV] page "上下文并行 (CP) 收益评估实验设计", §名词定义 (pass-KV / pass-Q) and
+ *          §Decode (partial attention on every KV shard, then a reduction).
+ *
+ * Conventions shared by every call.
+ *   - Tensors are dense, contiguous, row-major "BHSD": batch, head, sequence,
+ *     head-dim (innermost). LSE tensors are [B, H, S] fp32 (natural log, scale
+ *     included). Pointers marked "device" are HIP device memory owned by the
+ *     caller; the library never allocates, frees or synchronises.
+ *   - dtype: RA_F32 (fp32 in, fp32 arithmetic) or RA_BF16 (bf16 in, fp32
+ *     accumulation, softmax probabilities rounded to bf16 for the PV product,
+ *     outputs rounded to nearest-even bf16).
+ *   - Causal visibility uses global token positions: a key is visible to a query
+ *     iff key_pos <= query_pos.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - A query with no visible key gets O = 0 and LSE = -inf.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. Work is
+ *     enqueued asynchronously on it; results are valid once the stream has been
+ *     synchronised.
+ *   - Return value: RA_OK, or an error code with a message in ra_last_error().
+ *     No call throws. Arguments are validated before anything is enqueued, so an
+ *     error return has enqueued no work.
+ *   - The library keeps no state between calls apart from the per-thread error
+ *     message; calls are reentrant.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_ABI_VERSION 1
+
+typedef enum {
+  RA_OK = 0,
+  RA_EINVAL = 1,        /* null pointer, bad size, inconsistent shapes, misalignment */
+  RA_EUNSUPPORTED = 2,  /* valid request this build has no kernel for (dtype/head dims) */
+  RA_EHIP = 3           /* the HIP runtime reported an error at launch */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* ABI version of the loaded library (RA_ABI_VERSION of the headers it was built with). */
+int ra_abi_version(void);
+
+/* Message for the last non-OK return on the calling thread ("" if none). The pointer
+ * stays valid until the next library call on the same thread. */
+const char* ra_last_error(void);
+
+/* Host only, no GPU. Ring visiting order of query partition i in a ring of P
+ * partitions ([RING] §"KV 在 Ring 中如何流动"): at step s the partition works on KV
+ * block kv_block[s] = (i - s) mod P. kind[s] is 0 = skip (causal and the block lies
+ * wholly after partition i), 1 = diagonal (causal, own block, masked elementwise),
+ * 2 = full. kv_block and kind are host arrays of at least P ints.
+ * Returns P, or -RA_EINVAL on bad arguments. */
+int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind);
+
+/* Ring prefill for nq consecutive query partitions, all in one launch.
+ * The sequence has P * Sp tokens cut into P contiguous partitions of Sp tokens.
+ *   q   device [B, Hq,  nq*Sp, Dqk]  queries of partitions q_part0 .. q_part0+nq-1
+ *   k   device [B, Hkv, P*Sp,  Dqk]  all P KV blocks (block j = tokens j*Sp ..)
+ *   v   device [B, Hkv, P*Sp,  Dv ]
+ *   o   device [B, Hq,  nq*Sp, Dv ]  output, same dtype as q
+ *   lse device [B, Hq,  nq*Sp] fp32  output
+ * Each query partition i visits KV blocks in the order of ra_ring_schedule(P, i,
+ * causal), skipping "skip" blocks and masking the diagonal one; the running state
+ * stays in registers across the blocks.
+ * Supported head dims: RA_BF16 (Dqk, Dv) in {(64,64), (128,128), (192,128)};
+ * RA_F32 Dqk, Dv in {64, 128}. scale must be finite and > 0.
+ * Errors: RA_EINVAL for null pointers, non-positive sizes, Hq % Hkv != 0,
+ * q_part0 + nq > P, pointers not 16-byte aligned; RA_EUNSUPPORTED for other head
+ * dims or a per-head slab of 2^31 elements or more. */
+int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
+                     float scale, int causal, void* stream);
+
+/* One ring step: merge one KV block into a running fp32 state ([IMPL] §Ring
+ * Attention实现代码与通信重叠; [RING] §最容易被忽略的细节).
+ *   q       device [B, Hq,  Sq, Dqk]  queries at global positions q_pos0 .. q_pos0+Sq-1
+ *   k_blk   device [B, Hkv, Sk, Dqk]  keys at global positions k_pos0 .. k_pos0+Sk-1
+ *   v_blk   device [B, Hkv, Sk, Dv ]
+ *   o_acc   device [B, Hq,  Sq, Dv ] fp32, normalised running output (in/out)
+ *   lse_acc device [B, Hq,  Sq] fp32, running log-sum-exp (in/out)
+ * Start from o_acc = 0, lse_acc = -inf. After the call the state equals the merge
+ * of the old state with exact attention over this block. A block with no visible
+ * key for any query leaves the state untouched. Head-dim support and errors as
+ * ra_ring_attn_fwd. o_acc/lse_acc must not overlap q, k_blk or v_blk. */
+int ra_block_attn_step(int dtype, const void* q, long long q_pos0, int Sq,
+                       const void* k_blk, const void* v_blk, long long k_pos0, int Sk,
+                       int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal,
+                       float* o_acc, float* lse_acc, void* stream);
+
+/* Two-way merge of normalised partial results over disjoint key sets, per row:
+ * L = log(e^{La} + e^{Lb}); O = e^{La-L} O_a + e^{Lb-L} O_b. A side with -inf
+ * LSE contributes nothing; two empty sides give O = 0, L = -inf.
+ *   o_a, o_b, o_out  device [rows, Dv] fp32;  lse_a, lse_b, lse_out device [rows] fp32.
+ * o_out/lse_out may alias o_a/lse_a (or o_b/lse_b) exactly; other overlaps are
+ * undefined. Errors: RA_EINVAL for null pointers, rows < 0, Dv <= 0, Dv % 4 != 0,
+ * pointers not 16-byte aligned. rows == 0 is a no-op. */
+int ra_lse_merge(long long rows, int Dv, const float* o_a, const float* lse_a,
+                 const float* o_b, const float* lse_b, float* o_out, float* lse_out, void* stream);
+
+/* n-way reduction of partials, the pass-Q reduce ([CPEV] §Decode).
+ *   o_parts   device [rows, n, Dv] fp32 normalised partial outputs
+ *   lse_parts device [rows, n] fp32
+ *   o_out     device [rows, Dv] in out_dtype (RA_F32 or RA_BF16)
+ *   lse_out   device [rows] fp32
+ * Errors: RA_EINVAL for null pointers, rows < 0, n <= 0, Dv <= 0, Dv % 4 != 0. */
+int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_parts,
+                   const float* lse_parts, void* o_out, float* lse_out, void* stream);
+
+/* Split-KV decode: one new query token per sequence attends to its whole KV cache
+ * (no mask: every cached key precedes it). The cache is cut into n_splits
+ * contiguous chunks of L / n_splits keys; each chunk yields a partial (O_p, LSE_p),
+ * then an LSE-weighted reduction gives the result ([CPEV] §名词定义 pass-Q;
+ * [CH] §KV 是 Decode 阶段的隐性瓶颈).
+ *   q        device [B, Hq, Dqk]
+ *   k_cache  device [B, Hkv, L, Dqk]
+ *   v_cache  device [B, Hkv, L, Dv]
+ *   o_part   device [B, Hq, n_splits, Dv] fp32  output (partials)
+ *   lse_part device [B, Hq, n_splits] fp32      output
+ *   o        device [B, Hq, Dv] dtype of q       output
+ *   lse      device [B, Hq] fp32                 output
+ * Supported: RA_BF16 with Dqk = Dv = 128 and Hq / Hkv <= 16; RA_F32 with
+ * Dqk, Dv in {64, 128}. Errors: RA_EINVAL also when L % n_splits != 0. */
+int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                      int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                      float* o_part, float* lse_part, void* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RINGATTN_H */

@@ -1,0 +1,248 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle, element by element,
+at sizes that span several tiles and ragged tails, plus the degenerate cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, prefill_inputs_np, randn_np
+from gpu_util import assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import blockwise_exact_attention_block_amd as m
+    m.load_library()
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return m
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype).contiguous()
+
+
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def ring_case(ra, *, dtype, B, Hq, Hkv, Sp, P, Dqk, Dv, causal, q_part0=0, nq=None, seed=0):
+    nq = P if nq is None else nq
+    say(f"ring_attn_fwd {dtype} B{B} Hq{Hq} Hkv{Hkv} Sp{Sp} P{P} D{Dqk}/{Dv} causal={causal} "
+        f"parts {q_part0}..{q_part0 + nq - 1} seed {seed}")
+    S = P * Sp
+    q_all, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, Dqk, Dv, seed=seed, dtype=dtype)
+    q = q_all[:, :, q_part0 * Sp:(q_part0 + nq) * Sp]
+    scale = 1.0 / math.sqrt(Dqk)
+    o, lse = ra.ring_attn_fwd(to_dev(q, TD[dtype]), to_dev(k, TD[dtype]), to_dev(v, TD[dtype]),
+                              P=P, causal=causal, scale=scale, q_part0=q_part0)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, scale=scale, causal=causal, q_pos0=q_part0 * Sp, k_pos0=0)
+    return assert_close(np64(o), np64(lse), o_ref, l_ref, dtype, "ring_attn_fwd")
+
+
+# ------------------------------------------------------------------------------ fp32
+
+def test_fp32_c1_all_rows(ra):
+    c = CONFIGS["C1"]
+    ring_case(ra, dtype="f32", B=c.B, Hq=c.Hq, Hkv=c.Hkv, Sp=c.Sp, P=c.P, Dqk=c.Dqk, Dv=c.Dv,
+              causal=c.causal, seed=c.seed)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sp,P", [(37, 3), (100, 1), (65, 2)])
+def test_fp32_ring_ragged(ra, dims, causal, Sp, P):
+    ring_case(ra, dtype="f32", B=2, Hq=4, Hkv=2, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+              seed=11 + Sp + P)
+
+
+# ------------------------------------------------------------------------------ bf16
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sp,P", [(300, 3), (513, 1), (256, 2)])
+def test_bf16_ring_ragged(ra, dims, causal, Sp, P):
+    ring_case(ra, dtype="bf16", B=2, Hq=4, Hkv=2, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+              seed=21 + Sp + P)
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+def test_bf16_one_partition_share(ra, dims):
+    """One device's share: only the last query partition, all KV blocks (the shape of
+    the MLA-like configuration, scaled down)."""
+    ring_case(ra, dtype="bf16", B=1, Hq=4, Hkv=4, Sp=700, P=4, Dqk=dims[0], Dv=dims[1], causal=True,
+              q_part0=3, nq=1, seed=5)
+
+
+def test_bf16_gqa_group8(ra):
+    ring_case(ra, dtype="bf16", B=1, Hq=16, Hkv=2, Sp=384, P=4, Dqk=128, Dv=128, causal=True, seed=8)
+
+
+def test_single_token_partitions(ra):
+    ring_case(ra, dtype="bf16", B=1, Hq=2, Hkv=1, Sp=1, P=5, Dqk=128, Dv=128, causal=True, seed=9)
+    ring_case(ra, dtype="f32", B=1, Hq=2, Hkv=1, Sp=1, P=5, Dqk=64, Dv=64, causal=True, seed=9)
+
+
+def test_c2_all_rows(ra):
+    c = CONFIGS["C2"]
+    ring_case(ra, dtype="bf16", B=c.B, Hq=c.Hq, Hkv=c.Hkv, Sp=c.Sp, P=c.P, Dqk=c.Dqk, Dv=c.Dv,
+              causal=c.causal, seed=c.seed)
+
+
+def test_deterministic(ra):
+    q, k, v = (to_dev(x, torch.bfloat16) for x in prefill_inputs_np(1, 8, 2, 2048, 2048, 128, 128, seed=3,
+                                                                       dtype="bf16"))
+    o1, l1 = ra.ring_attn_fwd(q, k, v, P=4, causal=True)
+    o2, l2 = ra.ring_attn_fwd(q, k, v, P=4, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_equals_repeated_kv_heads(ra):
+    q, k, v = (to_dev(x, torch.bfloat16) for x in prefill_inputs_np(1, 8, 2, 1024, 1024, 128, 128, seed=4,
+                                                                       dtype="bf16"))
+    o1, l1 = ra.ring_attn_fwd(q, k, v, P=2, causal=True)
+    o2, l2 = ra.ring_attn_fwd(q, k.repeat_interleave(4, dim=1).contiguous(),
+                              v.repeat_interleave(4, dim=1).contiguous(), P=2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_one_partition_ring_equals_plain_and_split(ra):
+    """A ring of one partition is plain attention; cutting the same sequence into 4
+    partitions must reach the same result within rounding."""
+    q, k, v = prefill_inputs_np(1, 4, 4, 1536, 1536, 128, 128, seed=6, dtype="bf16")
+    dq, dk, dv = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    o1, l1 = ra.ring_attn_fwd(dq, dk, dv, P=1, causal=True)
+    o4, l4 = ra.ring_attn_fwd(dq, dk, dv, P=4, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, scale=1 / math.sqrt(128), causal=True)
+    assert_close(np64(o1), np64(l1), o_ref, l_ref, "bf16", "P=1")
+    assert_close(np64(o4), np64(l4), o_ref, l_ref, "bf16", "P=4")
+    assert float((o1.float() - o4.float()).abs().max()) <= 2e-2
+
+
+# ------------------------------------------------------------------------------ step API
+
+@pytest.mark.parametrize("dtype,dims", [("bf16", (128, 128)), ("bf16", (192, 128)), ("f32", (64, 64))])
+@pytest.mark.parametrize("causal", [False, True])
+def test_step_chain_equals_ring_and_oracle(ra, dtype, dims, causal):
+    """P chained block steps in ring order give the ring result and the oracle's."""
+    B, Hq, Hkv, Sp, P = 1, 4, 2, 200, 4
+    Dqk, Dv = dims
+    S = Sp * P
+    say(f"block_attn_step chain {dtype} D{Dqk}/{Dv} causal={causal}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, Dqk, Dv, seed=31, dtype=dtype)
+    dq, dk, dv = (to_dev(x, TD[dtype]) for x in (q, k, v))
+    o_ring, l_ring = ra.ring_attn_fwd(dq, dk, dv, P=P, causal=causal)
+    o_ref, l_ref = oracle.attention(q, k, v, scale=1 / math.sqrt(Dqk), causal=causal)
+    for i in range(P):
+        qi = dq[:, :, i * Sp:(i + 1) * Sp].contiguous()
+        o_acc, l_acc = ra.init_state(qi, Dv)
+        for j, kind in ra.ring_schedule(P, i, causal):
+            if kind == "skip":
+                continue
+            ra.block_attn_step(qi, dk[:, :, j * Sp:(j + 1) * Sp].contiguous(), dv[:, :, j * Sp:(j + 1) * Sp].contiguous(),
+                               o_acc, l_acc, q_pos0=i * Sp, k_pos0=j * Sp, causal=causal)
+        torch.cuda.synchronize()
+        sl = slice(i * Sp, (i + 1) * Sp)
+        assert_close(np64(o_acc), np64(l_acc), o_ref[:, :, sl], l_ref[:, :, sl], dtype, f"chain part {i}")
+        tol = 2e-2 if dtype == "bf16" else 1e-4
+        assert float((o_acc - o_ring[:, :, sl].float()).abs().max()) <= tol
+        assert float((l_acc - l_ring[:, :, sl]).abs().max()) <= (1e-2 if dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_fully_masked_block_is_a_noop(ra, dtype):
+    B, Hq, Sq, Sk, D = 1, 2, 100, 64, 64 if dtype == "f32" else 128
+    q, k, v = prefill_inputs_np(B, Hq, Hq, Sq, Sk, D, D, seed=41, dtype=dtype)
+    dq, dk, dv = (to_dev(x, TD[dtype]) for x in (q, k, v))
+    o_acc = to_dev(randn_np((B, Hq, Sq, D), 42), torch.float32)
+    l_acc = to_dev(randn_np((B, Hq, Sq), 43), torch.float32)
+    o0, l0 = o_acc.clone(), l_acc.clone()
+    ra.block_attn_step(dq, dk, dv, o_acc, l_acc, q_pos0=0, k_pos0=Sq, causal=True)   # keys all in the future
+    torch.cuda.synchronize()
+    assert torch.equal(o_acc, o0) and torch.equal(l_acc, l0)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("bf16", 64)])
+def test_step_partial_overlap_positions(ra, dtype, D):
+    """Arbitrary query/key positions: the block's keys straddle the queries, so the
+    mask cuts through tiles; the incoming state is a genuine partial result."""
+    B, Hq, Hkv, Sq, Sk = 2, 4, 1, 177, 150
+    q_pos0, k_pos0 = 100, 37
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, D, seed=51, dtype=dtype)
+    k0, v0 = randn_np((B, Hkv, 30, D), 52, dtype), randn_np((B, Hkv, 30, D), 53, dtype)
+    o_a, l_a = oracle.attention(q, k0, v0, scale=1 / math.sqrt(D), causal=True, q_pos0=q_pos0, k_pos0=0)
+    o_b, l_b = oracle.attention(q, k, v, scale=1 / math.sqrt(D), causal=True, q_pos0=q_pos0, k_pos0=k_pos0)
+    o_ref, l_ref = oracle.merge(o_a, l_a, o_b, l_b)
+    o_acc = to_dev(o_a.astype(np.float32), torch.float32)
+    l_acc = to_dev(l_a.astype(np.float32), torch.float32)
+    ra.block_attn_step(to_dev(q, TD[dtype]), to_dev(k, TD[dtype]), to_dev(v, TD[dtype]), o_acc, l_acc,
+                       q_pos0=q_pos0, k_pos0=k_pos0, causal=True)
+    torch.cuda.synchronize()
+    assert_close(np64(o_acc), np64(l_acc), o_ref, l_ref, dtype, "step partial")
+
+
+# ------------------------------------------------------------------------------ merges
+
+@pytest.mark.parametrize("alias", [False, True])
+def test_lse_merge(ra, alias):
+    rows, Dv = 3001, 128
+    rng = np.random.default_rng(61)
+    o_a = rng.standard_normal((rows, Dv)).astype(np.float32)
+    o_b = rng.standard_normal((rows, Dv)).astype(np.float32)
+    l_a = (rng.standard_normal(rows) * 30).astype(np.float32)
+    l_b = (rng.standard_normal(rows) * 30).astype(np.float32)
+    l_a[::7] = -np.inf
+    l_b[::11] = -np.inf
+    o_a[::7] = 0
+    o_b[::11] = 0
+    o_ref, l_ref = oracle.merge(o_a, l_a, o_b, l_b)
+    da, dla, db, dlb = (to_dev(x, torch.float32) for x in (o_a, l_a, o_b, l_b))
+    if alias:
+        o, l = ra.lse_merge(da, dla, db, dlb, out=da, lse_out=dla)
+        assert o.data_ptr() == da.data_ptr()
+    else:
+        o, l = ra.lse_merge(da, dla, db, dlb)
+    torch.cuda.synchronize()
+    assert_close(np64(o), np64(l), o_ref, l_ref, "f32", "lse_merge")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge_n(ra, out_dtype):
+    rows, n, Dv = 517, 8, 128
+    rng = np.random.default_rng(62)
+    op = rng.standard_normal((rows, n, Dv)).astype(np.float32)
+    lp = (rng.standard_normal((rows, n)) * 5).astype(np.float32)
+    lp[::5, 3] = -np.inf
+    lp[7, :] = -np.inf
+    op[7] = 0
+    o_ref, l_ref = oracle.merge_n(op, lp)
+    o, l = ra.lse_merge_n(to_dev(op, torch.float32), to_dev(lp, torch.float32), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert_close(np64(o), np64(l), o_ref, l_ref, "f32" if out_dtype == torch.float32 else "bf16", "merge_n")
+
+
+# ------------------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (8, 8), (12, 3)])
+@pytest.mark.parametrize("L,n", [(768, 1), (768, 3), (768, 8), (1000, 8)])
+def test_splitkv_decode_small(ra, D, Hq, Hkv, L, n):
+    B = 2
+    say(f"splitkv_decode B{B} Hq{Hq} Hkv{Hkv} L{L} n{n} D{D}")
+    q = randn_np((B, Hq, D), 71, "bf16")
+    k = randn_np((B, Hkv, L, D), 72, "bf16")
+    v = randn_np((B, Hkv, L, D), 73, "bf16")
+    op, lp, o, l = ra.splitkv_decode(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                                     to_dev(v, torch.bfloat16), n_splits=n)
+    torch.cuda.synchronize()
+    op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
+    assert_close(np64(op), np64(lp), op_r, lp_r, "bf16", "decode partials")
+    assert_close(np64(o), np64(l), o_r, l_r, "bf16", "decode merged")
