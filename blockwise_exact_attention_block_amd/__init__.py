@@ -11,6 +11,7 @@ Entry points (same names as the C ABI without the ``ra_`` prefix):
   block_attn_step  merge one KV block into a running fp32 (O, LSE) state
   lse_merge        two-way merge of normalised partials
   lse_merge_n      n-way merge of normalised partials
+  splitkv_partial  split-KV partial attention per chunk (no reduction)
   splitkv_decode   split-KV (pass-Q) decode: partials per chunk + reduction
 """
 from __future__ import annotations
@@ -25,7 +26,7 @@ import torch
 __all__ = [
     "RingAttnError", "library_path", "load_library", "abi_version", "ring_schedule",
     "ring_attn_fwd", "block_attn_step", "init_state", "lse_merge", "lse_merge_n",
-    "splitkv_decode",
+    "splitkv_partial", "splitkv_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,7 @@ def load_library() -> ctypes.CDLL:
         "ra_lse_merge": ([ll, i, vp, vp, vp, vp, vp, vp, vp], i),
         "ra_lse_merge_n": ([i, ll, i, i, vp, vp, vp, vp, vp], i),
         "ra_splitkv_decode": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
+        "ra_splitkv_partial": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -252,3 +254,25 @@ def splitkv_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                                  _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(o, "o"),
                                  _dev(lse, "lse"), _stream(q)))
     return o_part, lse_part, o, lse
+
+
+def splitkv_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_splits: int,
+                    scale: Optional[float] = None, o_part: Optional[torch.Tensor] = None,
+                    lse_part: Optional[torch.Tensor] = None):
+    """Partial attention of each of the n_splits chunks: returns (o_part [B,Hq,n,D]
+    fp32, lse_part [B,Hq,n] fp32); reduce them with lse_merge_n."""
+    lib = load_library()
+    B, Hq, Dqk = q.shape
+    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, n_splits, Dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, n_splits), dtype=torch.float32, device=q.device)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise RingAttnError(1, "q and the caches must share one dtype")
+    _check(lib.ra_splitkv_partial(_dtype_code(q), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                  _dev(v_cache, "v_cache"), B, Hq, Hkv, L, Dqk, Dv, int(n_splits), float(scale),
+                                  _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _stream(q)))
+    return o_part, lse_part

@@ -191,18 +191,21 @@ int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_
                     "ra_lse_merge_n launch");
 }
 
-int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
-                      int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part, void* o,
-                      float* lse, void* stream) {
-  if (!q || !k_cache || !v_cache || !o_part || !lse_part || !o || !lse)
-    return fail(RA_EINVAL, "ra_splitkv_decode: null pointer");
+}  // extern "C"
+
+namespace {
+
+int splitkv_launch(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
+                   int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part,
+                   hipStream_t st, const char* who) {
+  if (!q || !k_cache || !v_cache || !o_part || !lse_part) return fail(RA_EINVAL, "%s: null pointer", who);
   if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EINVAL, "dtype must be RA_F32 or RA_BF16");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || n_splits <= 0 || Dqk <= 0 || Dv <= 0)
     return fail(RA_EINVAL, "sizes must be positive");
   if (Hq % Hkv != 0) return fail(RA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (L % n_splits != 0) return fail(RA_EINVAL, "L (%d) must divide into n_splits (%d) equal chunks", L, n_splits);
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(RA_EINVAL, "scale must be finite and > 0");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) || !aligned16(o))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part))
     return fail(RA_EINVAL, "pointers must be 16-byte aligned");
   if (dtype != RA_BF16 || Dqk != Dv || (Dqk != 64 && Dqk != 128) || Hq / Hkv > 16)
     return fail(RA_EUNSUPPORTED, "split-KV decode supports bf16 with Dqk == Dv in {64, 128} and Hq/Hkv <= 16");
@@ -221,10 +224,30 @@ int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void*
   a.n_splits = n_splits;
   a.Ls = L / n_splits;
   a.scale_log2 = scale * ra::kLog2e;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = ra::decode_partial_bf16(a, Dqk, st);
-  if (e != hipSuccess) return hip_status(e, "ra_splitkv_decode partial launch");
-  e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse, st);
+  return hip_status(ra::decode_partial_bf16(a, Dqk, st), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_splitkv_partial(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
+                       int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part,
+                       void* stream) {
+  return splitkv_launch(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part, lse_part,
+                        (hipStream_t)stream, "ra_splitkv_partial");
+}
+
+int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
+                      int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part, void* o,
+                      float* lse, void* stream) {
+  if (!o || !lse) return fail(RA_EINVAL, "ra_splitkv_decode: null pointer");
+  if (!aligned16(o)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (int r = splitkv_launch(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part,
+                             lse_part, (hipStream_t)stream, "ra_splitkv_decode"))
+    return r;
+  const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
+                                       (hipStream_t)stream);
   return hip_status(e, "ra_splitkv_decode merge launch");
 }
 

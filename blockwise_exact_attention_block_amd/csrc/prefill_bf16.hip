@@ -199,12 +199,8 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int row = wave_row0 + nq * 32 + l32;
     const bool valid = row < row_end;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
+    for (int s = 0; s < C::DS; ++s)
       qf[nq][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(row * DQK + 16 * s + 8 * h) * 2u));
-      // Keep the stationary Q fragments in AGPRs: MFMA reads its B operand from
-      // there directly, which leaves the VGPRs to the softmax working set.
-      asm volatile("" : "+a"(qf[nq][s]));
-    }
     m[nq] = kNegInf;
     l[nq] = 0.f;
 #pragma unroll
@@ -328,12 +324,6 @@ prefill_bf16_kernel(PrefillArgs a) {
     const bool skip = a.causal && t.pos0 > wave_pos1;
     const bool need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
     if (!skip) compute_tile(buf, t, need_mask);
-    // the output accumulators live in AGPRs across iterations (MFMA reads and
-    // writes them there; only the rare rescale touches them with VALU)
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq)
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) asm volatile("" : "+a"(oacc[nq][mt]));
     if (n + 1 < ntiles) {
       store_tile(buf ^ 1);
       if (n + 2 < ntiles) load_tile(n + 2);
@@ -375,7 +365,9 @@ prefill_bf16_kernel(PrefillArgs a) {
 
 template <int DQK, int DV, int MODE>
 static hipError_t launch_one(PrefillArgs a, hipStream_t st) {
-  constexpr int NQ = 2, NW = 4;
+  // 8 waves of 32 query rows: two waves per SIMD, so one wave's softmax (VALU)
+  // overlaps the other's MFMAs, and each wave's working set fits in VGPRs.
+  constexpr int NQ = 1, NW = 8;
   using C = PCfg<DQK, DV, NQ, NW>;
   int rows_per_part = MODE == MODE_RING ? a.Sp : a.q_rows;
   a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;

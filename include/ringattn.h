@@ -86,7 +86,7 @@ int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind);
  * RA_F32 Dqk, Dv in {64, 128}. scale must be finite and > 0.
  * Errors: RA_EINVAL for null pointers, non-positive sizes, Hq % Hkv != 0,
  * q_part0 + nq > P, pointers not 16-byte aligned; RA_EUNSUPPORTED for other head
- * dims or a per-head slab of 2^31 elements or more. */
+ * dims or a per-(batch, head) slab of q, k, v or o of 2^31 bytes or more. */
 int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
                      float scale, int causal, void* stream);
@@ -138,11 +138,21 @@ int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_
  *   lse_part device [B, Hq, n_splits] fp32      output
  *   o        device [B, Hq, Dv] dtype of q       output
  *   lse      device [B, Hq] fp32                 output
- * Supported: RA_BF16 with Dqk = Dv = 128 and Hq / Hkv <= 16; RA_F32 with
- * Dqk, Dv in {64, 128}. Errors: RA_EINVAL also when L % n_splits != 0. */
+ * Supported: RA_BF16 with Dqk == Dv in {64, 128} and Hq / Hkv <= 16 (the query
+ * heads of one KV head share one matrix-core tile); anything else returns
+ * RA_EUNSUPPORTED. Errors: RA_EINVAL for null pointers, non-positive sizes,
+ * Hq % Hkv != 0, L % n_splits != 0, misaligned pointers. */
 int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                       int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                       float* o_part, float* lse_part, void* o, float* lse, void* stream);
+
+/* The partial half of ra_splitkv_decode: only o_part / lse_part, no reduction.
+ * This is what each KV shard computes before the partials are exchanged and
+ * reduced with ra_lse_merge_n ([CPEV] §Decode). Arguments, support and errors as
+ * ra_splitkv_decode without o / lse. */
+int ra_splitkv_partial(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                       int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                       float* o_part, float* lse_part, void* stream);
 
 #ifdef __cplusplus
 }

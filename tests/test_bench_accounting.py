@@ -1,0 +1,26 @@
+"""bench.py's algorithmic work counts agree with the oracle's brute-force accounting
+and with the numbers the workloads imply."""
+import oracle
+import bench
+from workloads import CONFIGS
+
+
+def test_prefill_flops_match_oracle_accounting():
+    for name in ("C1", "C2", "C3", "C4"):
+        c = CONFIGS[name]
+        pairs = sum(oracle.visible_pairs_partition(c.Sp, c.P, i, c.causal)
+                    for i in range(c.q_part0, c.q_part0 + c.n_qparts))
+        assert bench.prefill_flops(c) == oracle.attention_flops(pairs, c.Hq * c.B, c.Dqk, c.Dv)
+    # causal aligned sequences count S(S+1)/2 pairs per head
+    c2 = CONFIGS["C2"]
+    assert bench.prefill_flops(c2) == 2 * 256 * c2.Hq * oracle.visible_pairs_aligned_causal(c2.S)
+    assert abs(bench.prefill_flops(CONFIGS["C3"]) - 2.8148e14) / 2.8148e14 < 1e-4
+    assert abs(bench.prefill_flops(CONFIGS["C4"]) - 2.6388e15) / 2.6388e15 < 1e-4
+
+
+def test_decode_bytes():
+    c = CONFIGS["C5"]
+    kv = oracle.kv_cache_bytes(layers=1, h_kv=c.Hkv, d_h=c.Dqk, n=c.L, bytes_per_value=2, batch=c.B)
+    assert kv == 8_589_934_592
+    assert bench.decode_partial_bytes(c) > kv
+    assert bench.decode_partial_bytes(c) - kv < 5e6
