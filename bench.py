@@ -180,6 +180,49 @@ def copy_calibration(torch, steps: int):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": steps}), flush=True)
 
 
+def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
+    """Time split-KV decode (partials + reduction) and the partial kernel alone."""
+    log(f"[bench] generating {dcfg.name} inputs ({dcfg.description})")
+    dq, dk, dvv = decode_inputs_torch(dcfg, dev)
+    o_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits, dcfg.Dv), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    nsteps = max(args.decode_steps, args.steps)
+    log(f"[bench] decode: {max(args.warmup, 2)} warmup + {nsteps} timed steps")
+    d_wall, d_ev = timed(lambda: ra.splitkv_decode(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale),
+                         nsteps, max(args.warmup, 2), stream, torch)
+    p_wall, p_ev = timed(lambda: ra.splitkv_partial(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale,
+                                                    o_part=o_part, lse_part=lse_part),
+                         nsteps, max(args.warmup, 2), stream, torch)
+    tot_bytes = decode_total_bytes(dcfg)
+    part_bytes = decode_partial_bytes(dcfg)
+    d_value = tot_bytes / (d_wall * 1e-3) / 1e9
+    p_ach = part_bytes / (p_ev * 1e-3) / 1e9
+    log(f"[bench] decode {d_wall:.4f} ms/step ({d_value:.0f} GB/s); partial kernel {p_ev:.4f} ms "
+        f"({p_ach:.0f} GB/s)")
+    del dq, dk, dvv
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{dcfg.name}: {dcfg.description}",
+        "value": round(d_value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(d_wall, 5),
+        "steps": nsteps,
+        "algorithmic_bytes_per_step": tot_bytes,
+        "roofline": {
+            "kernel": f"decode_partial_kernel<{dcfg.Dqk}>",
+            "bound": "hbm",
+            "achieved": round(p_ach, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(p_ach / PEAK_HBM_GBPS, 4),
+            "traffic": recorded_traffic("decode", dcfg.name),
+            "algorithmic_bytes_per_launch": part_bytes,
+            "launch_ms": round(p_ev, 5),
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +231,7 @@ def main():
     ap.add_argument("--workload", default="C3", choices=["C2", "C3", "C4"])
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (for kernel profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -210,6 +254,13 @@ def main():
     ra.load_library()
     stream = torch.cuda.current_stream(dev)
     cfg = CONFIGS[args.workload]
+
+    line = {}
+    if args.no_prefill:
+        args.no_cpu_baseline = True
+        line = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        print(json.dumps(line), flush=True)
+        return
 
     log(f"[bench] generating {cfg.name} inputs ({cfg.description})")
     q, k, v = prefill_inputs_torch(cfg, dev)
@@ -266,54 +317,16 @@ def main():
     del out, lse
 
     if not args.no_decode:
-        dcfg = CONFIGS["C5"]
+        # the prefill inputs are dropped to make room and regenerated (same seeds) below
         del q, k, v
         torch.cuda.empty_cache()
-        log(f"[bench] generating {dcfg.name} inputs ({dcfg.description})")
-        dq, dk, dvv = decode_inputs_torch(dcfg, dev)
-        o_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits, dcfg.Dv), dtype=torch.float32, device=dev)
-        lse_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits), dtype=torch.float32, device=dev)
-        torch.cuda.synchronize()
-        nsteps = max(args.decode_steps, args.steps)
-        log(f"[bench] decode: {args.warmup} warmup + {nsteps} timed steps")
-        d_wall, d_ev = timed(lambda: ra.splitkv_decode(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale),
-                             nsteps, max(args.warmup, 2), stream, torch)
-        p_wall, p_ev = timed(lambda: ra.splitkv_partial(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale,
-                                                        o_part=o_part, lse_part=lse_part),
-                             nsteps, max(args.warmup, 2), stream, torch)
-        tot_bytes = decode_total_bytes(dcfg)
-        part_bytes = decode_partial_bytes(dcfg)
-        d_value = tot_bytes / (d_wall * 1e-3) / 1e9
-        p_ach = part_bytes / (p_ev * 1e-3) / 1e9
-        log(f"[bench] decode {d_wall:.4f} ms/step ({d_value:.0f} GB/s); partial kernel {p_ev:.4f} ms "
-            f"({p_ach:.0f} GB/s)")
-        line["decode"] = {
-            "workload": f"{dcfg.name}: {dcfg.description}",
-            "value": round(d_value, 2),
-            "unit": "GB/s",
-            "ms_per_step": round(d_wall, 5),
-            "steps": nsteps,
-            "algorithmic_bytes_per_step": tot_bytes,
-            "roofline": {
-                "kernel": f"decode_partial_kernel<{dcfg.Dqk}>",
-                "bound": "hbm",
-                "achieved": round(p_ach, 2),
-                "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s",
-                "frac": round(p_ach / PEAK_HBM_GBPS, 4),
-                "traffic": recorded_traffic("decode", dcfg.name),
-                "algorithmic_bytes_per_launch": part_bytes,
-                "launch_ms": round(p_ev, 5),
-            },
-        }
-        del dq, dk, dvv
-        torch.cuda.empty_cache()
+        line["decode"] = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        if not args.no_cpu_baseline:
+            q, k, v = prefill_inputs_torch(cfg, dev)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget:.0f} s")
-        q, k, v = prefill_inputs_torch(cfg, dev)
         line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_budget)
-        del q, k, v
 
     print(json.dumps(line), flush=True)
 

@@ -1,0 +1,130 @@
+"""Full-size parity on the large workloads, in the launch configuration bench.py times:
+sampled query rows checked one by one against the fp64 oracle, every decode row and
+partial, and closed forms that hold at any size (Q = 0 turns attention into a
+prefix mean of V with LSE = ln(number of visible keys))."""
+import math
+from collections import defaultdict
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, decode_inputs_torch, prefill_inputs_torch, sample_rows
+from gpu_util import assert_close, np64, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import blockwise_exact_attention_block_amd as m
+    m.load_library()
+    return m
+
+
+def run_prefill(ra, cfg, q, k, v):
+    say(f"ring_attn_fwd {cfg.name}: {cfg.description}")
+    o, lse = ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale, q_part0=cfg.q_part0)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_sampled_rows(cfg, q, k, v, o, lse, rows):
+    """Group the sampled (b, h, r) rows by KV head, pull that head's K/V to the host
+    once, and compare each row with the oracle's definition."""
+    group = cfg.Hq // cfg.Hkv
+    by_kv = defaultdict(list)
+    for b, h, r in rows:
+        by_kv[(b, h // group)].append((h, r))
+    worst_o = worst_l = 0.0
+    for (b, g), hr in sorted(by_kv.items()):
+        k_np = k[b, g].float().cpu().numpy()
+        v_np = v[b, g].float().cpu().numpy()
+        hs = torch.tensor([x[0] for x in hr], device=q.device)
+        rs = torch.tensor([x[1] for x in hr], device=q.device)
+        q_rows = q[b, hs, rs].float().cpu().numpy()
+        pos = cfg.q_part0 * cfg.Sp + rs.cpu().numpy()
+        o_ref, l_ref = oracle.attention_rows(q_rows, pos, k_np, v_np, scale=cfg.scale, causal=cfg.causal, k_pos0=0)
+        do, dl = assert_close(np64(o[b, hs, rs]), np64(lse[b, hs, rs]), o_ref, l_ref, cfg.dtype,
+                              f"{cfg.name} kv head {g}")
+        worst_o, worst_l = max(worst_o, do), max(worst_l, dl)
+    say(f"{cfg.name}: {len(rows)} rows, max|dO| {worst_o:.3e}, max|dLSE| {worst_l:.3e}")
+
+
+def check_zero_query_closed_form(ra, cfg, k, v):
+    """Q = 0: every visible score is 0, so O(row) = mean of V over keys 0..pos and
+    LSE = ln(pos + 1) (causal) -- checked on every row of every head. The prefix
+    means are taken in float64 with torch on the device (no kernel of this library)."""
+    q0 = torch.zeros((cfg.B, cfg.Hq, cfg.Sq, cfg.Dqk), dtype=torch.bfloat16, device=DEV)
+    o, lse = run_prefill(ra, cfg, q0, k, v)
+    del q0
+    group = cfg.Hq // cfg.Hkv
+    pos = torch.arange(cfg.q_part0 * cfg.Sp, (cfg.q_part0 + cfg.n_qparts) * cfg.Sp, device=DEV, dtype=torch.float64)
+    cnt = pos + 1 if cfg.causal else torch.full_like(pos, float(cfg.S))
+    lse_ref = torch.log(cnt)
+    worst_o = worst_l = 0.0
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            csum = torch.cumsum(v[b, g].double(), dim=0)
+            if cfg.causal:
+                mean = csum[cfg.q_part0 * cfg.Sp:(cfg.q_part0 + cfg.n_qparts) * cfg.Sp] / cnt[:, None]
+            else:
+                mean = (csum[-1] / cfg.S).expand(cfg.Sq, cfg.Dv)
+            for h in range(g * group, (g + 1) * group):
+                worst_o = max(worst_o, float((o[b, h].double() - mean).abs().max()))
+                worst_l = max(worst_l, float((lse[b, h].double() - lse_ref).abs().max()))
+            del csum, mean
+    say(f"{cfg.name} Q=0 closed form: max|dO| {worst_o:.3e}, max|dLSE| {worst_l:.3e}")
+    assert worst_o <= 2e-2 and worst_l <= 1e-2, (worst_o, worst_l)
+
+
+@pytest.mark.timeout(900)
+def test_c3_sampled_rows_and_closed_form(ra):
+    cfg = CONFIGS["C3"]
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    o, lse = run_prefill(ra, cfg, q, k, v)
+    rows = sample_rows(cfg, cfg.check_rows)
+    check_sampled_rows(cfg, q, k, v, o, lse, rows)
+    del o, lse, q
+    torch.cuda.empty_cache()
+    check_zero_query_closed_form(ra, cfg, k, v)
+
+
+@pytest.mark.timeout(1200)
+def test_c4_sampled_rows_and_closed_form(ra):
+    cfg = CONFIGS["C4"]
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    o, lse = run_prefill(ra, cfg, q, k, v)
+    rows = sample_rows(cfg, cfg.check_rows)
+    check_sampled_rows(cfg, q, k, v, o, lse, rows)
+    del o, lse, q
+    torch.cuda.empty_cache()
+    check_zero_query_closed_form(ra, cfg, k, v)
+    del k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_c5_every_row_and_partial(ra):
+    cfg = CONFIGS["C5"]
+    q, k, v = decode_inputs_torch(cfg, DEV)
+    say(f"splitkv_decode {cfg.name}: {cfg.description}")
+    op, lp, o, l = ra.splitkv_decode(q, k, v, n_splits=cfg.n_splits, scale=cfg.scale)
+    torch.cuda.synchronize()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for b in range(cfg.B):
+        opr, lpr, orf, lrf = oracle.splitkv_decode(q[b:b + 1].float().cpu().numpy(), k[b:b + 1].float().cpu().numpy(),
+                                                   v[b:b + 1].float().cpu().numpy(), n_splits=cfg.n_splits,
+                                                   scale=cfg.scale)
+        d1 = assert_close(np64(op[b:b + 1]), np64(lp[b:b + 1]), opr, lpr, "bf16", f"C5 partials b={b}")
+        d2 = assert_close(np64(o[b:b + 1]), np64(l[b:b + 1]), orf, lrf, "bf16", f"C5 merged b={b}")
+        worst = [max(worst[0], d1[0]), max(worst[1], d1[1]), max(worst[2], d2[0]), max(worst[3], d2[1])]
+    say(f"C5: partials max|dO| {worst[0]:.3e} |dLSE| {worst[1]:.3e}; merged max|dO| {worst[2]:.3e} "
+        f"|dLSE| {worst[3]:.3e}")
+    # the partial kernel alone reproduces the partials bit for bit
+    op2, lp2 = ra.splitkv_partial(q, k, v, n_splits=cfg.n_splits, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(op2, op) and torch.equal(lp2, lp)
