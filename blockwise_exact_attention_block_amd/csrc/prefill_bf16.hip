@@ -70,15 +70,26 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // Workgroup -> (batch, head, query partition, query tile). Workgroups of one head
-  // are consecutive so that the ones in flight together stream the same K/V
-  // (L2 / Infinity Cache reuse); inside a head the heaviest causal tiles go first.
+  // Workgroup -> (batch, head, query partition, query tile), XCD-aware. Workgroups
+  // are dealt to the 8 XCDs round-robin, so XCD x runs ids x, x+8, ...; those ids
+  // take the x-th contiguous eighth of the work list, ordered (batch, KV head,
+  // query tile, query head of the group). The ~32 workgroups an XCD runs at once
+  // are then the query heads of one KV head on a few adjacent query tiles, which
+  // stream the same K/V blocks at the same time through that XCD's L2. Inside a
+  // KV head the heaviest causal tiles go first.
   const int tiles_per_head = (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
-  const int bh = blockIdx.x / tiles_per_head;
-  const int gt = tiles_per_head - 1 - (int)(blockIdx.x % tiles_per_head);
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
-  const int g = hq / a.group;
+  const int n_items = a.B * a.Hq * tiles_per_head;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_items) return;  // padding of the last XCD's share: no work, no barrier
+  const int w = u % a.group;
+  const int rest = u / a.group;
+  const int gt = tiles_per_head - 1 - rest % tiles_per_head;
+  const int bg = rest / tiles_per_head;
+  const int b = bg / a.Hkv;
+  const int g = bg - b * a.Hkv;
+  const int hq = g * a.group + w;
+  const int bh = b * a.Hq + hq;
   int part = 0, qt = gt;
   if (MODE == MODE_RING) {
     part = gt / a.n_qtiles;
@@ -373,8 +384,9 @@ static hipError_t launch_one(PrefillArgs a, hipStream_t st) {
   a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;
   const long long tiles = (long long)a.B * a.Hq * (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE>), dim3((unsigned)tiles),
+  if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
+  const long long grid = 8 * ((tiles + 7) / 8);   // whole rounds of the 8 XCDs
+  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
