@@ -48,6 +48,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertv
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// max(v, v of the lane 32 apart), on every lane: v_permlane32_swap exchanges the
+// two 32-lane halves, so each lane sees both values without an LDS round trip.
+__device__ __forceinline__ float row_max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource over [base, base + nbytes): loads past the end return zero.

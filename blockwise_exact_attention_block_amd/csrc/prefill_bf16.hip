@@ -16,7 +16,8 @@
 // Data flow per workgroup (NW waves, each owning NQ x 32 query rows):
 //   * Q rows of the wave are loaded once into VGPRs as the B operand of
 //     S^T = K Q^T, so each lane owns one query column of the score tile and the row
-//     maximum / sum are in-lane plus one exchange with the lane 32 apart.
+//     maximum / sum are in-lane plus one exchange with the lane 32 apart
+//     (v_permlane32_swap).
 //   * K and V tiles of BK = 64 keys go HBM -> VGPR (raw buffer loads, prefetched
 //     two tiles ahead) -> LDS (double buffered, rows padded against bank conflicts).
 //   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
@@ -240,17 +241,25 @@ prefill_bf16_kernel(PrefillArgs a) {
   // keeps only 32 keys of scores and probabilities live per query column.
   const int gg = lane >> 4, L = lane & 15;
   auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) {
+    // K fragments of the sub-tile: the next sub-tile's are read from LDS as soon as
+    // the current S product has been issued, so they arrive during its softmax
+    bf16x8 kf[C::DS];
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][l32 * C::KS + 16 * s + 8 * h];
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
       f32x16 sacc[NQ];
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) sacc[nq] = f32x16{};
-      const int krow = kt * 32 + l32;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) {
-        const bf16x8 ka = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h];
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) sacc[nq] = mfma32(ka, qf[nq][s], sacc[nq]);
+        for (int nq = 0; nq < NQ; ++nq) sacc[nq] = mfma32(kf[s], qf[nq][s], sacc[nq]);
+      }
+      if (kt + 1 < BK / 32) {
+        const int krow = (kt + 1) * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h];
       }
       bf16x8 pb[NQ][2];
 #pragma unroll
@@ -273,7 +282,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nq][i]);
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        mx = row_max_halves(mx);
         const float mnew = fmaxf(m[nq], mx * a.scale_log2);
         const float muse = mnew == kNegInf ? 0.f : mnew;
         const float alpha = exp2_hw(m[nq] - muse);
