@@ -18,8 +18,11 @@
 //     S^T = K Q^T, so each lane owns one query column of the score tile and the row
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
 //     (v_permlane32_swap).
-//   * K and V tiles of BK = 64 keys go HBM -> VGPR (raw buffer loads, prefetched
-//     two tiles ahead) -> LDS (double buffered, rows padded against bank conflicts).
+//   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
+//     tiles fit in LDS) go HBM -> VGPR (raw buffer loads, prefetched two tiles
+//     ahead) -> LDS (double buffered, rows padded against bank conflicts).
+//   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
+//     blocks), the tile's row max, one correction factor, then exp2 and PV.
 //   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
 //     (converted to bf16, round to nearest even). V^T operands come from the
 //     natural [key][d] LDS tile through ds_read_b64_tr_b16, with the key order
@@ -34,16 +37,18 @@ enum { MODE_RING = 0, MODE_STEP = 1 };
 
 template <int DQK, int DV, int NQ, int NW>
 struct PCfg {
-  static constexpr int BK = 64;                       // keys per tile
+  // keys per tile: 128 where two double-buffered tiles fit in LDS, else 64; all of
+  // a tile's keys go through one online-softmax update
+  static constexpr int BK = DQK <= 128 ? 128 : 64;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
   static constexpr int KCH = BK * DQK / 8 / THREADS;  // 16-byte K chunks per thread per tile
   static constexpr int VCH = BK * DV / 8 / THREADS;
   // LDS rows are padded so that each lane's reads are a per-lane base plus a
-  // compile-time offset, and 8 (K) / 4 (V, transposed reads) consecutive rows fall
-  // on distinct banks.
+  // compile-time offset, and consecutive K rows (16-byte reads) and V rows
+  // (transposed 8-byte reads) start on different banks.
   static constexpr int KS = DQK + 8;
-  static constexpr int VS = DV + 16;
+  static constexpr int VS = DV + 32;
   static constexpr int K_TILE = BK * KS;
   static constexpr int V_TILE = BK * VS;
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
@@ -236,83 +241,90 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- one KV tile, consumed as BK/32 sub-tiles of 32 keys ----------------------
-  // Each sub-tile is a full online-softmax update (max, rescale, exp-sum, PV), which
-  // keeps only 32 keys of scores and probabilities live per query column.
+  // ---- one KV tile: S for all its keys, one online-softmax update, then PV --------
   const int gg = lane >> 4, L = lane & 15;
   auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) {
-    // K fragments of the sub-tile: the next sub-tile's are read from LDS as soon as
-    // the current S product has been issued, so they arrive during its softmax
+    static_assert(NQ == 1, "one 32-row query block per wave");
+    constexpr int NS = BK / 32;   // 32-key blocks of the S^T accumulator
+    f32x16 sacc[NS];
+    // K fragments of key block kt; the next block's are read from LDS as soon as
+    // the current block's products have been issued
     bf16x8 kf[C::DS];
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][l32 * C::KS + 16 * s + 8 * h];
 #pragma unroll
-    for (int kt = 0; kt < BK / 32; ++kt) {
-      f32x16 sacc[NQ];
+    for (int kt = 0; kt < NS; ++kt) {
+      sacc[kt] = f32x16{};
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) sacc[nq] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) sacc[nq] = mfma32(kf[s], qf[nq][s], sacc[nq]);
-      }
-      if (kt + 1 < BK / 32) {
+      for (int s = 0; s < C::DS; ++s) sacc[kt] = mfma32(kf[s], qf[0][s], sacc[kt]);
+      if (kt + 1 < NS) {
         const int krow = (kt + 1) * 32 + l32;
 #pragma unroll
         for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h];
       }
-      bf16x8 pb[NQ][2];
+    }
+    if (need_mask) {
+      // ragged tile or causal diagonal: keys past the last visible one become -inf.
+      // lim = last visible key of block kt for this lane's query, minus the lane's
+      // 4*h row offset, so each element compares a compile-time key offset
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) {
-        if (need_mask) {
-          // last visible key of the sub-tile for this lane's query, minus the lane's
-          // 4*h row offset, so each element compares a compile-time key offset
-          int lim = t.nvalid - 1 - kt * 32;
-          if (a.causal) {
-            const long long rel = wave_pos0 + nq * 32 + l32 - (t.pos0 + kt * 32);
-            lim = (int)min((long long)lim, max(rel, -1LL));
-          }
-          lim -= 4 * h;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key_off = 8 * (i >> 2) + (i & 3);
-            sacc[nq][i] = key_off <= lim ? sacc[nq][i] : kNegInf;
-          }
+      for (int kt = 0; kt < NS; ++kt) {
+        int lim = t.nvalid - 1 - kt * 32;
+        if (a.causal) {
+          const long long rel = wave_pos0 + l32 - (t.pos0 + kt * 32);
+          lim = (int)min((long long)lim, max(rel, -1LL));
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nq][i]);
-        mx = row_max_halves(mx);
-        const float mnew = fmaxf(m[nq], mx * a.scale_log2);
-        const float muse = mnew == kNegInf ? 0.f : mnew;
-        const float alpha = exp2_hw(m[nq] - muse);
-        m[nq] = mnew;
-        float rs = 0.f;
+        lim -= 4 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_hw(fmaf(sacc[nq][i], a.scale_log2, -muse));
-          sacc[nq][i] = p;
-          rs += p;
-        }
-        l[nq] = l[nq] * alpha + rs;
-        // alpha is exactly 1 unless this lane's running max grew: skip the rescale
-        // when that holds for the whole wave
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int mt = 0; mt < C::MT; ++mt) oacc[nq][mt] *= alpha;
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          f32x8 x;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = sacc[nq][8 * t2 + e];
-          pb[nq][t2] = to_bf16x8(x);
+          const int key_off = 8 * (i >> 2) + (i & 3);
+          sacc[kt][i] = key_off <= lim ? sacc[kt][i] : kNegInf;
         }
       }
-      // O^T += V^T P^T over the sub-tile's two 16-key MFMA steps. Step t2 holds,
-      // in lane half h, keys 16*t2 + 4*h + {0..3} and 16*t2 + 8 + 4*h + {0..3}
-      // (the accumulator rows of S^T). 16-lane group gg reads those keys for
-      // columns 32*mt + 16*(gg%2) + 0..15 of the V tile, transposed.
+    }
+    // running max over the whole tile (raw scores; scale > 0), in the exp2 domain
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kt = 0; kt < NS; ++kt)
+#pragma unroll
+      for (int i = (kt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = row_max_halves(mx);
+    const float mnew = fmaxf(m[0], mx * a.scale_log2);
+    const float muse = mnew == kNegInf ? 0.f : mnew;   // a row with nothing visible yet
+    const float alpha = exp2_hw(m[0] - muse);
+    m[0] = mnew;
+    // P = exp2(scale*log2e*S - m), its row sum, and P^T in bf16 (round to nearest
+    // even) straight from the accumulator registers
+    bf16x8 pb[NS][2];
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < NS; ++kt) {
+      f32x8 p0, p1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p0[i] = exp2_hw(fmaf(sacc[kt][i], a.scale_log2, -muse));
+        p1[i] = exp2_hw(fmaf(sacc[kt][8 + i], a.scale_log2, -muse));
+      }
+      pb[kt][0] = to_bf16x8(p0);
+      pb[kt][1] = to_bf16x8(p1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rs += p0[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rs += p1[i];
+    }
+    l[0] = l[0] * alpha + rs;
+    // alpha is exactly 1 unless this lane's running max grew: skip the rescale
+    // when that holds for the whole wave
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) oacc[0][mt] *= alpha;
+    }
+    // O^T += V^T P^T, 16 keys per MFMA step. Step t2 of block kt holds, in lane
+    // half h, keys 32*kt + 16*t2 + 4*h + {0..3} and 32*kt + 16*t2 + 8 + 4*h + {0..3}
+    // (the accumulator rows of S^T); 16-lane group gg reads those keys for columns
+    // 32*mt + 16*(gg%2) + 0..15 of the V tile, transposed.
+#pragma unroll
+    for (int kt = 0; kt < NS; ++kt)
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
@@ -324,12 +336,9 @@ prefill_bf16_kernel(PrefillArgs a) {
             const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
             half2[x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
           }
-          const bf16x8 va = cat(half2[0], half2[1]);
-#pragma unroll
-          for (int nq = 0; nq < NQ; ++nq) oacc[nq][mt] = mfma32(va, pb[nq][t2], oacc[nq][mt]);
+          oacc[0][mt] = mfma32(cat(half2[0], half2[1]), pb[kt][t2], oacc[0][mt]);
         }
       }
-    }
   };
 
   // ---- pipelined tile loop -------------------------------------------------------
