@@ -9,8 +9,10 @@ score matrix materialised:
   * attention / attention_rows: softmax(scale * Q K^T) V and the per-row
     log-sum-exp of the scaled scores.
   * merge / merge_n: combining normalised partial results by their LSE.
-  * ring_schedule / ring_attention: the ring visiting order and the blockwise
-    protocol built from the two above (used to pin "blockwise == one-shot").
+  * partition_positions / ring_schedule / ring_attention: where each partition's
+    tokens sit (contiguous or striped layout), the ring visiting order and the
+    blockwise protocol built from the two above (used to pin "blockwise ==
+    one-shot").
   * splitkv_decode: the split-KV decode partials and their reduction.
   * accounting helpers that reproduce the pages' own tables.
 
@@ -21,11 +23,13 @@ Citation keys:
   [CPEV]  page "上下文并行 (CP) 收益评估实验设计"
 """
 from .exact import (  # noqa: F401
+    LAYOUTS,
     NEG_INF,
     attention,
     attention_rows,
     merge,
     merge_n,
+    partition_positions,
     ring_schedule,
     ring_attention,
     splitkv_decode,

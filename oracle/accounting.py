@@ -29,17 +29,26 @@ def visible_pairs_aligned_causal(S: int) -> int:
     return S * (S + 1) // 2
 
 
-def visible_pairs_partition(Sp: int, P: int, i: int, causal: bool) -> int:
+def visible_pairs_partition(Sp: int, P: int, i: int, causal: bool, layout: str = "contiguous") -> int:
     """Visible pairs for query partition i of a ring of P partitions of Sp tokens,
-    counted by brute force over the ring schedule (blocks before i are full, block i
-    is the causal triangle, later blocks are skipped)."""
+    summed over the ring schedule.
+
+    Contiguous: blocks before i are full (Sp^2), block i is the causal triangle
+    with its diagonal, later blocks are skipped. Striped (partition p holds
+    positions p, p+P, ...): key c of block j is visible to local query row r iff
+    c*P + j <= r*P + i, i.e. c <= r when j <= i and c < r when j > i, so a block
+    holds the triangle with its diagonal (Sp(Sp+1)/2 pairs) or without it
+    (Sp(Sp-1)/2)."""
     from .exact import ring_schedule
     total = 0
-    for j, kind in ring_schedule(P, i, causal):
+    for j, kind in ring_schedule(P, i, causal, layout):
         if kind == "full":
             total += Sp * Sp
         elif kind == "diag":
-            total += Sp * (Sp + 1) // 2
+            if layout == "striped" and j > i:
+                total += Sp * (Sp - 1) // 2
+            else:
+                total += Sp * (Sp + 1) // 2
     return total
 
 

@@ -60,12 +60,13 @@ def _softmax_rows(s: np.ndarray, vis: np.ndarray, v: np.ndarray) -> Tuple[np.nda
 
 
 def attention(q, k, v, *, scale: float, causal: bool,
-              q_pos0: int = 0, k_pos0: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+              q_pos0: int = 0, k_pos0: int = 0, q_pos=None, k_pos=None) -> Tuple[np.ndarray, np.ndarray]:
     """Exact attention of a query block against one KV block, fp64.
 
     q [B,Hq,Sq,Dqk], k [B,Hkv,Sk,Dqk], v [B,Hkv,Sk,Dv] (any float dtype; upcast
     to fp64 exactly). Query r sits at global position q_pos0 + r and key c at
-    k_pos0 + c. Returns O [B,Hq,Sq,Dv] and LSE [B,Hq,Sq], both fp64.
+    k_pos0 + c, unless explicit position arrays q_pos [Sq] / k_pos [Sk] are given.
+    Returns O [B,Hq,Sq,Dv] and LSE [B,Hq,Sq], both fp64.
 
     This is softmax(scale * Q K^T) V with the full score matrix materialised for
     each (batch, head) ([CH] §挑战 1, eq. lc-ch-attention and the complexity table
@@ -78,7 +79,10 @@ def attention(q, k, v, *, scale: float, causal: bool,
     assert Hq % Hkv == 0, "query heads must be a multiple of KV heads (GQA groups)"
     group = Hq // Hkv
     Dv = v.shape[3]
-    vis = visible(q_pos0 + np.arange(Sq), k_pos0 + np.arange(Sk), causal)
+    qp = q_pos0 + np.arange(Sq) if q_pos is None else np.asarray(q_pos)
+    kp = k_pos0 + np.arange(Sk) if k_pos is None else np.asarray(k_pos)
+    assert qp.shape == (Sq,) and kp.shape == (Sk,)
+    vis = visible(qp, kp, causal)
     o = np.zeros((B, Hq, Sq, Dv))
     lse = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):
@@ -148,7 +152,28 @@ def merge_n(o_parts, lse_parts) -> Tuple[np.ndarray, np.ndarray]:
     return o, lse
 
 
-def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
+LAYOUTS = ("contiguous", "striped")
+
+
+def partition_positions(P: int, Sp: int, p: int, layout: str = "contiguous") -> np.ndarray:
+    """Global token positions held, in order, by partition p of P partitions of Sp
+    tokens each.
+
+    contiguous: p*Sp, ..., p*Sp + Sp - 1 -- each device keeps one consecutive slice
+    ([RING] opening example: 128K tokens on 4 GPUs, 32K consecutive tokens each).
+    striped: p, p + P, p + 2P, ... -- positions dealt round-robin to the devices,
+    the striped variant of ring attention, which interleaves positions so that
+    under a causal mask every device has visible keys in every ring step
+    ([IMPL] §长文本场景下的性能表现与调优).
+    """
+    if layout == "contiguous":
+        return p * Sp + np.arange(Sp, dtype=np.int64)
+    if layout == "striped":
+        return p + P * np.arange(Sp, dtype=np.int64)
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def ring_schedule(P: int, i: int, causal: bool, layout: str = "contiguous") -> List[Tuple[int, str]]:
     """KV block visited by query partition i at each of the P ring steps, with its
     class ('diag', 'full' or 'skip').
 
@@ -156,17 +181,23 @@ def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
     one place round the ring, device d receiving from d-1 (device 0 from the last
     one), so at step s device i holds block (i - s) mod P ([RING] §"KV 在 Ring 中
     如何流动" and its flowchart; [IMPL] code sends to rank+1, receives from rank-1).
-    Under a causal mask a block strictly after the query partition holds only
-    future keys and is skipped; the own block is the masked diagonal ([RING] same
-    section, block-pair skipping by relative position).
+    Contiguous layout under a causal mask: a block strictly after the query
+    partition holds only future keys and is skipped; the own block is the masked
+    diagonal ([RING] same section, block-pair skipping by relative position).
+    Striped layout under a causal mask: every block holds keys before and after
+    each query, so every block is a masked ('diag') one and none is skipped.
     """
     if P <= 0 or not (0 <= i < P):
         raise ValueError("need P > 0 and 0 <= i < P")
+    if layout not in LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
     out = []
     for s in range(P):
         j = (i - s) % P
         if not causal:
             kind = "full"
+        elif layout == "striped":
+            kind = "diag"
         elif j > i:
             kind = "skip"
         elif j == i:
@@ -178,26 +209,31 @@ def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
 
 
 def ring_attention(q_part, k_blocks: Sequence, v_blocks: Sequence, *, i: int,
-                   scale: float, causal: bool, Sp: int, block_order=None):
+                   scale: float, causal: bool, Sp: int, block_order=None,
+                   layout: str = "contiguous"):
     """Blockwise protocol for query partition i: start from O = 0, LSE = -inf,
     visit the KV blocks in ring order and merge each block's exact partial result
     ([RING] §最容易被忽略的细节; [IMPL] §Ring Attention环形注意力机制原理与超长序列处理).
 
-    q_part [B,Hq,Sp,Dqk]; k_blocks[j] [B,Hkv,Sp,Dqk]; v_blocks[j] [B,Hkv,Sp,Dv].
-    `block_order` overrides the order (a list of block indices) to show the result
-    does not depend on it. Exists to pin the protocol against one-shot attention.
+    q_part [B,Hq,Sp,Dqk]; k_blocks[j] [B,Hkv,Sp,Dqk]; v_blocks[j] [B,Hkv,Sp,Dv], the
+    tokens of each partition at the global positions partition_positions gives for
+    the layout. `block_order` overrides the order (a list of block indices) to show
+    the result does not depend on it. Exists to pin the protocol against one-shot
+    attention.
     """
     P = len(k_blocks)
     B, Hq, Sq, _ = np.shape(q_part)
     Dv = np.shape(v_blocks[0])[3]
     o = np.zeros((B, Hq, Sq, Dv))
     lse = np.full((B, Hq, Sq), -np.inf)
-    order = block_order if block_order is not None else [j for j, _ in ring_schedule(P, i, causal)]
+    sched = dict(ring_schedule(P, i, causal, layout))
+    order = block_order if block_order is not None else [j for j, _ in ring_schedule(P, i, causal, layout)]
+    q_pos = partition_positions(P, Sp, i, layout)
     for j in order:
-        if causal and j > i:
+        if sched[j] == "skip":
             continue
         ob, lb = attention(q_part, k_blocks[j], v_blocks[j], scale=scale, causal=causal,
-                           q_pos0=i * Sp, k_pos0=j * Sp)
+                           q_pos=q_pos, k_pos=partition_positions(P, Sp, j, layout))
         o, lse = merge(o, lse, ob, lb)
     return o, lse
 

@@ -58,6 +58,59 @@ def test_ring_protocol_equals_full_attention(causal, P):
         assert np.max(np.abs(o2 - o)) <= 1e-12 and np.max(np.abs(l2 - lse)) <= 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_striped_ring_equals_full_attention_on_strided_rows(causal, P):
+    """Striped layout: partition p holds tokens p, p+P, p+2P, ... of the sequence.
+    The ring over the striped partitions gives, row for row, one-shot attention
+    over the sequence in natural order (positions 0..S-1) taken at those rows."""
+    Sp = 5
+    q, k, v = prefill_inputs_np(2, 4, 2, P * Sp, P * Sp, 8, 7, seed=140 + P)
+    o_ref, l_ref = oracle.attention(q, k, v, scale=0.3, causal=causal)
+    kb = [k[:, :, j::P] for j in range(P)]
+    vb = [v[:, :, j::P] for j in range(P)]
+    for i in range(P):
+        o, lse = oracle.ring_attention(q[:, :, i::P], kb, vb, i=i, scale=0.3, causal=causal, Sp=Sp,
+                                       layout="striped")
+        assert np.max(np.abs(o - o_ref[:, :, i::P])) <= 1e-12
+        assert np.max(np.abs(lse - l_ref[:, :, i::P])) <= 1e-12
+
+
+def test_striped_schedule_and_positions():
+    assert list(oracle.partition_positions(4, 3, 1, "striped")) == [1, 5, 9]
+    assert list(oracle.partition_positions(4, 3, 1, "contiguous")) == [3, 4, 5]
+    # every block of a causal striped ring is masked, none skipped; order unchanged
+    for P in (1, 3, 8):
+        for i in range(P):
+            st_c = oracle.ring_schedule(P, i, True, "striped")
+            assert [j for j, _ in st_c] == [j for j, _ in oracle.ring_schedule(P, i, True)]
+            assert {kd for _, kd in st_c} == {"diag"}
+            assert {kd for _, kd in oracle.ring_schedule(P, i, False, "striped")} == {"full"}
+    with pytest.raises(ValueError):
+        oracle.ring_schedule(4, 0, True, "zigzag")
+
+
+@pytest.mark.parametrize("P,Sp", [(1, 7), (3, 5), (4, 8), (8, 3)])
+def test_visible_pairs_per_partition_brute_force_and_balance(P, Sp):
+    """The closed-form pair counts equal a brute-force count of the visibility
+    matrix on the true positions. Causal striped partitions differ by Sp pairs per
+    partition index (max - min = (P-1) Sp); contiguous ones by about Sp^2."""
+    S = P * Sp
+    for layout in ("contiguous", "striped"):
+        counts = []
+        for i in range(P):
+            qp = oracle.partition_positions(P, Sp, i, layout)
+            n = sum(int(oracle.visible(qp, oracle.partition_positions(P, Sp, j, layout), True).sum())
+                    for j in range(P))
+            assert n == oracle.visible_pairs_partition(Sp, P, i, True, layout)
+            counts.append(n)
+        assert sum(counts) == S * (S + 1) // 2
+        if layout == "striped":
+            assert max(counts) - min(counts) == (P - 1) * Sp
+        else:
+            assert max(counts) - min(counts) == (P - 1) * Sp * Sp
+
+
 def test_dropped_or_doubled_block_moves_lse():
     """A wrong schedule (a block missing or visited twice) is visible in LSE by at
     least log(8/7) when 8 equal-size blocks carry similar mass."""
