@@ -81,6 +81,66 @@ def prefill_flops(cfg) -> int:
     return 2 * (cfg.Dqk + cfg.Dv) * pairs * cfg.Hq * cfg.B
 
 
+def partition_pairs(Sp: int, P: int, i: int, causal: bool, layout: str) -> int:
+    """Visible (query, key) pairs of query partition i in a ring of P partitions of
+    Sp tokens. Contiguous: i full blocks and the diagonal triangle. Striped
+    (partition p = tokens p, p+P, ...): blocks j <= i hold the triangle with its
+    diagonal, blocks j > i the triangle without it."""
+    if not causal:
+        return P * Sp * Sp
+    if layout == "striped":
+        return (i + 1) * Sp * (Sp + 1) // 2 + (P - 1 - i) * Sp * (Sp - 1) // 2
+    return i * Sp * Sp + Sp * (Sp + 1) // 2
+
+
+def run_striped(args, ra, torch, stream, cfg, q, k, v):
+    """Striped layout on the same workload: the whole ring (same visible pairs as
+    the contiguous one), and the last partition's share -- the work of the ring's
+    slowest rank -- under both layouts."""
+    out = torch.empty((cfg.B, cfg.Hq, cfg.Sq, cfg.Dv), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Sq), dtype=torch.float32, device=q.device)
+    steps, warm = max(2, min(args.steps, 5)), 1
+    flops = prefill_flops(cfg)
+    log(f"[bench] striped ring: {warm} warmup + {steps} timed steps")
+    w_all, e_all = timed(lambda: ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale,
+                                                  q_part0=cfg.q_part0, out=out, lse=lse, layout="striped"),
+                         steps, warm, stream, torch)
+    last = cfg.P - 1
+    qs = q[:, :, (last - cfg.q_part0) * cfg.Sp:(last - cfg.q_part0 + 1) * cfg.Sp] if cfg.q_part0 <= last < cfg.q_part0 + cfg.n_qparts else None
+    share = {}
+    if qs is not None:
+        qs = qs.contiguous()
+        o1 = torch.empty((cfg.B, cfg.Hq, cfg.Sp, cfg.Dv), dtype=torch.bfloat16, device=q.device)
+        l1 = torch.empty((cfg.B, cfg.Hq, cfg.Sp), dtype=torch.float32, device=q.device)
+        for layout in ("contiguous", "striped"):
+            _, ev = timed(lambda: ra.ring_attn_fwd(qs, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale,
+                                                   q_part0=last, out=o1, lse=l1, layout=layout),
+                          steps, warm, stream, torch)
+            pairs = partition_pairs(cfg.Sp, cfg.P, last, cfg.causal, layout)
+            f = 2 * (cfg.Dqk + cfg.Dv) * pairs * cfg.Hq * cfg.B
+            share[layout] = {"launch_ms": round(ev, 4), "flops": f, "tflops": round(f / (ev * 1e-3) / 1e12, 2)}
+        del o1, l1
+    res = {
+        "workload": f"{cfg.name} in the striped layout (partition p = tokens p, p+P, ...)",
+        "ring_ms_per_step": round(w_all, 4),
+        "ring_tflops": round(flops / (w_all * 1e-3) / 1e12, 2),
+        "ring_launch_ms": round(e_all, 4),
+    }
+    if share:
+        c, s_ = share["contiguous"], share["striped"]
+        res["last_partition_share"] = {
+            "partition": last,
+            "contiguous": c,
+            "striped": s_,
+            "speedup": round(c["launch_ms"] / s_["launch_ms"], 3),
+            "pair_ratio": round(c["flops"] / s_["flops"], 3),
+        }
+        log(f"[bench] striped: ring {w_all:.3f} ms; last partition {c['launch_ms']:.3f} ms contiguous vs "
+            f"{s_['launch_ms']:.3f} ms striped ({c['launch_ms'] / s_['launch_ms']:.2f}x)")
+    del out, lse
+    return res
+
+
 def decode_partial_bytes(cfg) -> int:
     """Algorithmic HBM bytes of the split-KV partial kernel: K and V read once, q
     read, fp32 partial outputs and LSEs written."""
@@ -235,6 +295,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-striped", action="store_true", help="skip the striped-layout measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -315,6 +376,8 @@ def main():
         },
     }
     del out, lse
+    if not args.no_striped and cfg.causal:
+        line["striped"] = run_striped(args, ra, torch, stream, cfg, q, k, v)
 
     if not args.no_decode:
         # the prefill inputs are dropped to make room and regenerated (same seeds) below

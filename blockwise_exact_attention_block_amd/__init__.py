@@ -8,6 +8,8 @@ There is no fallback: if the library is missing, every call raises.
 Entry points (same names as the C ABI without the ``ra_`` prefix):
   ring_schedule    ring visiting order of one query partition (host only)
   ring_attn_fwd    ring prefill over P KV blocks, running state in registers
+                   (layout="contiguous" or "striped": ra_ring_attn_fwd /
+                   ra_ring_attn_fwd_striped, ra_ring_schedule / _striped)
   block_attn_step  merge one KV block into a running fp32 (O, LSE) state
   lse_merge        two-way merge of normalised partials
   lse_merge_n      n-way merge of normalised partials
@@ -31,7 +33,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libringattn.so"
-_ABI_VERSION = 1
+_ABI_VERSION = 2
 RA_F32, RA_BF16 = 0, 1
 _STATUS = {0: "RA_OK", 1: "RA_EINVAL", 2: "RA_EUNSUPPORTED", 3: "RA_EHIP"}
 _KIND = {0: "skip", 1: "diag", 2: "full"}
@@ -76,6 +78,8 @@ def load_library() -> ctypes.CDLL:
         "ra_last_error": ([], ctypes.c_char_p),
         "ra_ring_schedule": ([i, i, i, ip, ip], i),
         "ra_ring_attn_fwd": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp], i),
+        "ra_ring_schedule_striped": ([i, i, i, ip, ip], i),
+        "ra_ring_attn_fwd_striped": ([i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp], i),
         "ra_block_attn_step": ([i, vp, ll, i, vp, vp, ll, i, i, i, i, i, i, f, i, vp, vp, vp], i),
         "ra_lse_merge": ([ll, i, vp, vp, vp, vp, vp, vp, vp], i),
         "ra_lse_merge_n": ([i, ll, i, i, vp, vp, vp, vp, vp], i),
@@ -127,13 +131,23 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
+_LAYOUTS = ("contiguous", "striped")
+
+
+def _layout(layout: str) -> bool:
+    if layout not in _LAYOUTS:
+        raise RingAttnError(1, f"layout must be one of {_LAYOUTS}, not {layout!r}")
+    return layout == "striped"
+
+
+def ring_schedule(P: int, i: int, causal: bool, layout: str = "contiguous") -> List[Tuple[int, str]]:
     """[(kv_block, kind)] for the P ring steps of query partition i (host only)."""
     lib = load_library()
+    fn = lib.ra_ring_schedule_striped if _layout(layout) else lib.ra_ring_schedule
     n = max(int(P), 1)
     kv = (ctypes.c_int * n)()
     kind = (ctypes.c_int * n)()
-    r = lib.ra_ring_schedule(int(P), int(i), int(bool(causal)), kv, kind)
+    r = fn(int(P), int(i), int(bool(causal)), kv, kind)
     if r < 0:
         _check(-r)
     return [(kv[s], _KIND[kind[s]]) for s in range(r)]
@@ -141,11 +155,14 @@ def ring_schedule(P: int, i: int, causal: bool) -> List[Tuple[int, str]]:
 
 def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, causal: bool,
                   scale: Optional[float] = None, q_part0: int = 0,
-                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  layout: str = "contiguous"):
     """Ring prefill. q [B,Hq,nq*Sp,Dqk] holds query partitions q_part0..q_part0+nq-1;
-    k [B,Hkv,P*Sp,Dqk] and v [B,Hkv,P*Sp,Dv] hold all P KV blocks. Returns
-    (o [B,Hq,nq*Sp,Dv] in q's dtype, lse [B,Hq,nq*Sp] fp32)."""
+    k [B,Hkv,P*Sp,Dqk] and v [B,Hkv,P*Sp,Dv] hold all P KV blocks. Partition p is
+    tokens p*Sp.. (layout "contiguous") or tokens p, p+P, p+2P, ... ("striped").
+    Returns (o [B,Hq,nq*Sp,Dv] in q's dtype, lse [B,Hq,nq*Sp] fp32)."""
     lib = load_library()
+    fn = lib.ra_ring_attn_fwd_striped if _layout(layout) else lib.ra_ring_attn_fwd
     B, Hq, Sq, Dqk = q.shape
     Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
     if Skv % P:
@@ -162,9 +179,9 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, 
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype or lse.dtype != torch.float32:
         raise RingAttnError(1, "q, k, v, out must share one dtype and lse must be fp32")
-    _check(lib.ra_ring_attn_fwd(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                _dev(lse, "lse"), B, Hq, Hkv, Sp, int(P), int(q_part0), nq, Dqk, Dv,
-                                float(scale), int(bool(causal)), _stream(q)))
+    _check(fn(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+              _dev(lse, "lse"), B, Hq, Hkv, Sp, int(P), int(q_part0), nq, Dqk, Dv,
+              float(scale), int(bool(causal)), _stream(q)))
     return out, lse
 
 

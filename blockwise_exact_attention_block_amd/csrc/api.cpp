@@ -97,10 +97,27 @@ int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind) {
   return P;
 }
 
-int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv, float scale,
-                     int causal, void* stream) {
-  if (!q || !k || !v || !o || !lse) return fail(RA_EINVAL, "ra_ring_attn_fwd: null pointer");
+int ra_ring_schedule_striped(int P, int i, int causal, int* kv_block, int* kind) {
+  if (P <= 0 || i < 0 || i >= P || !kv_block || !kind) {
+    fail(RA_EINVAL, "ra_ring_schedule_striped: need P > 0, 0 <= i < P and non-null outputs");
+    return -RA_EINVAL;
+  }
+  for (int s = 0; s < P; ++s) {
+    kv_block[s] = ((i - s) % P + P) % P;
+    kind[s] = causal ? 1 : 2;   // every block is a masked triangle under a causal mask
+  }
+  ok();
+  return P;
+}
+
+}  // extern "C"
+
+namespace {
+
+int ring_fwd(const char* name, int striped, int dtype, const void* q, const void* k, const void* v, void* o,
+             float* lse, int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
+             float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(RA_EINVAL, "%s: null pointer", name);
   if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
   if (Sp <= 0 || P <= 0 || nq <= 0) return fail(RA_EINVAL, "Sp, P, nq must be positive");
   if (q_part0 < 0 || (long long)q_part0 + nq > P)
@@ -129,9 +146,28 @@ int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
   a.nq = nq;
   a.scale_log2 = scale * ra::kLog2e;
   a.causal = causal ? 1 : 0;
+  a.striped = striped;
   hipStream_t st = (hipStream_t)stream;
   const hipError_t e = dtype == RA_BF16 ? ra::prefill_bf16(a, Dqk, Dv, 0, st) : ra::prefill_f32(a, Dqk, Dv, 0, st);
-  return hip_status(e, "ra_ring_attn_fwd launch");
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv, float scale,
+                     int causal, void* stream) {
+  return ring_fwd("ra_ring_attn_fwd", 0, dtype, q, k, v, o, lse, B, Hq, Hkv, Sp, P, q_part0, nq, Dqk, Dv, scale,
+                  causal, stream);
+}
+
+int ra_ring_attn_fwd_striped(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
+                             float scale, int causal, void* stream) {
+  return ring_fwd("ra_ring_attn_fwd_striped", 1, dtype, q, k, v, o, lse, B, Hq, Hkv, Sp, P, q_part0, nq, Dqk,
+                  Dv, scale, causal, stream);
 }
 
 int ra_block_attn_step(int dtype, const void* q, long long q_pos0, int Sq, const void* k_blk, const void* v_blk,

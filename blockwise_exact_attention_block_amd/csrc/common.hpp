@@ -82,12 +82,78 @@ struct PrefillArgs {
   int kv_rows;        // key rows per (b, kv head) in the k/v tensors
   // ring mode
   int Sp, P, q_part0, nq;
+  int striped;        // 0: partition p = tokens p*Sp .. p*Sp+Sp-1; 1: tokens p, p+P, p+2P, ...
   // step mode
   long long q_pos0, k_pos0;
   int Sk;
   int n_qtiles;       // query tiles per (b, h) and per query partition
   float scale_log2;   // softmax scale * log2(e)
   int causal;
+};
+
+// Key-tile schedule of one query tile in ring mode: the KV blocks in ring order,
+// block (i - s) mod P at step s, each cut into tiles of BK keys.
+//   * contiguous layout (partition p holds global tokens p*Sp .. p*Sp + Sp - 1),
+//     causal: the own block i first, only up to the query tile's last row, then
+//     the full blocks i-1 .. 0; blocks after i hold only future keys and are not
+//     visited. Tile positions are global token positions.
+//   * striped layout (partition p holds global tokens p, p + P, p + 2P, ...),
+//     causal: key c of block j is visible to local query row r iff
+//     c*P + j <= r*P + i, i.e. c + [j > i] <= r. Every block is visited up to the
+//     query tile's last row, and masks compare "virtual" positions: the local row
+//     for a query, local index + [j > i] for a key.
+//   * without a causal mask both layouts visit every tile of every block.
+// last_local: local index of the query tile's last row inside its partition.
+struct RingTiles {
+  int i, P, Sp, BK, n_full, na, nb, ntiles;
+  bool causal, striped;
+  __device__ __forceinline__ void init(int i_, int P_, int Sp_, int BK_, bool causal_, bool striped_,
+                                       int last_local) {
+    i = i_; P = P_; Sp = Sp_; BK = BK_; causal = causal_; striped = striped_ && causal_;
+    n_full = (Sp + BK - 1) / BK;
+    na = last_local / BK + 1;                                 // tiles up to the last row
+    nb = last_local >= 1 ? (last_local - 1) / BK + 1 : 0;    // same, one key position later
+    if (!causal)
+      ntiles = P * n_full;
+    else if (striped)
+      ntiles = (i + 1) * na + (P - 1 - i) * nb;
+    else
+      ntiles = na + i * n_full;
+  }
+  // tile n -> first key row in the [P*Sp] block-major K/V slab, position of that
+  // key (global, or virtual for the striped causal case) and valid keys (<= BK)
+  __device__ __forceinline__ void tile(int n, int& row0, long long& pos0, int& nvalid) const {
+    int j, tt, shift = 0;
+    if (!causal) {
+      const int s = n / n_full;
+      tt = n - s * n_full;
+      j = i - s;
+      if (j < 0) j += P;
+    } else if (striped) {
+      if (n < (i + 1) * na) {
+        const int s = n / na;
+        tt = n - s * na;
+        j = i - s;
+      } else {
+        const int r = n - (i + 1) * na;
+        const int s = r / nb;
+        tt = r - s * nb;
+        j = P - 1 - s;          // steps i+1 .. P-1 visit blocks P-1 .. i+1
+        shift = 1;
+      }
+    } else if (n < na) {
+      j = i;
+      tt = n;
+    } else {
+      const int r = n - na;
+      const int s = 1 + r / n_full;
+      j = i - s;
+      tt = r - (s - 1) * n_full;
+    }
+    row0 = j * Sp + tt * BK;
+    pos0 = striped ? (long long)(tt * BK + shift) : (long long)j * Sp + tt * BK;
+    nvalid = min(BK, Sp - tt * BK);
+  }
 };
 
 // Arguments of the split-KV decode partial kernel.

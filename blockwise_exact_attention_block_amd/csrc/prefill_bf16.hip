@@ -107,7 +107,8 @@ prefill_bf16_kernel(PrefillArgs a) {
   if (MODE == MODE_RING) {
     row_base = part * a.Sp + qt * C::BQ;
     row_end = part * a.Sp + a.Sp;
-    pos_base = (long long)(a.q_part0 + part) * a.Sp + qt * C::BQ;
+    // striped causal: virtual query position = local row (see RingTiles)
+    pos_base = (a.causal && a.striped ? 0LL : (long long)(a.q_part0 + part) * a.Sp) + qt * C::BQ;
   } else {
     row_base = qt * C::BQ;
     row_end = a.q_rows;
@@ -124,18 +125,11 @@ prefill_bf16_kernel(PrefillArgs a) {
   const auto vrs = make_rsrc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
 
   // ---- tile schedule -------------------------------------------------------------
-  int ntiles, n_first = 0, n_full = 0, ring_i = 0;
+  RingTiles ring;
+  int ntiles;
   if (MODE == MODE_RING) {
-    ring_i = a.q_part0 + part;
-    n_full = (a.Sp + BK - 1) / BK;
-    if (a.causal) {
-      // the own (diagonal) block first, then blocks i-1 .. 0; blocks after i hold
-      // only future keys and are skipped
-      n_first = (last_row - part * a.Sp) / BK + 1;
-      ntiles = n_first + ring_i * n_full;
-    } else {
-      ntiles = a.P * n_full;
-    }
+    ring.init(a.q_part0 + part, a.P, a.Sp, BK, a.causal != 0, a.striped != 0, last_row - part * a.Sp);
+    ntiles = ring.ntiles;
   } else {
     long long kmax = a.Sk;
     if (a.causal) kmax = min(kmax, last_pos - a.k_pos0 + 1);
@@ -145,26 +139,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   auto tile_ref = [&](int n) -> TileRef {
     TileRef t;
     if (MODE == MODE_RING) {
-      int j, tt;
-      if (a.causal) {
-        if (n < n_first) {
-          j = ring_i;
-          tt = n;
-        } else {
-          const int r = n - n_first;
-          const int s = 1 + r / n_full;
-          j = ring_i - s;
-          tt = r - (s - 1) * n_full;
-        }
-      } else {
-        const int s = n / n_full;
-        tt = n - s * n_full;
-        j = ring_i - s;
-        if (j < 0) j += a.P;
-      }
-      t.row0 = j * a.Sp + tt * BK;
-      t.pos0 = (long long)j * a.Sp + tt * BK;
-      t.nvalid = min(BK, a.Sp - tt * BK);
+      ring.tile(n, t.row0, t.pos0, t.nvalid);
     } else {
       t.row0 = n * BK;
       t.pos0 = a.k_pos0 + (long long)n * BK;

@@ -50,7 +50,8 @@ prefill_f32_kernel(PrefillArgs a) {
   if (MODE == F32_RING) {
     row_base = part * a.Sp + qt * BQ;
     row_end = part * a.Sp + a.Sp;
-    pos_base = (long long)(a.q_part0 + part) * a.Sp + qt * BQ;
+    // striped causal: virtual query position = local row (see RingTiles)
+    pos_base = (a.causal && a.striped ? 0LL : (long long)(a.q_part0 + part) * a.Sp) + qt * BQ;
   } else {
     row_base = qt * BQ;
     row_end = a.q_rows;
@@ -64,17 +65,12 @@ prefill_f32_kernel(PrefillArgs a) {
   const float* k_head = (const float*)a.k + kvh * DQK;
   const float* v_head = (const float*)a.v + kvh * DV;
 
-  // tile schedule (identical rules to the bf16 kernel)
-  int ntiles, n_first = 0, n_full = 0, ring_i = 0;
+  // tile schedule (the same RingTiles rules as the bf16 kernel)
+  RingTiles ring;
+  int ntiles;
   if (MODE == F32_RING) {
-    ring_i = a.q_part0 + part;
-    n_full = (a.Sp + BK - 1) / BK;
-    if (a.causal) {
-      n_first = (last_row - part * a.Sp) / BK + 1;
-      ntiles = n_first + ring_i * n_full;
-    } else {
-      ntiles = a.P * n_full;
-    }
+    ring.init(a.q_part0 + part, a.P, a.Sp, BK, a.causal != 0, a.striped != 0, last_row - part * a.Sp);
+    ntiles = ring.ntiles;
   } else {
     long long kmax = a.Sk;
     if (a.causal) kmax = min(kmax, last_pos - a.k_pos0 + 1);
@@ -111,26 +107,7 @@ prefill_f32_kernel(PrefillArgs a) {
     int krow0, nvalid;
     long long kpos0;
     if (MODE == F32_RING) {
-      int j, tt;
-      if (a.causal) {
-        if (n < n_first) {
-          j = ring_i;
-          tt = n;
-        } else {
-          const int r = n - n_first;
-          const int s = 1 + r / n_full;
-          j = ring_i - s;
-          tt = r - (s - 1) * n_full;
-        }
-      } else {
-        const int s = n / n_full;
-        tt = n - s * n_full;
-        j = ring_i - s;
-        if (j < 0) j += a.P;
-      }
-      krow0 = j * a.Sp + tt * BK;
-      kpos0 = (long long)j * a.Sp + tt * BK;
-      nvalid = min(BK, a.Sp - tt * BK);
+      ring.tile(n, krow0, kpos0, nvalid);
     } else {
       krow0 = n * BK;
       kpos0 = a.k_pos0 + (long long)n * BK;

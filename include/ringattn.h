@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 
 typedef enum {
   RA_OK = 0,
@@ -90,6 +90,24 @@ int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind);
 int ra_ring_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
                      float scale, int causal, void* stream);
+
+/* Striped layout ([IMPL] §长文本场景下的性能表现与调优: the striped variant deals
+ * token positions to the devices round-robin so that, under a causal mask, every
+ * device has visible keys in every ring step): partition p holds global tokens
+ * p, p + P, p + 2P, ..., in that order. Key c of block j is visible to local query
+ * row r of partition i iff c*P + j <= r*P + i. Fills kv_block[s] as
+ * ra_ring_schedule and kind[s] = 1 (masked triangle) for every step when causal,
+ * 2 otherwise; no step is skipped. Returns P, or -RA_EINVAL on bad arguments. */
+int ra_ring_schedule_striped(int P, int i, int causal, int* kv_block, int* kind);
+
+/* Ring prefill as ra_ring_attn_fwd, for the striped layout: row r of partition p
+ * in q, k, v, o and lse is global token r*P + p. Visits the blocks in the order of
+ * ra_ring_schedule_striped; under a causal mask each query tile reads every block
+ * up to its own last local row. Without a causal mask the result equals
+ * ra_ring_attn_fwd's. Arguments, head-dim support and errors as ra_ring_attn_fwd. */
+int ra_ring_attn_fwd_striped(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sp, int P, int q_part0, int nq, int Dqk, int Dv,
+                             float scale, int causal, void* stream);
 
 /* One ring step: merge one KV block into a running fp32 state ([IMPL] §Ring
  * Attention实现代码与通信重叠; [RING] §最容易被忽略的细节).

@@ -31,7 +31,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
-    for name in ("ra_ring_attn_fwd", "ra_block_attn_step", "ra_lse_merge", "ra_splitkv_decode"):
+    for name in ("ra_ring_attn_fwd", "ra_ring_attn_fwd_striped", "ra_block_attn_step", "ra_lse_merge",
+                 "ra_splitkv_decode"):
         assert name in syms
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version(ra):
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 13])
@@ -50,6 +51,13 @@ def test_abi_version(ra):
 def test_schedule_matches_oracle(ra, P, causal):
     for i in range(P):
         assert ra.ring_schedule(P, i, causal) == oracle.ring_schedule(P, i, causal)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 13])
+@pytest.mark.parametrize("causal", [False, True])
+def test_striped_schedule_matches_oracle(ra, P, causal):
+    for i in range(P):
+        assert ra.ring_schedule(P, i, causal, "striped") == oracle.ring_schedule(P, i, causal, "striped")
 
 
 def test_schedule_rejects_bad_arguments(ra):
@@ -61,6 +69,10 @@ def test_schedule_rejects_bad_arguments(ra):
     assert lib.ra_ring_schedule(4, -1, 1, kv, kind) == -1
     assert lib.ra_ring_schedule(4, 0, 1, None, kind) == -1
     assert b"ra_ring_schedule" in lib.ra_last_error()
+    assert lib.ra_ring_schedule_striped(4, 4, 1, kv, kind) == -1
+    assert b"ra_ring_schedule_striped" in lib.ra_last_error()
+    with pytest.raises(ra.RingAttnError):
+        ra.ring_schedule(4, 0, True, "zigzag")
 
 
 FAKE = 1 << 20   # non-null, 16-byte aligned; never dereferenced: validation fails first
@@ -71,9 +83,14 @@ def test_ring_fwd_validation(ra):
     args = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=8, Hkv=8, Sp=64, P=4, q_part0=0,
                 nq=4, Dqk=128, Dv=128, scale=0.088, causal=1, stream=None)
 
-    def call(**kw):
-        a = dict(args, **kw)
-        return lib.ra_ring_attn_fwd(*a.values())
+    for fn in (lib.ra_ring_attn_fwd, lib.ra_ring_attn_fwd_striped):
+        def call(**kw):
+            a = dict(args, **kw)
+            return fn(*a.values())
+        check_ring_validation(lib, call)
+
+
+def check_ring_validation(lib, call):
 
     assert call(q=None) == 1
     assert call(B=0) == 1

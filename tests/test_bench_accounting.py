@@ -18,6 +18,19 @@ def test_prefill_flops_match_oracle_accounting():
     assert abs(bench.prefill_flops(CONFIGS["C4"]) - 2.6388e15) / 2.6388e15 < 1e-4
 
 
+def test_partition_pairs_match_oracle_accounting():
+    for layout in ("contiguous", "striped"):
+        for causal in (False, True):
+            for P, Sp in ((1, 5), (3, 7), (8, 16384), (8, 65536)):
+                for i in range(P):
+                    assert bench.partition_pairs(Sp, P, i, causal, layout) == \
+                        oracle.visible_pairs_partition(Sp, P, i, causal, layout)
+    # the last partition of C3 does 1.875x the pairs of its striped counterpart
+    c = CONFIGS["C3"]
+    r = bench.partition_pairs(c.Sp, c.P, 7, True, "contiguous") / bench.partition_pairs(c.Sp, c.P, 7, True, "striped")
+    assert abs(r - 1.875) < 1e-3
+
+
 def test_decode_bytes():
     c = CONFIGS["C5"]
     kv = oracle.kv_cache_bytes(layers=1, h_kv=c.Hkv, d_h=c.Dqk, n=c.L, bytes_per_value=2, batch=c.B)

@@ -127,6 +127,83 @@ def test_one_partition_ring_equals_plain_and_split(ra):
     assert float((o1.float() - o4.float()).abs().max()) <= 2e-2
 
 
+# ------------------------------------------------------------------------------ striped layout
+
+def striped(x, P):
+    """[B, H, S, D] in natural token order -> partition-major striped order: the
+    rows of partition p are tokens p, p+P, p+2P, ..."""
+    return np.concatenate([x[:, :, p::P] for p in range(P)], axis=2)
+
+
+def striped_case(ra, *, dtype, B, Hq, Hkv, Sp, P, Dqk, Dv, causal, q_part0=0, nq=None, seed=0):
+    """Striped ring on the GPU against one-shot attention over the sequence in
+    natural order (the oracle's plain definition), taken at the striped rows."""
+    nq = P if nq is None else nq
+    say(f"ring_attn_fwd_striped {dtype} B{B} Hq{Hq} Hkv{Hkv} Sp{Sp} P{P} D{Dqk}/{Dv} causal={causal} "
+        f"parts {q_part0}..{q_part0 + nq - 1} seed {seed}")
+    S = P * Sp
+    q_nat, k_nat, v_nat = prefill_inputs_np(B, Hq, Hkv, S, S, Dqk, Dv, seed=seed, dtype=dtype)
+    q_st, k_st, v_st = striped(q_nat, P), striped(k_nat, P), striped(v_nat, P)
+    q = q_st[:, :, q_part0 * Sp:(q_part0 + nq) * Sp]
+    scale = 1.0 / math.sqrt(Dqk)
+    o, lse = ra.ring_attn_fwd(to_dev(q, TD[dtype]), to_dev(k_st, TD[dtype]), to_dev(v_st, TD[dtype]),
+                              P=P, causal=causal, scale=scale, q_part0=q_part0, layout="striped")
+    torch.cuda.synchronize()
+    o_nat, l_nat = oracle.attention(q_nat, k_nat, v_nat, scale=scale, causal=causal)
+    o_ref = striped(o_nat, P)[:, :, q_part0 * Sp:(q_part0 + nq) * Sp]
+    l_ref = striped(l_nat[..., None], P)[..., 0][:, :, q_part0 * Sp:(q_part0 + nq) * Sp]
+    return assert_close(np64(o), np64(lse), o_ref, l_ref, dtype, "ring_attn_fwd_striped")
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sp,P", [(300, 3), (129, 4), (256, 2), (1, 5)])
+def test_bf16_striped_ring(ra, dims, causal, Sp, P):
+    striped_case(ra, dtype="bf16", B=2, Hq=4, Hkv=2, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+                 seed=71 + Sp + P)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sp,P", [(37, 3), (65, 2)])
+def test_fp32_striped_ring(ra, dims, causal, Sp, P):
+    striped_case(ra, dtype="f32", B=2, Hq=4, Hkv=2, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+                 seed=81 + Sp + P)
+
+
+def test_bf16_striped_one_partition_share(ra):
+    """One device's share of a striped ring (the last partition, all KV blocks),
+    GQA 8:1 -- the shape of one rank's work, scaled down."""
+    striped_case(ra, dtype="bf16", B=1, Hq=16, Hkv=2, Sp=384, P=8, Dqk=128, Dv=128, causal=True,
+                 q_part0=7, nq=1, seed=91)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_striped_ring_equals_step_chain_with_virtual_positions(ra, dtype):
+    """The striped causal mask is k_pos <= q_pos on virtual positions (query: local
+    row; key: local index + [j > i]), so P block steps with q_pos0 = 0 and
+    k_pos0 = [j > i] reproduce the striped ring."""
+    B, Hq, Hkv, Sp, P = 1, 4, 2, 150, 4
+    D = 128
+    S = Sp * P
+    say(f"striped ring vs step chain {dtype}")
+    q_nat, k_nat, v_nat = prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=93, dtype=dtype)
+    dq, dk, dv = (to_dev(striped(x, P), TD[dtype]) for x in (q_nat, k_nat, v_nat))
+    o_ring, l_ring = ra.ring_attn_fwd(dq, dk, dv, P=P, causal=True, layout="striped")
+    for i in range(P):
+        qi = dq[:, :, i * Sp:(i + 1) * Sp].contiguous()
+        o_acc, l_acc = ra.init_state(qi, D)
+        for j, kind in ra.ring_schedule(P, i, True, "striped"):
+            assert kind == "diag"
+            ra.block_attn_step(qi, dk[:, :, j * Sp:(j + 1) * Sp].contiguous(), dv[:, :, j * Sp:(j + 1) * Sp].contiguous(),
+                               o_acc, l_acc, q_pos0=0, k_pos0=1 if j > i else 0, causal=True)
+        torch.cuda.synchronize()
+        sl = slice(i * Sp, (i + 1) * Sp)
+        tol_o, tol_l = (2e-2, 1e-2) if dtype == "bf16" else (1e-4, 1e-4)
+        assert float((o_acc - o_ring[:, :, sl].float()).abs().max()) <= tol_o
+        assert float((l_acc - l_ring[:, :, sl]).abs().max()) <= tol_l
+
+
 # ------------------------------------------------------------------------------ step API
 
 @pytest.mark.parametrize("dtype,dims", [("bf16", (128, 128)), ("bf16", (192, 128)), ("f32", (64, 64))])
