@@ -142,9 +142,10 @@ def run_striped(args, ra, torch, stream, cfg, q, k, v):
 
 
 def decode_partial_bytes(cfg) -> int:
-    """Algorithmic HBM bytes of the split-KV partial kernel: K and V read once, q
-    read, fp32 partial outputs and LSEs written."""
-    kv = cfg.B * cfg.Hkv * cfg.L * (cfg.Dqk + cfg.Dv) * 2
+    """Algorithmic HBM bytes of the split-KV partial kernel: K and V read once (2
+    bytes per value, 1 for an fp8 cache), q read, fp32 partial outputs and LSEs
+    written."""
+    kv = cfg.B * cfg.Hkv * cfg.L * (cfg.Dqk + cfg.Dv) * (1 if cfg.kv_dtype == "fp8" else 2)
     q = cfg.B * cfg.Hq * cfg.Dqk * 2
     parts = cfg.B * cfg.Hq * cfg.n_splits * (cfg.Dv + 1) * 4
     return kv + q + parts
@@ -244,16 +245,26 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
     """Time split-KV decode (partials + reduction) and the partial kernel alone."""
     log(f"[bench] generating {dcfg.name} inputs ({dcfg.description})")
     dq, dk, dvv = decode_inputs_torch(dcfg, dev)
+    if dcfg.kv_dtype == "fp8":
+        from workloads import FP8_K_SCALE, FP8_V_SCALE
+        dec = lambda: ra.splitkv_decode_fp8(dq, dk, dvv, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE,
+                                            n_splits=dcfg.n_splits, scale=dcfg.scale)
+        part = lambda: ra.splitkv_partial_fp8(dq, dk, dvv, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE,
+                                              n_splits=dcfg.n_splits, scale=dcfg.scale, o_part=o_part,
+                                              lse_part=lse_part)
+        kname = f"decode_partial_kernel<{dcfg.Dqk},fp8>"
+    else:
+        dec = lambda: ra.splitkv_decode(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale)
+        part = lambda: ra.splitkv_partial(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale,
+                                          o_part=o_part, lse_part=lse_part)
+        kname = f"decode_partial_kernel<{dcfg.Dqk}>"
     o_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits, dcfg.Dv), dtype=torch.float32, device=dev)
     lse_part = torch.empty((dcfg.B, dcfg.Hq, dcfg.n_splits), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     nsteps = max(args.decode_steps, args.steps)
     log(f"[bench] decode: {max(args.warmup, 2)} warmup + {nsteps} timed steps")
-    d_wall, d_ev = timed(lambda: ra.splitkv_decode(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale),
-                         nsteps, max(args.warmup, 2), stream, torch)
-    p_wall, p_ev = timed(lambda: ra.splitkv_partial(dq, dk, dvv, n_splits=dcfg.n_splits, scale=dcfg.scale,
-                                                    o_part=o_part, lse_part=lse_part),
-                         nsteps, max(args.warmup, 2), stream, torch)
+    d_wall, d_ev = timed(dec, nsteps, max(args.warmup, 2), stream, torch)
+    p_wall, p_ev = timed(part, nsteps, max(args.warmup, 2), stream, torch)
     tot_bytes = decode_total_bytes(dcfg)
     part_bytes = decode_partial_bytes(dcfg)
     d_value = tot_bytes / (d_wall * 1e-3) / 1e9
@@ -270,7 +281,7 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
         "steps": nsteps,
         "algorithmic_bytes_per_step": tot_bytes,
         "roofline": {
-            "kernel": f"decode_partial_kernel<{dcfg.Dqk}>",
+            "kernel": kname,
             "bound": "hbm",
             "achieved": round(p_ach, 2),
             "peak": PEAK_HBM_GBPS,
@@ -296,6 +307,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-striped", action="store_true", help="skip the striped-layout measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode measurement")
+    ap.add_argument("--decode-workload", default="C5", choices=["C5", "C5F"],
+                    help="decode workload of a --no-prefill run")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -305,7 +319,7 @@ def main():
 
     import torch
     import blockwise_exact_attention_block_amd as ra
-    from workloads import CONFIGS, decode_inputs_torch, prefill_inputs_torch
+    from workloads import CONFIGS, decode_inputs_fp8_torch, decode_inputs_torch, prefill_inputs_torch
 
     if args.copy_calibration:
         copy_calibration(torch, max(args.steps, 1))
@@ -319,7 +333,9 @@ def main():
     line = {}
     if args.no_prefill:
         args.no_cpu_baseline = True
-        line = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        dcfg = CONFIGS[args.decode_workload]
+        gen = decode_inputs_fp8_torch if dcfg.kv_dtype == "fp8" else decode_inputs_torch
+        line = run_decode(args, ra, torch, dev, stream, dcfg, gen)
         print(json.dumps(line), flush=True)
         return
 
@@ -384,6 +400,10 @@ def main():
         del q, k, v
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        if not args.no_fp8:
+            fp8 = run_decode(args, ra, torch, dev, stream, CONFIGS["C5F"], decode_inputs_fp8_torch)
+            fp8["speedup_vs_bf16_cache"] = round(line["decode"]["ms_per_step"] / fp8["ms_per_step"], 3)
+            line["decode_fp8"] = fp8
         if not args.no_cpu_baseline:
             q, k, v = prefill_inputs_torch(cfg, dev)
 

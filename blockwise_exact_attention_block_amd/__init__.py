@@ -15,6 +15,7 @@ Entry points (same names as the C ABI without the ``ra_`` prefix):
   lse_merge_n      n-way merge of normalised partials
   splitkv_partial  split-KV partial attention per chunk (no reduction)
   splitkv_decode   split-KV (pass-Q) decode: partials per chunk + reduction
+  splitkv_partial_fp8 / splitkv_decode_fp8   the same over an fp8 e4m3 KV cache
 """
 from __future__ import annotations
 
@@ -28,12 +29,12 @@ import torch
 __all__ = [
     "RingAttnError", "library_path", "load_library", "abi_version", "ring_schedule",
     "ring_attn_fwd", "block_attn_step", "init_state", "lse_merge", "lse_merge_n",
-    "splitkv_partial", "splitkv_decode",
+    "splitkv_partial", "splitkv_decode", "splitkv_partial_fp8", "splitkv_decode_fp8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libringattn.so"
-_ABI_VERSION = 2
+_ABI_VERSION = 3
 RA_F32, RA_BF16 = 0, 1
 _STATUS = {0: "RA_OK", 1: "RA_EINVAL", 2: "RA_EUNSUPPORTED", 3: "RA_EHIP"}
 _KIND = {0: "skip", 1: "diag", 2: "full"}
@@ -85,6 +86,8 @@ def load_library() -> ctypes.CDLL:
         "ra_lse_merge_n": ([i, ll, i, i, vp, vp, vp, vp, vp], i),
         "ra_splitkv_decode": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
         "ra_splitkv_partial": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp], i),
+        "ra_splitkv_decode_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
+        "ra_splitkv_partial_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -293,3 +296,54 @@ def splitkv_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                                   _dev(v_cache, "v_cache"), B, Hq, Hkv, L, Dqk, Dv, int(n_splits), float(scale),
                                   _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _stream(q)))
     return o_part, lse_part
+
+
+def _fp8_args(q, k_cache, v_cache, k_scale, v_scale):
+    if q.dtype != torch.bfloat16:
+        raise RingAttnError(1, "q must be bf16 for the fp8 cache path")
+    if k_cache.dtype != torch.float8_e4m3fn or v_cache.dtype != torch.float8_e4m3fn:
+        raise RingAttnError(1, "k_cache and v_cache must be torch.float8_e4m3fn")
+    return float(k_scale), float(v_scale)
+
+
+def splitkv_partial_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, k_scale: float,
+                        v_scale: float, n_splits: int, scale: Optional[float] = None,
+                        o_part: Optional[torch.Tensor] = None, lse_part: Optional[torch.Tensor] = None):
+    """splitkv_partial over an fp8 e4m3 cache: keys are k_scale * k_cache, values
+    v_scale * v_cache; q is bf16. Returns (o_part, lse_part) fp32."""
+    lib = load_library()
+    ks, vs = _fp8_args(q, k_cache, v_cache, k_scale, v_scale)
+    B, Hq, Dqk = q.shape
+    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if o_part is None:
+        o_part = torch.empty((B, Hq, n_splits, Dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq, n_splits), dtype=torch.float32, device=q.device)
+    _check(lib.ra_splitkv_partial_fp8(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ks, vs,
+                                      B, Hq, Hkv, L, Dqk, Dv, int(n_splits), float(scale),
+                                      _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _stream(q)))
+    return o_part, lse_part
+
+
+def splitkv_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, k_scale: float,
+                       v_scale: float, n_splits: int, scale: Optional[float] = None):
+    """splitkv_decode over an fp8 e4m3 cache (see splitkv_partial_fp8). Returns
+    (o_part, lse_part, o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
+    lib = load_library()
+    ks, vs = _fp8_args(q, k_cache, v_cache, k_scale, v_scale)
+    B, Hq, Dqk = q.shape
+    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    dev = q.device
+    o_part = torch.empty((B, Hq, n_splits, Dv), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, Hq, n_splits), dtype=torch.float32, device=dev)
+    o = torch.empty((B, Hq, Dv), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check(lib.ra_splitkv_decode_fp8(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ks, vs,
+                                     B, Hq, Hkv, L, Dqk, Dv, int(n_splits), float(scale),
+                                     _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(o, "o"),
+                                     _dev(lse, "lse"), _stream(q)))
+    return o_part, lse_part, o, lse

@@ -19,7 +19,7 @@ hipError_t lse_merge2(long long rows, int Dv, const float* o_a, const float* lse
                       const float* lse_b, float* o_out, float* lse_out, hipStream_t st);
 hipError_t lse_merge_n(int out_bf16, long long rows, int n, int Dv, const float* o_parts,
                        const float* lse_parts, void* o_out, float* lse_out, hipStream_t st);
-hipError_t decode_partial_bf16(const DecodeArgs& a, int d, hipStream_t st);
+hipError_t decode_partial_bf16(const DecodeArgs& a, int d, int kv8, hipStream_t st);
 }  // namespace ra
 
 namespace {
@@ -231,9 +231,10 @@ int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_
 
 namespace {
 
+// kv8: k_cache / v_cache hold fp8 e4m3 values, dequantised by k_scale / v_scale.
 int splitkv_launch(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq, int Hkv,
                    int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part,
-                   hipStream_t st, const char* who) {
+                   hipStream_t st, const char* who, int kv8 = 0, float k_scale = 1.f, float v_scale = 1.f) {
   if (!q || !k_cache || !v_cache || !o_part || !lse_part) return fail(RA_EINVAL, "%s: null pointer", who);
   if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EINVAL, "dtype must be RA_F32 or RA_BF16");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || n_splits <= 0 || Dqk <= 0 || Dv <= 0)
@@ -241,15 +242,19 @@ int splitkv_launch(int dtype, const void* q, const void* k_cache, const void* v_
   if (Hq % Hkv != 0) return fail(RA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (L % n_splits != 0) return fail(RA_EINVAL, "L (%d) must divide into n_splits (%d) equal chunks", L, n_splits);
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(RA_EINVAL, "scale must be finite and > 0");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(RA_EINVAL, "k_scale and v_scale must be finite and > 0");
+  if (!std::isfinite(scale * k_scale * ra::kLog2e))
+    return fail(RA_EINVAL, "scale * k_scale overflows");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part))
     return fail(RA_EINVAL, "pointers must be 16-byte aligned");
   if (dtype != RA_BF16 || Dqk != Dv || (Dqk != 64 && Dqk != 128) || Hq / Hkv > 16)
     return fail(RA_EUNSUPPORTED, "split-KV decode supports bf16 with Dqk == Dv in {64, 128} and Hq/Hkv <= 16");
-  if (int r = check_slab(L, Dqk, 2, "k/v cache")) return r;
+  if (int r = check_slab(L, Dqk, kv8 ? 1 : 2, "k/v cache")) return r;
   ra::DecodeArgs a{};
   a.q = (const __bf16*)q;
-  a.k = (const __bf16*)k_cache;
-  a.v = (const __bf16*)v_cache;
+  a.k = k_cache;
+  a.v = v_cache;
   a.o_part = o_part;
   a.lse_part = lse_part;
   a.B = B;
@@ -259,8 +264,9 @@ int splitkv_launch(int dtype, const void* q, const void* k_cache, const void* v_
   a.L = L;
   a.n_splits = n_splits;
   a.Ls = L / n_splits;
-  a.scale_log2 = scale * ra::kLog2e;
-  return hip_status(ra::decode_partial_bf16(a, Dqk, st), who);
+  a.scale_log2 = scale * k_scale * ra::kLog2e;
+  a.v_scale = v_scale;
+  return hip_status(ra::decode_partial_bf16(a, Dqk, kv8, st), who);
 }
 
 }  // namespace
@@ -285,6 +291,26 @@ int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void*
   const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
                                        (hipStream_t)stream);
   return hip_status(e, "ra_splitkv_decode merge launch");
+}
+
+int ra_splitkv_partial_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                           int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                           float* o_part, float* lse_part, void* stream) {
+  return splitkv_launch(RA_BF16, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part, lse_part,
+                        (hipStream_t)stream, "ra_splitkv_partial_fp8", 1, k_scale, v_scale);
+}
+
+int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                          float* o_part, float* lse_part, void* o, float* lse, void* stream) {
+  if (!o || !lse) return fail(RA_EINVAL, "ra_splitkv_decode_fp8: null pointer");
+  if (!aligned16(o)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (int r = splitkv_launch(RA_BF16, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part,
+                             lse_part, (hipStream_t)stream, "ra_splitkv_decode_fp8", 1, k_scale, v_scale))
+    return r;
+  const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
+                                       (hipStream_t)stream);
+  return hip_status(e, "ra_splitkv_decode_fp8 merge launch");
 }
 
 }  // extern "C"

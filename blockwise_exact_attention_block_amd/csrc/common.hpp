@@ -66,6 +66,21 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned b
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Four fp8 e4m3 values (OCP format, one 32-bit word) to four bf16, exactly: every
+// e4m3 value is a bf16 value. v_cvt_scalef32_pk_bf16_fp8 converts the low or high
+// 16 bits of the word, with a scale of 1.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(unsigned w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi));
+}
 
 // Arguments of one prefill launch (ring or single step). Element strides are in
 // elements of the tensor's own dtype; all tensors are BHSD.
@@ -159,12 +174,13 @@ struct RingTiles {
 // Arguments of the split-KV decode partial kernel.
 struct DecodeArgs {
   const __bf16* q;   // [B, Hq, D]
-  const __bf16* k;   // [B, Hkv, L, D]
-  const __bf16* v;   // [B, Hkv, L, D]
+  const void* k;     // [B, Hkv, L, D], bf16 or fp8 e4m3
+  const void* v;     // [B, Hkv, L, D], bf16 or fp8 e4m3
   float* o_part;     // [B, Hq, n_splits, D]
   float* lse_part;   // [B, Hq, n_splits]
   int B, Hq, Hkv, G, L, n_splits, Ls;
-  float scale_log2;
+  float scale_log2;  // softmax scale (times the K dequantisation scale) times log2(e)
+  float v_scale;     // V dequantisation scale, applied to the normalised output
 };
 
 }  // namespace ra

@@ -17,18 +17,26 @@
 //     VGPR -> a wave-private LDS tile and is read back transposed with
 //     ds_read_b64_tr_b16 in the accumulator's key order.
 // The four waves' states are merged through LDS at the end.
+//
+// FP8 KV (KV8): the cache holds e4m3 values with one dequantisation scale for K and
+// one for V (1 byte per value, [CH] §挑战 2 KV-size equation with b = 1). K and V
+// are read at half the bytes and converted exactly to bf16 in registers, so the
+// products are the bf16 ones; the K scale is folded into the score scale and the
+// V scale multiplies the normalised output.
 #include "common.hpp"
 
 namespace ra {
 
-template <int D>
+template <int D, bool KV8>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(DecodeArgs a) {
   constexpr int NW = 4, CK = 32;        // waves, keys per wave-chunk
+  constexpr int EB = KV8 ? 1 : 2;       // bytes per cached value
   constexpr int VS = D + 16;            // padded LDS row (keys are rows)
   constexpr int DSTEP = D / 32;         // K-dim steps of the S MFMA
   constexpr int DM = D / 16;            // 16-row output tiles
-  constexpr int VCH = CK * D / 8 / 64;  // 16-byte V chunks per lane per chunk
+  constexpr int VCH = CK * D / 8 / 64;  // 16-byte V chunks per lane per chunk (bf16)
+  constexpr int VCH8 = CK * D / 16 / 64;  // 16-byte V chunks per lane per chunk (fp8)
   constexpr int VBUF = CK * VS;         // elements of one wave's V tile
   __shared__ __attribute__((aligned(16))) __bf16 vbuf[NW][2][VBUF];
 
@@ -40,8 +48,8 @@ decode_partial_kernel(DecodeArgs a) {
   const int key_begin = split * a.Ls;
 
   const size_t slab = (size_t)a.L * D;
-  const auto krs = make_rsrc(a.k + (size_t)bg * slab, (unsigned)(slab * 2));
-  const auto vrs = make_rsrc(a.v + (size_t)bg * slab, (unsigned)(slab * 2));
+  const auto krs = make_rsrc((const char*)a.k + (size_t)bg * slab * EB, (unsigned)(slab * EB));
+  const auto vrs = make_rsrc((const char*)a.v + (size_t)bg * slab * EB, (unsigned)(slab * EB));
 
   // Q^T fragments: lane column = head L16 of the group, k-slots 8*gg + j of step s
   bf16x8 qf[DSTEP];
@@ -61,19 +69,35 @@ decode_partial_kernel(DecodeArgs a) {
   const int nchunks = (a.Ls + CK - 1) / CK;
   const int iters = (nchunks + NW - 1) / NW;
 
-  uint4 kreg[2][DSTEP], vreg[VCH];
+  uint4 kreg[2][DSTEP], vreg[VCH];       // bf16 cache
+  uint2 kreg8[2][DSTEP];                  // fp8 cache: 8 values of one K row
+  uint4 vreg8[VCH8];                      // fp8 cache: 16 values of one V row
   auto load_chunk = [&](int it) {
     const int key0 = key_begin + (it * NW + wave) * CK;   // may lie past the split: masked later
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int s = 0; s < DSTEP; ++s)
-        kreg[kt][s] = buf_load16(krs, (unsigned)((key0 + 16 * kt + L16) * D + 32 * s + 8 * gg) * 2u);
+      for (int s = 0; s < DSTEP; ++s) {
+        const unsigned off = (unsigned)((key0 + 16 * kt + L16) * D + 32 * s + 8 * gg) * (unsigned)EB;
+        if (KV8)
+          kreg8[kt][s] = buf_load8(krs, off);
+        else
+          kreg[kt][s] = buf_load16(krs, off);
+      }
+    if (KV8) {
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int e = c * 64 + lane;
-      const int row = e / (D / 8), col = e % (D / 8);
-      vreg[c] = buf_load16(vrs, (unsigned)((key0 + row) * D + col * 8) * 2u);
+      for (int c = 0; c < VCH8; ++c) {
+        const int e = c * 64 + lane;
+        const int row = e / (D / 16), col = e % (D / 16);
+        vreg8[c] = buf_load16(vrs, (unsigned)((key0 + row) * D + col * 16));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const int e = c * 64 + lane;
+        const int row = e / (D / 8), col = e % (D / 8);
+        vreg[c] = buf_load16(vrs, (unsigned)((key0 + row) * D + col * 8) * 2u);
+      }
     }
   };
 
@@ -86,17 +110,36 @@ decode_partial_kernel(DecodeArgs a) {
   for (int it = 0; it < iters; ++it) {
     const int buf = it & 1;
     __bf16* vb = vbuf[wave][buf];
+    if (KV8) {
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int e = c * 64 + lane;
-      const int row = e / (D / 8), col = e % (D / 8);
-      *(uint4*)&vb[row * VS + col * 8] = vreg[c];
+      for (int c = 0; c < VCH8; ++c) {
+        const int e = c * 64 + lane;
+        const int row = e / (D / 16), col = e % (D / 16);
+        const uint2 b0 = fp8x4_to_bf16x4(vreg8[c].x), b1 = fp8x4_to_bf16x4(vreg8[c].y);
+        const uint2 b2 = fp8x4_to_bf16x4(vreg8[c].z), b3 = fp8x4_to_bf16x4(vreg8[c].w);
+        *(uint4*)&vb[row * VS + col * 16] = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        *(uint4*)&vb[row * VS + col * 16 + 8] = make_uint4(b2.x, b2.y, b3.x, b3.y);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const int e = c * 64 + lane;
+        const int row = e / (D / 8), col = e % (D / 8);
+        *(uint4*)&vb[row * VS + col * 8] = vreg[c];
+      }
     }
     uint4 kcur[2][DSTEP];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int s = 0; s < DSTEP; ++s) kcur[kt][s] = kreg[kt][s];
+      for (int s = 0; s < DSTEP; ++s) {
+        if (KV8) {
+          const uint2 lo = fp8x4_to_bf16x4(kreg8[kt][s].x), hi = fp8x4_to_bf16x4(kreg8[kt][s].y);
+          kcur[kt][s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+          kcur[kt][s] = kreg[kt][s];
+        }
+      }
     if (it + 1 < iters) load_chunk(it + 1);
     __syncthreads();  // V tile visible (the other buffer was drained before the last barrier)
 
@@ -185,19 +228,25 @@ decode_partial_kernel(DecodeArgs a) {
     }
     const size_t hq = (size_t)b * a.Hq + (size_t)g * a.G + head;
     const size_t pi = hq * a.n_splits + split;
-    a.o_part[pi * D + d] = lsum_all > 0.f ? o / lsum_all : 0.f;
+    a.o_part[pi * D + d] = lsum_all > 0.f ? o / lsum_all * a.v_scale : 0.f;
     if (d == 0) a.lse_part[pi] = lsum_all > 0.f ? (Ms + log2_hw(lsum_all)) * kLn2 : kNegInf;
   }
 }
 
-hipError_t decode_partial_bf16(const DecodeArgs& a, int d, hipStream_t st) {
+// kv8: the cache is fp8 e4m3 (1 byte per value) instead of bf16.
+hipError_t decode_partial_bf16(const DecodeArgs& a, int d, int kv8, hipStream_t st) {
   const long long grid = (long long)a.B * a.Hkv * a.n_splits;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (d == 128)
-    hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a);
-  else if (d == 64)
-    hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  const dim3 g((unsigned)grid), blk(256);
+  if (d == 128 && !kv8)
+    hipLaunchKernelGGL((decode_partial_kernel<128, false>), g, blk, 0, st, a);
+  else if (d == 64 && !kv8)
+    hipLaunchKernelGGL((decode_partial_kernel<64, false>), g, blk, 0, st, a);
+  else if (d == 128 && kv8)
+    hipLaunchKernelGGL((decode_partial_kernel<128, true>), g, blk, 0, st, a);
+  else if (d == 64 && kv8)
+    hipLaunchKernelGGL((decode_partial_kernel<64, true>), g, blk, 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

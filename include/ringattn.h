@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 
 typedef enum {
   RA_OK = 0,
@@ -171,6 +171,28 @@ int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void*
 int ra_splitkv_partial(int dtype, const void* q, const void* k_cache, const void* v_cache,
                        int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                        float* o_part, float* lse_part, void* stream);
+
+/* Split-KV decode over an FP8 KV cache: one byte per cached value ([CH] §挑战 2
+ * KV-size equation, b = 1 for FP8), so the cache scan that bounds decode
+ * ([CH] §KV 是 Decode 阶段的隐性瓶颈) reads half the bytes of bf16.
+ *   q        device [B, Hq, Dqk] bf16
+ *   k_cache  device [B, Hkv, L, Dqk] fp8 e4m3 (OCP: 1 sign, 4 exponent bits with
+ *            bias 7, 3 mantissa bits, no infinities, 0x7f / 0xff are NaN); the
+ *            key used is k_scale times the stored value
+ *   v_cache  device [B, Hkv, L, Dv] fp8 e4m3; the value used is v_scale times it
+ *   o_part, lse_part, o (bf16), lse: as ra_splitkv_decode.
+ * The stored values are widened exactly to bf16 for the products; k_scale
+ * multiplies the scores (with scale) and v_scale the normalised outputs.
+ * Supported: Dqk == Dv in {64, 128}, Hq/Hkv <= 16. Errors as ra_splitkv_decode,
+ * plus RA_EINVAL for k_scale or v_scale not finite and > 0. */
+int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                          float* o_part, float* lse_part, void* o, float* lse, void* stream);
+
+/* The partial half of ra_splitkv_decode_fp8 (no reduction), as ra_splitkv_partial. */
+int ra_splitkv_partial_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                           int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                           float* o_part, float* lse_part, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,7 @@ score matrix materialised:
     blockwise protocol built from the two above (used to pin "blockwise ==
     one-shot").
   * splitkv_decode: the split-KV decode partials and their reduction.
+  * e4m3_to_float / dequantize: values of an FP8 (E4M3) KV cache.
   * accounting helpers that reproduce the pages' own tables.
 
 Citation keys:
@@ -35,6 +36,7 @@ from .exact import (  # noqa: F401
     splitkv_decode,
     visible,
 )
+from .fp8 import e4m3_to_float, dequantize  # noqa: F401
 from .accounting import (  # noqa: F401
     kv_cache_bytes,
     decode_lower_bound_s,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version(ra):
-    assert ra.abi_version() == 2
+    assert ra.abi_version() == 3
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 13])
@@ -112,6 +112,15 @@ def test_step_merge_decode_validation(ra):
     assert lib.ra_block_attn_step(1, FAKE, 0, 0, FAKE, FAKE, 0, 64, 1, 2, 2, 64, 64, 0.1, 1, FAKE, FAKE, None) == 1
     assert lib.ra_block_attn_step(1, FAKE, -1, 8, FAKE, FAKE, 0, 64, 1, 2, 2, 64, 64, 0.1, 1, FAKE, FAKE, None) == 1
     assert lib.ra_block_attn_step(1, None, 0, 8, FAKE, FAKE, 0, 64, 1, 2, 2, 64, 64, 0.1, 1, FAKE, FAKE, None) == 1
+    # fp8 decode: bad scales, bf16 shapes rules still apply
+    assert lib.ra_splitkv_decode_fp8(FAKE, FAKE, FAKE, 0.0, 1.0, 1, 8, 2, 64, 128, 128, 2, 0.1, FAKE, FAKE,
+                                     FAKE, FAKE, None) == 1
+    assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1.0, float("inf"), 1, 8, 2, 64, 128, 128, 2, 0.1,
+                                      FAKE, FAKE, None) == 1
+    assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1.0, 1.0, 1, 8, 2, 64, 96, 96, 2, 0.1, FAKE, FAKE,
+                                      None) == 2
+    assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1e30, 1.0, 1, 8, 2, 64, 128, 128, 2, 1e10, FAKE, FAKE,
+                                      None) == 1
     # merges: zero rows is a no-op; bad Dv rejected
     assert lib.ra_lse_merge(0, 128, None, None, None, None, None, None, None) == 0
     assert lib.ra_lse_merge(10, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1

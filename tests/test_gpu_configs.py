@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from workloads import CONFIGS, decode_inputs_torch, prefill_inputs_torch, sample_rows
+from workloads import (CONFIGS, FP8_K_SCALE, FP8_V_SCALE, decode_inputs_fp8_torch, decode_inputs_torch,
+                       prefill_inputs_torch, sample_rows)
 from gpu_util import assert_close, np64, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -128,3 +129,24 @@ def test_c5_every_row_and_partial(ra):
     op2, lp2 = ra.splitkv_partial(q, k, v, n_splits=cfg.n_splits, scale=cfg.scale)
     torch.cuda.synchronize()
     assert torch.equal(op2, op) and torch.equal(lp2, lp)
+
+
+@pytest.mark.timeout(900)
+def test_c5f_fp8_cache_every_row_and_partial(ra):
+    cfg = CONFIGS["C5F"]
+    q, k, v = decode_inputs_fp8_torch(cfg, DEV)
+    say(f"splitkv_decode_fp8 {cfg.name}: {cfg.description}")
+    op, lp, o, l = ra.splitkv_decode_fp8(q, k, v, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE,
+                                         n_splits=cfg.n_splits, scale=cfg.scale)
+    torch.cuda.synchronize()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for b in range(cfg.B):
+        kb = oracle.dequantize(k[b:b + 1].view(torch.uint8).cpu().numpy(), FP8_K_SCALE)
+        vb = oracle.dequantize(v[b:b + 1].view(torch.uint8).cpu().numpy(), FP8_V_SCALE)
+        opr, lpr, orf, lrf = oracle.splitkv_decode(q[b:b + 1].float().cpu().numpy(), kb, vb,
+                                                   n_splits=cfg.n_splits, scale=cfg.scale)
+        d1 = assert_close(np64(op[b:b + 1]), np64(lp[b:b + 1]), opr, lpr, "bf16", f"C5F partials b={b}")
+        d2 = assert_close(np64(o[b:b + 1]), np64(l[b:b + 1]), orf, lrf, "bf16", f"C5F merged b={b}")
+        worst = [max(worst[0], d1[0]), max(worst[1], d1[1]), max(worst[2], d2[0]), max(worst[3], d2[1])]
+    say(f"C5F: partials max|dO| {worst[0]:.3e} |dLSE| {worst[1]:.3e}; merged max|dO| {worst[2]:.3e} "
+        f"|dLSE| {worst[3]:.3e}")

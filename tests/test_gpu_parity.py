@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import CONFIGS, prefill_inputs_np, randn_np
+from workloads import CONFIGS, FP8_K_SCALE, FP8_V_SCALE, fp8_cache_torch, prefill_inputs_np, randn_np
 from gpu_util import assert_close, np64, say
 
 pytestmark = pytest.mark.gpu
@@ -323,3 +323,49 @@ def test_splitkv_decode_small(ra, D, Hq, Hkv, L, n):
     op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
     assert_close(np64(op), np64(lp), op_r, lp_r, "bf16", "decode partials")
     assert_close(np64(o), np64(l), o_r, l_r, "bf16", "decode merged")
+
+
+# ------------------------------------------------------------------------------ fp8 KV decode
+
+def fp8_codes(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (8, 8), (12, 3)])
+@pytest.mark.parametrize("L,n", [(768, 1), (768, 3), (1000, 8)])
+def test_splitkv_decode_fp8_small(ra, D, Hq, Hkv, L, n):
+    """FP8 e4m3 cache with per-tensor scales against the oracle's decode of the
+    dequantised values (the oracle decodes the stored codes itself)."""
+    B = 2
+    say(f"splitkv_decode_fp8 B{B} Hq{Hq} Hkv{Hkv} L{L} n{n} D{D}")
+    q = randn_np((B, Hq, D), 171, "bf16")
+    kc = fp8_cache_torch((B, Hkv, L, D), 172, DEV)
+    vc = fp8_cache_torch((B, Hkv, L, D), 173, DEV)
+    op, lp, o, l = ra.splitkv_decode_fp8(to_dev(q, torch.bfloat16), kc, vc, k_scale=FP8_K_SCALE,
+                                         v_scale=FP8_V_SCALE, n_splits=n)
+    torch.cuda.synchronize()
+    k = oracle.dequantize(fp8_codes(kc), FP8_K_SCALE)
+    v = oracle.dequantize(fp8_codes(vc), FP8_V_SCALE)
+    op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
+    assert_close(np64(op), np64(lp), op_r, lp_r, "bf16", "fp8 decode partials")
+    assert_close(np64(o), np64(l), o_r, l_r, "bf16", "fp8 decode merged")
+    op2, lp2 = ra.splitkv_partial_fp8(to_dev(q, torch.bfloat16), kc, vc, k_scale=FP8_K_SCALE,
+                                      v_scale=FP8_V_SCALE, n_splits=n)
+    torch.cuda.synchronize()
+    assert torch.equal(op2, op) and torch.equal(lp2, lp)
+
+
+def test_splitkv_decode_fp8_equals_bf16_path_on_the_widened_cache(ra):
+    """The fp8 path widens codes exactly to bf16 and folds the scales into the
+    score scale and the output: with scales 1 it reproduces the bf16 decode of the
+    widened cache to fp32 rounding of the scale folding."""
+    B, Hq, Hkv, L, D, n = 2, 8, 2, 2048, 128, 4
+    say("splitkv_decode_fp8 vs bf16 path on the widened cache")
+    q = to_dev(randn_np((B, Hq, D), 181, "bf16"), torch.bfloat16)
+    kc = fp8_cache_torch((B, Hkv, L, D), 182, DEV)
+    vc = fp8_cache_torch((B, Hkv, L, D), 183, DEV)
+    op8, lp8, o8, l8 = ra.splitkv_decode_fp8(q, kc, vc, k_scale=1.0, v_scale=1.0, n_splits=n)
+    op, lp, o, l = ra.splitkv_decode(q, kc.to(torch.bfloat16), vc.to(torch.bfloat16), n_splits=n)
+    torch.cuda.synchronize()
+    assert float((op8 - op).abs().max()) <= 1e-5 and float((lp8 - lp).abs().max()) <= 1e-5

@@ -1,4 +1,4 @@
-"""Synthetic workloads: the five configurations and their seeded input generators.
+"""Synthetic workloads: the configurations and their seeded input generators.
 
 This module holds shapes, seeds and random-number draws only. It computes no part
 of attention, so both the fp64 oracle side (tests, cpu baseline) and the GPU side
@@ -83,6 +83,7 @@ class DecodeConfig:
     n_splits: int
     seed: int = 0
     description: str = ""
+    kv_dtype: str = "bf16"      # "fp8": e4m3 cache with per-tensor K / V scales
 
     @property
     def scale(self) -> float:
@@ -111,7 +112,16 @@ CONFIGS: Dict[str, object] = {
         name="C5", dtype="bf16", B=16, Hq=64, Hkv=8, L=131072, Dqk=128, Dv=128,
         n_splits=8, seed=5000,
         description="split-KV decode, B=16, 64/8 heads, KV length 131072 in 8 splits, bf16"),
+    "C5F": DecodeConfig(
+        name="C5F", dtype="bf16", B=16, Hq=64, Hkv=8, L=131072, Dqk=128, Dv=128,
+        n_splits=8, seed=5500, kv_dtype="fp8",
+        description="split-KV decode over an fp8 e4m3 KV cache, B=16, 64/8 heads, KV length 131072 "
+                    "in 8 splits, bf16 query"),
 }
+
+# per-tensor dequantisation scales of the synthetic fp8 caches (key = K_SCALE * code)
+FP8_K_SCALE = 0.25
+FP8_V_SCALE = 0.5
 
 
 # ----------------------------------------------------------------------------------
@@ -171,6 +181,29 @@ def prefill_inputs_torch(cfg: PrefillConfig, device):
     q = randn_torch((cfg.B, cfg.Hq, cfg.Sq, cfg.Dqk), cfg.seed + 1, cfg.dtype, device)
     k = randn_torch((cfg.B, cfg.Hkv, cfg.S, cfg.Dqk), cfg.seed + 2, cfg.dtype, device)
     v = randn_torch((cfg.B, cfg.Hkv, cfg.S, cfg.Dv), cfg.seed + 3, cfg.dtype, device)
+    return q, k, v
+
+
+def fp8_cache_torch(shape, seed: int, device) -> "torch.Tensor":
+    """Seeded fp8 e4m3 cache: N(0,1) drawn in bf16 slab by slab and cast to
+    torch.float8_e4m3fn (round to nearest even; no draw comes near 448)."""
+    import torch
+    t = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    flat = t.view(-1, *shape[2:])
+    tmp = torch.empty(flat.shape[1:], dtype=torch.bfloat16, device=device)
+    for i in range(flat.shape[0]):
+        tmp.normal_(0.0, 1.0, generator=gen)
+        flat[i].copy_(tmp)
+    return t
+
+
+def decode_inputs_fp8_torch(cfg: DecodeConfig, device):
+    """bf16 query, fp8 K and V caches (dequantised by FP8_K_SCALE / FP8_V_SCALE)."""
+    q = randn_torch((cfg.B, cfg.Hq, cfg.Dqk), cfg.seed + 1, cfg.dtype, device)
+    k = fp8_cache_torch((cfg.B, cfg.Hkv, cfg.L, cfg.Dqk), cfg.seed + 2, device)
+    v = fp8_cache_torch((cfg.B, cfg.Hkv, cfg.L, cfg.Dv), cfg.seed + 3, device)
     return q, k, v
 
 
