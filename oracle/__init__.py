@@ -15,6 +15,8 @@ score matrix materialised:
     one-shot").
   * splitkv_decode: the split-KV decode partials and their reduction.
   * e4m3_to_float / dequantize: values of an FP8 (E4M3) KV cache.
+  * attention_bwd / block_bwd: exact gradients of attention, whole and per
+    (query block, KV block) pair given the saved row LSE.
   * accounting helpers that reproduce the pages' own tables.
 
 Citation keys:
@@ -37,6 +39,7 @@ from .exact import (  # noqa: F401
     visible,
 )
 from .fp8 import e4m3_to_float, dequantize  # noqa: F401
+from .backward import attention_bwd, block_bwd  # noqa: F401
 from .accounting import (  # noqa: F401
     kv_cache_bytes,
     decode_lower_bound_s,
