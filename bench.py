@@ -141,6 +141,47 @@ def run_striped(args, ra, torch, stream, cfg, q, k, v):
     return res
 
 
+def backward_flops(cfg) -> int:
+    """Algorithmic FLOPs of the backward pass: the five products per visible pair
+    (S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K), 2 (3 D_qk + 2 D_v)
+    per pair; recomputed S and dP are not counted."""
+    return prefill_flops(cfg) // (2 * (cfg.Dqk + cfg.Dv)) * 2 * (3 * cfg.Dqk + 2 * cfg.Dv)
+
+
+def run_backward(args, ra, torch, stream, cfg, q, k, v):
+    """Whole-sequence backward of the prefill workload: delta preprocess plus one
+    step over all (query partition, KV block) pairs, fp32 gradients."""
+    if cfg.q_part0 != 0 or cfg.n_qparts != cfg.P:
+        return None
+    out, lse = ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale)
+    dout = torch.empty_like(out).normal_(0.0, 1.0, generator=torch.Generator(device=q.device).manual_seed(cfg.seed + 7))
+    delta = ra.attn_bwd_preprocess(out, dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    steps, warm = max(2, min(args.steps, 3)), 1
+    log(f"[bench] backward: {warm} warmup + {steps} timed steps")
+
+    def step():
+        ra.attn_bwd_preprocess(out, dout, delta)
+        ra.block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=0, k_pos0=0, causal=cfg.causal,
+                               scale=cfg.scale)
+
+    wall, ev = timed(step, steps, warm, stream, torch)
+    flops = backward_flops(cfg)
+    log(f"[bench] backward {wall:.3f} ms/step, {flops / (wall * 1e-3) / 1e12:.1f} TFLOP/s (algorithmic)")
+    del out, lse, dout, delta, dq, dk, dv
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{cfg.name} backward (delta + dK/dV + dQ over all pairs, fp32 gradients)",
+        "ms_per_step": round(wall, 4),
+        "launch_ms": round(ev, 4),
+        "algorithmic_flops": flops,
+        "tflops": round(flops / (wall * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def decode_partial_bytes(cfg) -> int:
     """Algorithmic HBM bytes of the split-KV partial kernel: K and V read once (2
     bytes per value, 1 for an fp8 cache), q read, fp32 partial outputs and LSEs
@@ -308,6 +349,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-striped", action="store_true", help="skip the striped-layout measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--decode-workload", default="C5", choices=["C5", "C5F"],
                     help="decode workload of a --no-prefill run")
     args = ap.parse_args()
@@ -394,6 +436,10 @@ def main():
     del out, lse
     if not args.no_striped and cfg.causal:
         line["striped"] = run_striped(args, ra, torch, stream, cfg, q, k, v)
+    if not args.no_backward:
+        bwd = run_backward(args, ra, torch, stream, cfg, q, k, v)
+        if bwd is not None:
+            line["backward"] = bwd
 
     if not args.no_decode:
         # the prefill inputs are dropped to make room and regenerated (same seeds) below

@@ -16,6 +16,9 @@ Entry points (same names as the C ABI without the ``ra_`` prefix):
   splitkv_partial  split-KV partial attention per chunk (no reduction)
   splitkv_decode   split-KV (pass-Q) decode: partials per chunk + reduction
   splitkv_partial_fp8 / splitkv_decode_fp8   the same over an fp8 e4m3 KV cache
+  attn_bwd_preprocess  delta = rowsum(dO o O) for the backward pass
+  block_attn_bwd_step  one (query block, KV block) pair's dQ, dK, dV contributions
+  attn_bwd         whole-sequence backward (preprocess + one step over all pairs)
 """
 from __future__ import annotations
 
@@ -30,11 +33,12 @@ __all__ = [
     "RingAttnError", "library_path", "load_library", "abi_version", "ring_schedule",
     "ring_attn_fwd", "block_attn_step", "init_state", "lse_merge", "lse_merge_n",
     "splitkv_partial", "splitkv_decode", "splitkv_partial_fp8", "splitkv_decode_fp8",
+    "attn_bwd_preprocess", "block_attn_bwd_step", "attn_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libringattn.so"
-_ABI_VERSION = 3
+_ABI_VERSION = 4
 RA_F32, RA_BF16 = 0, 1
 _STATUS = {0: "RA_OK", 1: "RA_EINVAL", 2: "RA_EUNSUPPORTED", 3: "RA_EHIP"}
 _KIND = {0: "skip", 1: "diag", 2: "full"}
@@ -88,6 +92,8 @@ def load_library() -> ctypes.CDLL:
         "ra_splitkv_partial": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp], i),
         "ra_splitkv_decode_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
         "ra_splitkv_partial_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp], i),
+        "ra_attn_bwd_preprocess": ([i, vp, vp, ll, i, vp, vp], i),
+        "ra_block_attn_bwd_step": ([i, vp, vp, vp, vp, ll, i, vp, vp, ll, i, i, i, i, i, i, f, i, vp, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -347,3 +353,52 @@ def splitkv_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                      _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(o, "o"),
                                      _dev(lse, "lse"), _stream(q)))
     return o_part, lse_part, o, lse
+
+
+def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None):
+    """delta [B,H,S] fp32 = rowsum(dout * o) for bf16 o, dout [B,H,S,Dv]."""
+    lib = load_library()
+    if o.shape != dout.shape or o.dtype != dout.dtype:
+        raise RingAttnError(1, "o and dout must have one shape and dtype")
+    Dv = o.shape[-1]
+    rows = o.numel() // Dv
+    if delta is None:
+        delta = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    _check(lib.ra_attn_bwd_preprocess(_dtype_code(o), _dev(o, "o"), _dev(dout, "dout"), rows, Dv,
+                                      _dev(delta, "delta"), _stream(o)))
+    return delta
+
+
+def block_attn_bwd_step(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, delta: torch.Tensor,
+                        k_blk: torch.Tensor, v_blk: torch.Tensor, dq_acc: torch.Tensor, dk_acc: torch.Tensor,
+                        dv_acc: torch.Tensor, *, q_pos0: int, k_pos0: int, causal: bool,
+                        scale: Optional[float] = None) -> None:
+    """Adds one (query block, KV block) pair's gradient contributions into the fp32
+    accumulators dq_acc [B,Hq,Sq,Dqk], dk_acc [B,Hkv,Sk,Dqk], dv_acc [B,Hkv,Sk,Dv].
+    lse / delta are the queries' full-row values."""
+    lib = load_library()
+    B, Hq, Sq, Dqk = q.shape
+    Hkv, Sk, Dv = k_blk.shape[1], k_blk.shape[2], v_blk.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    for t, name in ((dq_acc, "dq_acc"), (dk_acc, "dk_acc"), (dv_acc, "dv_acc"), (lse, "lse"), (delta, "delta")):
+        if t.dtype != torch.float32:
+            raise RingAttnError(1, f"{name} must be fp32")
+    _check(lib.ra_block_attn_bwd_step(_dtype_code(q), _dev(q, "q"), _dev(dout, "dout"), _dev(lse, "lse"),
+                                      _dev(delta, "delta"), int(q_pos0), Sq, _dev(k_blk, "k_blk"),
+                                      _dev(v_blk, "v_blk"), int(k_pos0), Sk, B, Hq, Hkv, Dqk, Dv, float(scale),
+                                      int(bool(causal)), _dev(dq_acc, "dq_acc"), _dev(dk_acc, "dk_acc"),
+                                      _dev(dv_acc, "dv_acc"), _stream(q)))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, *, causal: bool, scale: Optional[float] = None):
+    """Backward of ring_attn_fwd over a whole contiguous sequence on one device:
+    returns fp32 (dq, dk, dv). Every (query partition, KV block) pair of the ring
+    is covered by one step over the full sequence (positions 0..S-1)."""
+    delta = attn_bwd_preprocess(o, dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=0, k_pos0=0, causal=causal, scale=scale)
+    return dq, dk, dv

@@ -20,6 +20,8 @@ hipError_t lse_merge2(long long rows, int Dv, const float* o_a, const float* lse
 hipError_t lse_merge_n(int out_bf16, long long rows, int n, int Dv, const float* o_parts,
                        const float* lse_parts, void* o_out, float* lse_out, hipStream_t st);
 hipError_t decode_partial_bf16(const DecodeArgs& a, int d, int kv8, hipStream_t st);
+hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long long rows, int Dv, hipStream_t st);
+hipError_t bwd_bf16(const BwdArgs& a, int dqk, int dv, hipStream_t st);
 }  // namespace ra
 
 namespace {
@@ -311,6 +313,56 @@ int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cach
   const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
                                        (hipStream_t)stream);
   return hip_status(e, "ra_splitkv_decode_fp8 merge launch");
+}
+
+int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,
+                           void* stream) {
+  if (!o || !dout || !delta) return fail(RA_EINVAL, "ra_attn_bwd_preprocess: null pointer");
+  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ra_attn_bwd_preprocess: bf16 only");
+  if (rows < 0 || Dv <= 0 || Dv % 8 != 0) return fail(RA_EINVAL, "need rows >= 0 and Dv a positive multiple of 8");
+  if (!aligned16(o) || !aligned16(dout)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  return hip_status(ra::bwd_delta((const __bf16*)o, (const __bf16*)dout, delta, rows, Dv, (hipStream_t)stream),
+                    "ra_attn_bwd_preprocess launch");
+}
+
+int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
+                           long long q_pos0, int Sq, const void* k_blk, const void* v_blk, long long k_pos0, int Sk,
+                           int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal, float* dq_acc,
+                           float* dk_acc, float* dv_acc, void* stream) {
+  if (!q || !dout || !lse || !delta || !k_blk || !v_blk || !dq_acc || !dk_acc || !dv_acc)
+    return fail(RA_EINVAL, "ra_block_attn_bwd_step: null pointer");
+  if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
+  if (dtype != RA_BF16 || !((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)))
+    return fail(RA_EUNSUPPORTED, "the backward step supports bf16 with (Dqk, Dv) in {(64,64), (128,128)}");
+  if (Sq <= 0 || Sk <= 0) return fail(RA_EINVAL, "Sq and Sk must be positive");
+  if (q_pos0 < 0 || k_pos0 < 0) return fail(RA_EINVAL, "positions must be >= 0");
+  if (!aligned16(q) || !aligned16(dout) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(dq_acc) ||
+      !aligned16(dk_acc) || !aligned16(dv_acc))
+    return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (int r = check_slab(Sq, Dqk > Dv ? Dqk : Dv, 2, "q/dout")) return r;
+  if (int r = check_slab(Sk, Dqk > Dv ? Dqk : Dv, 2, "k/v")) return r;
+  ra::BwdArgs a{};
+  a.q = q;
+  a.k = k_blk;
+  a.v = v_blk;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq_acc;
+  a.dk = dk_acc;
+  a.dv = dv_acc;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.q_pos0 = q_pos0;
+  a.k_pos0 = k_pos0;
+  a.scale = scale;
+  a.scale_log2 = scale * ra::kLog2e;
+  a.causal = causal ? 1 : 0;
+  return hip_status(ra::bwd_bf16(a, Dqk, Dv, (hipStream_t)stream), "ra_block_attn_bwd_step launch");
 }
 
 }  // extern "C"

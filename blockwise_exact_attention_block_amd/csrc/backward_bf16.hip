@@ -1,0 +1,489 @@
+// Backward pass of blockwise exact attention for gfx950 (bf16 inputs, fp32
+// gradient accumulators), on v_mfma_f32_32x32x16_bf16.
+//
+// What is computed: the exact gradients of O = softmax(scale * Q K^T) V over the
+// visible keys, for one (query block, KV block) pair at a time, given the
+// queries' full-row LSE saved by the forward pass and delta = rowsum(dO o O)
+// (page "长上下文的第一性挑战", §挑战 1, eq. lc-ch-attention is the function
+// differentiated; page "AI 推理系列（十一）：Ring Attention 如何让多张 GPU 共同计算
+// 一条超长序列", §什么时候值得引入 Context Parallelism, names the backward pass's
+// data dependencies among what a ring must get right). With P = exp(scale q k -
+// LSE) restricted to the block, each pair adds
+//     dV += P^T dO,  dS = P o (dO V^T - delta),  dQ += scale dS K,  dK += scale dS^T Q
+// to fp32 accumulators, so a ring backward is P such steps per device with dK / dV
+// travelling with their KV block; the sums are order independent.
+//
+// Three kernels:
+//   * bwd_delta_kernel: delta = rowsum(dO o O) per query row.
+//   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
+//     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column);
+//     K and V tiles of 64 keys are staged in LDS. Per 32 keys: S^T = K Q^T and
+//     dP^T = V dO^T (lane-local LSE and delta), dS^T, then dQ^T += K^T dS^T with
+//     K^T read through ds_read_b64_tr_b16.
+//   * bwd_dkdv_kernel: one workgroup per 256 keys of one (batch, KV head), 8 waves
+//     of 32 keys, looping over the group's query heads and the visible query tiles
+//     (64 rows, staged in LDS with their LSE and delta). K rows stay in VGPRs as the
+//     B operand of S = Q K^T (lane = key column); the workgroup's V rows sit in LDS
+//     for dP = dO V^T. dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T through
+//     ds_read_b64_tr_b16. Rows past the query block carry LSE = +inf, so their P
+//     and dS are exactly 0 with no row mask.
+#include "common.hpp"
+
+namespace ra {
+
+constexpr float kPosInf = __builtin_huge_valf();
+
+// ---- delta = rowsum(dO o O) ----------------------------------------------------------
+// A 16-lane group per row: Dv/8 16-byte chunks over the group, then a butterfly sum.
+__global__ void __launch_bounds__(256)
+bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long rows, int Dv) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int L = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    for (int c = L; c < Dv / 8; c += 16) {
+      const bf16x8 x = *(const bf16x8*)(o + row * Dv + c * 8);
+      const bf16x8 y = *(const bf16x8*)(dout + row * Dv + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && L == 0) delta[row] = acc;
+}
+
+// LDS row strides (elements): +8 keeps 16-byte rows starting on different banks
+template <int DQK, int DV>
+struct BCfg {
+  static constexpr int THREADS = 512;               // 8 waves
+  static constexpr int ROWS = 256;                  // query rows (dQ) / keys (dK, dV) per workgroup
+  static constexpr int BK = 64;                     // keys per LDS tile (dQ kernel)
+  static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
+  static constexpr int KS = DQK + 8, VS = DV + 8;
+  static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
+  static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
+};
+
+// ---- dQ -------------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ void __launch_bounds__(512)
+bwd_dq_kernel(BwdArgs a) {
+  using C = BCfg<DQK, DV>;
+  constexpr int BK = C::BK;
+  constexpr int KCH = BK * DQK / 8 / C::THREADS, VCH = BK * DV / 8 / C::THREADS;
+  static_assert(KCH * C::THREADS * 8 == BK * DQK && VCH * C::THREADS * 8 == BK * DV, "tile split");
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BK * C::KS];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BK * C::VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
+  const int qt = blockIdx.x % a.n_tiles;
+  const int bh = blockIdx.x / a.n_tiles;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / a.group;
+  const int row_base = qt * C::ROWS;
+  const int last_row = min(row_base + C::ROWS, a.Sq) - 1;
+  long long kmax = a.Sk;
+  if (a.causal) kmax = min(kmax, a.q_pos0 + last_row - a.k_pos0 + 1);
+  if (kmax <= 0) return;  // no key of the block is visible to this tile
+  const int ntiles = (int)((kmax + BK - 1) / BK);
+
+  const size_t kvh = (size_t)(b * a.Hkv + g) * a.Sk;
+  const auto qrs = make_rsrc((const __bf16*)a.q + (size_t)bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 2));
+  const auto ors = make_rsrc((const __bf16*)a.dout + (size_t)bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 2));
+  const auto krs = make_rsrc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.Sk * DQK * 2));
+  const auto vrs = make_rsrc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.Sk * DV * 2));
+
+  const int wave_row0 = row_base + wave * 32;
+  const long long wave_pos0 = a.q_pos0 + wave_row0;
+  const int my_row = wave_row0 + l32;
+  bf16x8 qf[C::DS], of[C::DSV];
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(my_row * DQK + 16 * s + 8 * h) * 2u));
+#pragma unroll
+  for (int s = 0; s < C::DSV; ++s)
+    of[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
+  // a row past the block, or with no visible key at all, gets P = 0
+  float lse2 = kPosInf, dlt = 0.f;
+  if (my_row < a.Sq) {
+    const float l = a.lse[(size_t)bh * a.Sq + my_row];
+    if (l != kNegInf) lse2 = l * kLog2e;
+    dlt = a.delta[(size_t)bh * a.Sq + my_row];
+  }
+  f32x16 dqacc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) dqacc[mt] = f32x16{};
+
+  uint4 kr[KCH], vr[VCH];
+  auto load_tile = [&](int n) {
+    const int row0 = n * BK;
+#pragma unroll
+    for (int it = 0; it < KCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
+      kr[it] = buf_load16(krs, (unsigned)((row0 + row) * DQK + col * 8) * 2u);
+    }
+#pragma unroll
+    for (int it = 0; it < VCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
+      vr[it] = buf_load16(vrs, (unsigned)((row0 + row) * DV + col * 8) * 2u);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < KCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
+      *(uint4*)&ks[buf][row * C::KS + col * 8] = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
+      *(uint4*)&vs[buf][row * C::VS + col * 8] = vr[it];
+    }
+  };
+
+  auto compute_tile = [&](int buf, long long kpos0, int nvalid, bool need_mask) {
+#pragma unroll
+    for (int kt = 0; kt < BK / 32; ++kt) {
+      const int krow = kt * 32 + l32;
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h], qf[s], st);
+#pragma unroll
+      for (int s = 0; s < C::DSV; ++s)
+        dpt = mfma32(*(const bf16x8*)&vs[buf][krow * C::VS + 16 * s + 8 * h], of[s], dpt);
+      if (need_mask) {
+        // last visible key of this 32-key block for the lane's query, minus 4*h
+        int lim = nvalid - 1 - kt * 32;
+        if (a.causal) {
+          const long long rel = wave_pos0 + l32 - (kpos0 + kt * 32);
+          lim = (int)min((long long)lim, max(rel, -1LL));
+        }
+        lim -= 4 * h;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > lim) st[i] = kNegInf;
+      }
+      // dS^T = P^T o (dP^T - delta), rounded to bf16 as the B operand of dQ^T
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        f32x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * t2 + e;
+          const float p = exp2_hw(fmaf(st[i], a.scale_log2, -lse2));
+          x[e] = p * (dpt[i] - dlt);
+        }
+        dsb[t2] = to_bf16x8(x);
+      }
+      // dQ^T += K^T dS^T: step t2 holds keys 16*t2 + 4*h + {0..3} and
+      // 16*t2 + 8 + 4*h + {0..3} in lane half h; K^T rows d = 32*mt + lane%32
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x4 half2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            half2[x] = lds_read_tr16(&ks[buf][key * C::KS + dcol]);
+          }
+          dqacc[mt] = mfma32(cat(half2[0], half2[1]), dsb[t2], dqacc[mt]);
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (ntiles > 1) load_tile(1);
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    const long long kpos0 = a.k_pos0 + (long long)n * BK;
+    const int nvalid = min(BK, a.Sk - n * BK);
+    const bool skip = a.causal && kpos0 > wave_pos0 + 31;
+    const bool need_mask = nvalid < BK || (a.causal && kpos0 + BK - 1 > wave_pos0);
+    if (!skip) compute_tile(buf, kpos0, nvalid, need_mask);
+    if (n + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      if (n + 2 < ntiles) load_tile(n + 2);
+    }
+    __syncthreads();
+  }
+
+  if (my_row < a.Sq) {
+    float* dqp = a.dq + ((size_t)bh * a.Sq + my_row) * DQK;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * mt + 8 * g4 + 4 * h;
+        f32x4 cur = *(const f32x4*)(dqp + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[e] = fmaf(a.scale, dqacc[mt][4 * g4 + e], cur[e]);
+        *(f32x4*)(dqp + d) = cur;
+      }
+  }
+}
+
+// ---- dK, dV ---------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ void __launch_bounds__(512)
+bwd_dkdv_kernel(BwdArgs a) {
+  using C = BCfg<DQK, DV>;
+  constexpr int BQ = C::BQ;
+  constexpr int QS = C::KS, OS = C::VS;   // Q rows like K rows, dO rows like V rows
+  constexpr int QCH = BQ * DQK / 8 / C::THREADS, OCH = BQ * DV / 8 / C::THREADS;
+  constexpr int VCH = C::ROWS * DV / 8 / C::THREADS;
+  static_assert(QCH * C::THREADS * 8 == BQ * DQK && OCH * C::THREADS * 8 == BQ * DV, "tile split");
+  __shared__ __attribute__((aligned(16))) __bf16 qsm[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) __bf16 osm[2][BQ * OS];
+  __shared__ __attribute__((aligned(16))) __bf16 vsm[C::ROWS * C::VS];
+  __shared__ __attribute__((aligned(16))) float lsm[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dsm[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
+  const int ktile = blockIdx.x % a.n_tiles;
+  const int bg = blockIdx.x / a.n_tiles;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int key_base = ktile * C::ROWS;
+
+  // queries that can see the workgroup's first key (all of them without a mask)
+  int q_first = 0;
+  if (a.causal) {
+    const long long f = a.k_pos0 + key_base - a.q_pos0;
+    q_first = (int)max(0LL, min(f, (long long)a.Sq));
+  }
+  if (q_first >= a.Sq) return;  // no query of the block sees these keys
+  const int qt0 = q_first / BQ;
+  const int nqt = (a.Sq + BQ - 1) / BQ - qt0;
+  const int ntiles = a.group * nqt;   // (query head of the group, query tile) pairs
+
+  const size_t kvh = (size_t)bg * a.Sk;
+  const auto krs = make_rsrc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.Sk * DQK * 2));
+  const auto vrs = make_rsrc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.Sk * DV * 2));
+  const int wave_key0 = key_base + wave * 32;
+  const long long wave_kpos0 = a.k_pos0 + wave_key0;
+  const int my_key = wave_key0 + l32;
+
+  // K row of the lane's key as the B operand of S = Q K^T (keys past the block read 0)
+  bf16x8 kf[C::DS];
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s)
+    kf[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
+  // the workgroup's V rows into LDS, once
+#pragma unroll
+  for (int it = 0; it < VCH; ++it) {
+    const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
+    *(uint4*)&vsm[row * C::VS + col * 8] = buf_load16(vrs, (unsigned)((key_base + row) * DV + col * 8) * 2u);
+  }
+  f32x16 dkacc[C::MT], dvacc[C::MTV];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) dkacc[mt] = f32x16{};
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) dvacc[mt] = f32x16{};
+
+  uint4 qr[QCH], orr[OCH];
+  float rowv = 0.f;   // threads 0..63: LSE * log2(e) of a row; 64..127: its delta
+  auto tile_head = [&](int n) { return g * a.group + n / nqt; };
+  auto tile_row0 = [&](int n) { return (qt0 + n % nqt) * BQ; };
+  auto load_tile = [&](int n) {
+    const int hq = tile_head(n), row0 = tile_row0(n);
+    const size_t bh = (size_t)b * a.Hq + hq;
+    const auto qrs = make_rsrc((const __bf16*)a.q + bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 2));
+    const auto ors = make_rsrc((const __bf16*)a.dout + bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 2));
+#pragma unroll
+    for (int it = 0; it < QCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
+      qr[it] = buf_load16(qrs, (unsigned)((row0 + row) * DQK + col * 8) * 2u);
+    }
+#pragma unroll
+    for (int it = 0; it < OCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
+      orr[it] = buf_load16(ors, (unsigned)((row0 + row) * DV + col * 8) * 2u);
+    }
+    if (tid < 2 * BQ) {
+      const int r = row0 + (tid & (BQ - 1));
+      if (tid < BQ) {
+        rowv = kPosInf;   // rows past the block, or with no visible key: P = 0
+        if (r < a.Sq) {
+          const float l = a.lse[bh * a.Sq + r];
+          if (l != kNegInf) rowv = l * kLog2e;
+        }
+      } else {
+        rowv = r < a.Sq ? a.delta[bh * a.Sq + r] : 0.f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < QCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
+      *(uint4*)&qsm[buf][row * QS + col * 8] = qr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < OCH; ++it) {
+      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
+      *(uint4*)&osm[buf][row * OS + col * 8] = orr[it];
+    }
+    if (tid < BQ)
+      lsm[buf][tid] = rowv;
+    else if (tid < 2 * BQ)
+      dsm[buf][tid - BQ] = rowv;
+  };
+
+  auto compute_tile = [&](int buf, long long qpos_t) {
+#pragma unroll
+    for (int qs = 0; qs < BQ / 32; ++qs) {
+      const long long qpos_s = qpos_t + qs * 32;
+      if (a.causal && qpos_s + 31 < wave_kpos0) continue;   // these queries precede all the wave's keys
+      const bool need_mask = a.causal && qpos_s < wave_kpos0 + 31;
+      const int qrow = qs * 32 + l32;
+      // S = Q K^T and dP = dO V^T: lane = key column, rows = queries 8*(i/4) + 4*h + i%4
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kf[s], st);
+#pragma unroll
+      for (int s = 0; s < C::DSV; ++s) {
+        const bf16x8 vb = *(const bf16x8*)&vsm[(wave * 32 + l32) * C::VS + 16 * s + 8 * h];
+        dpt = mfma32(*(const bf16x8*)&osm[buf][qrow * OS + 16 * s + 8 * h], vb, dpt);
+      }
+      if (need_mask) {
+        // key visible iff key_pos <= query_pos: row offset >= key_pos - qpos_s (minus 4*h)
+        const int lim = (int)(wave_kpos0 + l32 - qpos_s) - 4 * h;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) < lim) st[i] = kNegInf;
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
+        const f32x4 d0 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 d1 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
+        f32x8 p, ds;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * t2 + e;
+          const float lr = e < 4 ? l0[e] : l1[e - 4];
+          const float dr = e < 4 ? d0[e] : d1[e - 4];
+          p[e] = exp2_hw(fmaf(st[i], a.scale_log2, -lr));
+          ds[e] = p[e] * (dpt[i] - dr);
+        }
+        pb[t2] = to_bf16x8(p);
+        dsb[t2] = to_bf16x8(ds);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: step t2 holds queries 16*t2 + 4*h + {0..3}
+      // and 16*t2 + 8 + 4*h + {0..3} in lane half h; dO^T / Q^T rows = 32*mt + lane%32
+#pragma unroll
+      for (int mt = 0; mt < C::MTV; ++mt) {
+        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x4 half2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int r = qs * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            half2[x] = lds_read_tr16(&osm[buf][r * OS + dcol]);
+          }
+          dvacc[mt] = mfma32(cat(half2[0], half2[1]), pb[t2], dvacc[mt]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x4 half2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int r = qs * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            half2[x] = lds_read_tr16(&qsm[buf][r * QS + dcol]);
+          }
+          dkacc[mt] = mfma32(cat(half2[0], half2[1]), dsb[t2], dkacc[mt]);
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();   // also publishes the V rows
+  if (ntiles > 1) load_tile(1);
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    compute_tile(buf, a.q_pos0 + tile_row0(n));
+    if (n + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      if (n + 2 < ntiles) load_tile(n + 2);
+    }
+    __syncthreads();
+  }
+
+  if (my_key < a.Sk) {
+    float* dkp = a.dk + (kvh + my_key) * DQK;
+    float* dvp = a.dv + (kvh + my_key) * DV;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * mt + 8 * g4 + 4 * h;
+        f32x4 cur = *(const f32x4*)(dkp + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[e] = fmaf(a.scale, dkacc[mt][4 * g4 + e], cur[e]);
+        *(f32x4*)(dkp + d) = cur;
+      }
+#pragma unroll
+    for (int mt = 0; mt < C::MTV; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * mt + 8 * g4 + 4 * h;
+        f32x4 cur = *(const f32x4*)(dvp + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[e] += dvacc[mt][4 * g4 + e];
+        *(f32x4*)(dvp + d) = cur;
+      }
+  }
+}
+
+// ---- launchers ------------------------------------------------------------------------
+hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long long rows, int Dv, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long long grid = (rows + 15) / 16;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)grid), dim3(256), 0, st, o, dout, delta, rows, Dv);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
+  using C = BCfg<DQK, DV>;
+  // dK, dV first: one workgroup per 256 keys of a (batch, KV head)
+  BwdArgs b = a;
+  b.n_tiles = (a.Sk + C::ROWS - 1) / C::ROWS;
+  long long grid = (long long)a.B * a.Hkv * b.n_tiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dQ: one workgroup per 256 query rows of a (batch, head)
+  b.n_tiles = (a.Sq + C::ROWS - 1) / C::ROWS;
+  grid = (long long)a.B * a.Hq * b.n_tiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  return hipGetLastError();
+}
+
+// Returns hipErrorInvalidValue when no kernel instance covers (dqk, dv).
+hipError_t bwd_bf16(const BwdArgs& a, int dqk, int dv, hipStream_t st) {
+  if (dqk == 128 && dv == 128) return bwd_launch<128, 128>(a, st);
+  if (dqk == 64 && dv == 64) return bwd_launch<64, 64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

@@ -171,6 +171,26 @@ struct RingTiles {
   }
 };
 
+// Arguments of the backward kernels: one (query block, KV block) pair's gradient
+// contributions, added into fp32 accumulators. BHSD layouts; lse / delta are the
+// queries' full-row values saved by (or derived from) the forward pass.
+struct BwdArgs {
+  const void* q;      // [B, Hq, Sq, Dqk]
+  const void* k;      // [B, Hkv, Sk, Dqk]
+  const void* v;      // [B, Hkv, Sk, Dv]
+  const void* dout;   // [B, Hq, Sq, Dv]
+  const float* lse;   // [B, Hq, Sq]
+  const float* delta; // [B, Hq, Sq]  rowsum(dO o O)
+  float* dq;          // [B, Hq, Sq, Dqk]  += scale * dS K
+  float* dk;          // [B, Hkv, Sk, Dqk] += scale * dS^T Q (summed over the group's heads)
+  float* dv;          // [B, Hkv, Sk, Dv]  += P^T dO
+  int B, Hq, Hkv, group, Sq, Sk;
+  long long q_pos0, k_pos0;
+  float scale, scale_log2;
+  int causal;
+  int n_tiles;        // launcher: query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+};
+
 // Arguments of the split-KV decode partial kernel.
 struct DecodeArgs {
   const __bf16* q;   // [B, Hq, D]

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 3
+#define RA_ABI_VERSION 4
 
 typedef enum {
   RA_OK = 0,
@@ -193,6 +193,39 @@ int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cach
 int ra_splitkv_partial_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
                            int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                            float* o_part, float* lse_part, void* stream);
+
+/* Backward pass. The pages run ring attention on training samples and name the
+ * backward pass's data dependencies among what a ring must get right ([RING]
+ * opening example; §什么时候值得引入 Context Parallelism); the gradients are those
+ * of the attention definition ([CH] §挑战 1), with P = exp(scale q k - LSE) from
+ * the forward's saved row LSE.
+ *
+ * delta[r] = sum_d dout[r, d] * o[r, d] in fp32, for `rows` rows of Dv values
+ * (o: the forward output, dout: its incoming gradient; bf16, device, [rows, Dv]).
+ * Errors: RA_EINVAL for null or misaligned pointers, rows < 0, Dv not a positive
+ * multiple of 8; RA_EUNSUPPORTED for a dtype other than RA_BF16. */
+int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,
+                           void* stream);
+
+/* One backward ring step: adds one (query block, KV block) pair's gradient
+ * contributions to fp32 accumulators (which the caller zero-initialises):
+ *   dv_acc += P^T dout,  dS = P o (dout V^T - delta),
+ *   dq_acc += scale dS K, dk_acc += scale dS^T Q   (dk/dv summed over each KV
+ *   head's query heads),  P = exp(scale Q K^T - lse) on the visible keys.
+ *   q, dout  device [B, Hq,  Sq, Dqk / Dv] bf16, queries at global positions q_pos0 ..
+ *   lse, delta device [B, Hq, Sq] fp32: the queries' full-row LSE (forward output)
+ *            and delta (ra_attn_bwd_preprocess); a row with LSE = -inf adds nothing
+ *   k_blk, v_blk device [B, Hkv, Sk, Dqk / Dv] bf16, keys at global positions k_pos0 ..
+ *   dq_acc [B, Hq, Sq, Dqk], dk_acc [B, Hkv, Sk, Dqk], dv_acc [B, Hkv, Sk, Dv] fp32 (in/out)
+ * A ring backward is this step for every (query block, KV block) pair, in any
+ * order, with dk_acc / dv_acc travelling with their block. Two launches (dK/dV,
+ * then dQ) on the stream. Supported: RA_BF16 with (Dqk, Dv) in {(64,64),
+ * (128,128)}. Errors as ra_block_attn_step. The accumulators must not overlap the
+ * inputs or each other. */
+int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
+                           long long q_pos0, int Sq, const void* k_blk, const void* v_blk, long long k_pos0, int Sk,
+                           int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal, float* dq_acc,
+                           float* dk_acc, float* dv_acc, void* stream);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version(ra):
-    assert ra.abi_version() == 3
+    assert ra.abi_version() == 4
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 13])
@@ -121,6 +121,18 @@ def test_step_merge_decode_validation(ra):
                                       None) == 2
     assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1e30, 1.0, 1, 8, 2, 64, 128, 128, 2, 1e10, FAKE, FAKE,
                                       None) == 1
+    # backward: unsupported dims and dtypes, bad sizes
+    bw = lambda **kw: lib.ra_block_attn_bwd_step(*dict(dict(
+        dtype=1, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, q_pos0=0, Sq=64, k=FAKE, v=FAKE, k_pos0=0, Sk=64, B=1,
+        Hq=2, Hkv=2, Dqk=128, Dv=128, scale=0.1, causal=1, dq=FAKE, dk=FAKE, dv=FAKE, stream=None), **kw).values())
+    assert bw(Dqk=192, Dv=128) == 2
+    assert bw(dtype=0) == 2
+    assert bw(Sq=0) == 1
+    assert bw(q=None) == 1
+    assert bw(Hkv=3) == 1
+    assert lib.ra_attn_bwd_preprocess(0, FAKE, FAKE, 10, 128, FAKE, None) == 2
+    assert lib.ra_attn_bwd_preprocess(1, FAKE, FAKE, 10, 12, FAKE, None) == 1
+    assert lib.ra_attn_bwd_preprocess(1, FAKE, FAKE, 0, 128, FAKE, None) == 0
     # merges: zero rows is a no-op; bad Dv rejected
     assert lib.ra_lse_merge(0, 128, None, None, None, None, None, None, None) == 0
     assert lib.ra_lse_merge(10, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1

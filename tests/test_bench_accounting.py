@@ -31,6 +31,15 @@ def test_partition_pairs_match_oracle_accounting():
     assert abs(r - 1.875) < 1e-3
 
 
+def test_backward_flops():
+    # five products per visible pair: 2 (3 Dqk + 2 Dv); 2.5x the forward at Dqk = Dv
+    c = CONFIGS["C3"]
+    assert bench.backward_flops(c) * 2 == bench.prefill_flops(c) * 5
+    c4 = CONFIGS["C4"]
+    pairs = bench.prefill_flops(c4) // (2 * (192 + 128))
+    assert bench.backward_flops(c4) == pairs * 2 * (3 * 192 + 2 * 128)
+
+
 def test_decode_bytes():
     c = CONFIGS["C5"]
     kv = oracle.kv_cache_bytes(layers=1, h_kv=c.Hkv, d_h=c.Dqk, n=c.L, bytes_per_value=2, batch=c.B)
