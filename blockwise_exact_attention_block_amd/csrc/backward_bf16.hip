@@ -78,9 +78,18 @@ bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
-  const int qt = blockIdx.x % a.n_tiles;
-  const int bh = blockIdx.x / a.n_tiles;
-  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / a.group;
+  // XCD-aware order (as the forward): XCD x runs the x-th eighth of the work list
+  // (batch, KV head, query tile from the last, query head of the group), so the
+  // co-resident workgroups of an XCD stream the same K/V tiles through its L2.
+  const int n_items = a.B * a.Hq * a.n_tiles;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_items) return;
+  const int w = u % a.group, rest = u / a.group;
+  const int qt = a.n_tiles - 1 - rest % a.n_tiles;
+  const int bgi = rest / a.n_tiles;
+  const int b = bgi / a.Hkv, g = bgi - b * a.Hkv, hq = g * a.group + w;
+  const int bh = b * a.Hq + hq;
   const int row_base = qt * C::ROWS;
   const int last_row = min(row_base + C::ROWS, a.Sq) - 1;
   long long kmax = a.Sk;
@@ -247,8 +256,15 @@ bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
-  const int ktile = blockIdx.x % a.n_tiles;
-  const int bg = blockIdx.x / a.n_tiles;
+  // XCD-aware order: XCD x runs the x-th eighth of the work list (batch, KV head,
+  // key tile), so its co-resident workgroups stream the same Q / dO tiles through
+  // its L2; under a causal mask the first key tiles (the most queries) go first.
+  const int n_items = a.B * a.Hkv * a.n_tiles;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= n_items) return;
+  const int ktile = u % a.n_tiles;
+  const int bg = u / a.n_tiles;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int key_base = ktile * C::ROWS;
 
@@ -466,15 +482,15 @@ static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
   // dK, dV first: one workgroup per 256 keys of a (batch, KV head)
   BwdArgs b = a;
   b.n_tiles = (a.Sk + C::ROWS - 1) / C::ROWS;
-  long long grid = (long long)a.B * a.Hkv * b.n_tiles;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long grid = 8 * (((long long)a.B * a.Hkv * b.n_tiles + 7) / 8);   // whole rounds of the 8 XCDs
+  if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
   if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dQ: one workgroup per 256 query rows of a (batch, head)
   b.n_tiles = (a.Sq + C::ROWS - 1) / C::ROWS;
-  grid = (long long)a.B * a.Hq * b.n_tiles;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  grid = 8 * (((long long)a.B * a.Hq * b.n_tiles + 7) / 8);
+  if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
   if (grid > 0) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
   return hipGetLastError();
 }
