@@ -154,3 +154,32 @@ def test_ring_backward_protocol_equals_whole(ra, causal):
     grad_close(rq, ref[0], "ring dq")
     grad_close(rk, ref[1], "ring dk")
     grad_close(rv, ref[2], "ring dv")
+
+
+def test_striped_ring_backward_with_virtual_positions(ra):
+    """Striped layout: every (partition i, block j) step uses the virtual positions
+    of the striped mask (query: local row, key: local index + [j > i]). The
+    accumulated gradients, taken back to natural order, are the exact gradients of
+    the natural-order sequence."""
+    B, Hq, Hkv, Sp, P, D = 1, 4, 2, 120, 4, 128
+    S = Sp * P
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=901, dtype="bf16")
+    do = randn_np((B, Hq, S, D), 902, "bf16")
+    st = lambda x: np.concatenate([x[:, :, p::P] for p in range(P)], axis=2)
+    dq_, dk_, dv_, ddo = (to_dev(st(x)) for x in (q, k, v, do))
+    o, lse = ra.ring_attn_fwd(dq_, dk_, dv_, P=P, causal=True, layout="striped")
+    delta = ra.attn_bwd_preprocess(o, ddo)
+    part = lambda t, i: t[:, :, i * Sp:(i + 1) * Sp].contiguous()
+    dqs = [torch.zeros((B, Hq, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    dks = [torch.zeros((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    dvs = [torch.zeros((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    for i in range(P):
+        for j, _ in ra.ring_schedule(P, i, True, "striped"):
+            ra.block_attn_bwd_step(part(dq_, i), part(ddo, i), part(lse, i), part(delta, i), part(dk_, j),
+                                   part(dv_, j), dqs[i], dks[j], dvs[j], q_pos0=0, k_pos0=1 if j > i else 0,
+                                   causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, _ = oracle.attention_bwd(q, k, v, do, scale=1 / math.sqrt(D), causal=True)
+    grad_close(torch.cat(dqs, 2), st(rq), "striped dq")
+    grad_close(torch.cat(dks, 2), st(rk), "striped dk")
+    grad_close(torch.cat(dvs, 2), st(rv), "striped dv")
