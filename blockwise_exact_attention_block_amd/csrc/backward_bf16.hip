@@ -53,14 +53,16 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
   if (row < rows && L == 0) delta[row] = acc;
 }
 
-// LDS row strides (elements): +8 keeps 16-byte rows starting on different banks
+// LDS row strides (elements). K (dQ kernel), Q and dO (dK/dV kernel) are read both
+// as 16-byte rows and transposed; a pad of 16 elements suits the mix (measured).
+// V is only read as rows: a pad of 8 starts 16 consecutive rows on different banks.
 template <int DQK, int DV>
 struct BCfg {
   static constexpr int THREADS = 512;               // 8 waves
   static constexpr int ROWS = 256;                  // query rows (dQ) / keys (dK, dV) per workgroup
   static constexpr int BK = 64;                     // keys per LDS tile (dQ kernel)
   static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
-  static constexpr int KS = DQK + 8, VS = DV + 8;
+  static constexpr int KS = DQK + 16, VS = DV + 8, OS = DV + 16;
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
   static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
 };
@@ -244,7 +246,7 @@ __global__ void __launch_bounds__(512)
 bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<DQK, DV>;
   constexpr int BQ = C::BQ;
-  constexpr int QS = C::KS, OS = C::VS;   // Q rows like K rows, dO rows like V rows
+  constexpr int QS = C::KS, OS = C::OS;   // Q rows like K rows
   constexpr int QCH = BQ * DQK / 8 / C::THREADS, OCH = BQ * DV / 8 / C::THREADS;
   constexpr int VCH = C::ROWS * DV / 8 / C::THREADS;
   static_assert(QCH * C::THREADS * 8 == BQ * DQK && OCH * C::THREADS * 8 == BQ * DV, "tile split");
