@@ -150,3 +150,64 @@ def test_c5f_fp8_cache_every_row_and_partial(ra):
         worst = [max(worst[0], d1[0]), max(worst[1], d1[1]), max(worst[2], d2[0]), max(worst[3], d2[1])]
     say(f"C5F: partials max|dO| {worst[0]:.3e} |dLSE| {worst[1]:.3e}; merged max|dO| {worst[2]:.3e} "
         f"|dLSE| {worst[3]:.3e}")
+
+
+@pytest.mark.timeout(900)
+def test_c3_backward_sampled_rows_and_keys(ra):
+    """Backward at the full C3 shape, in the launch configuration bench.py times.
+    dQ rows: exact gradients (the oracle's forward statistics of each sampled row
+    over its whole causal key range). dK / dV keys: the definition of one key's
+    gradient summed over every query of its group that sees it, given the GPU's
+    saved row LSE and delta (the step's inputs, checked themselves above)."""
+    cfg = CONFIGS["C3"]
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    o, lse = run_prefill(ra, cfg, q, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 7)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    say(f"attn_bwd {cfg.name} (whole sequence)")
+    dq, dk, dv = ra.attn_bwd(q, k, v, o, lse, dout, causal=True, scale=cfg.scale)
+    delta = ra.attn_bwd_preprocess(o, dout)
+    torch.cuda.synchronize()
+    del o
+    group = cfg.Hq // cfg.Hkv
+    rng = np.random.default_rng(cfg.seed + 11)
+    worst = 0.0
+    # dQ of sampled rows, exact
+    for g in (0, cfg.Hkv - 1):
+        k_np, v_np = k[0, g].float().cpu().numpy(), v[0, g].float().cpu().numpy()
+        for h in (g * group, g * group + group - 1):
+            rows = np.unique(np.concatenate([rng.integers(0, cfg.Sq, 6), [0, cfg.Sq - 1, cfg.Sp, cfg.Sp - 1]]))
+            rt = torch.as_tensor(rows, device=DEV)
+            qr = q[0, h, rt].float().cpu().numpy()
+            dr = dout[0, h, rt].float().cpu().numpy()
+            o_r, l_r = oracle.attention_rows(qr, rows, k_np, v_np, scale=cfg.scale, causal=True)
+            d_r = (dr * o_r).sum(-1)
+            ref, _, _ = oracle.block_bwd(qr[None, None], k_np[None, None], v_np[None, None], dr[None, None],
+                                         l_r[None, None], d_r[None, None], scale=cfg.scale, causal=True,
+                                         q_pos=rows, k_pos0=0)
+            got = dq[0, h, rt].double().cpu().numpy()
+            err = np.abs(got - ref[0, 0]).max() / np.abs(ref[0, 0]).max()
+            worst = max(worst, err)
+            assert err <= 2e-2, (g, h, err)
+    # dK, dV of sampled keys, given the saved row statistics
+    for g in (0, cfg.Hkv // 2):
+        keys = np.unique(np.concatenate([rng.integers(0, cfg.S, 3), [0, cfg.S - 1]]))
+        kt = torch.as_tensor(keys, device=DEV)
+        k_s = k[0, g, kt].float().cpu().numpy()
+        v_s = v[0, g, kt].float().cpu().numpy()
+        ref_k = np.zeros_like(k_s, dtype=np.float64)
+        ref_v = np.zeros_like(v_s, dtype=np.float64)
+        for h in range(g * group, (g + 1) * group):
+            qh = q[0, h].float().cpu().numpy()
+            dh = dout[0, h].float().cpu().numpy()
+            _, gk, gv = oracle.block_bwd(qh[None, None], k_s[None, None], v_s[None, None], dh[None, None],
+                                         lse[0, h].double().cpu().numpy()[None, None],
+                                         delta[0, h].double().cpu().numpy()[None, None], scale=cfg.scale,
+                                         causal=True, q_pos0=0, k_pos=keys)
+            ref_k += gk[0, 0]
+            ref_v += gv[0, 0]
+        for got, ref, name in ((dk[0, g, kt], ref_k, "dk"), (dv[0, g, kt], ref_v, "dv")):
+            err = np.abs(got.double().cpu().numpy() - ref).max() / np.abs(ref).max()
+            worst = max(worst, err)
+            assert err <= 2e-2, (name, g, err)
+    say(f"C3 backward: worst relative max error {worst:.3e}")
