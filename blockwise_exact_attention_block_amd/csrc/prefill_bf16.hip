@@ -327,8 +327,15 @@ prefill_bf16_kernel(PrefillArgs a) {
     const long long wave_pos1 = wave_pos0 + NQ * 32 - 1;
     const bool skip = a.causal && t.pos0 > wave_pos1;
     const bool need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
+    // With 64-key tiles the next tile's LDS store goes before this tile's work (its
+    // buffer was last read before the previous barrier), so it overlaps the
+    // products; with 128-key tiles it goes after (measured either way).
+    if (BK == 64 && n + 1 < ntiles) {
+      store_tile(buf ^ 1);
+      if (n + 2 < ntiles) load_tile(n + 2);
+    }
     if (!skip) compute_tile(buf, t, need_mask);
-    if (n + 1 < ntiles) {
+    if (BK != 64 && n + 1 < ntiles) {
       store_tile(buf ^ 1);
       if (n + 2 < ntiles) load_tile(n + 2);
     }
