@@ -17,9 +17,9 @@
 //   * bwd_delta_kernel: delta = rowsum(dO o O) per query row.
 //   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
 //     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column);
-//     K and V tiles of 64 keys are staged in LDS. Per 32 keys: S^T = K Q^T and
+//     K and V tiles are staged in LDS (double buffered). Per 32 keys: S^T = K Q^T and
 //     dP^T = V dO^T (lane-local LSE and delta), dS^T, then dQ^T += K^T dS^T with
-//     K^T read through ds_read_b64_tr_b16.
+//     K^T read through ds_read_b64_tr_b16. K / V tiles are 128 keys.
 //   * bwd_dkdv_kernel: one workgroup per 256 keys of one (batch, KV head), 8 waves
 //     of 32 keys, looping over the group's query heads and the visible query tiles
 //     (64 rows, staged in LDS with their LSE and delta). K rows stay in VGPRs as the
@@ -60,7 +60,7 @@ template <int DQK, int DV>
 struct BCfg {
   static constexpr int THREADS = 512;               // 8 waves
   static constexpr int ROWS = 256;                  // query rows (dQ) / keys (dK, dV) per workgroup
-  static constexpr int BK = 64;                     // keys per LDS tile (dQ kernel)
+  static constexpr int BK = 128;                    // keys per LDS tile (dQ kernel)
   static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
   static constexpr int KS = DQK + 16, VS = DV + 8, OS = DV + 16;
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
