@@ -38,6 +38,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// The same read at a 32-bit LDS byte address.
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(unsigned addr) {
+  lds_bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((RA_LDS lds_bf16x4_t*)(uintptr_t)addr);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -62,6 +68,33 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nbytes, 0x00020000);
 }
+// Buffer descriptor words of make_rsrc, as four scalars for inline asm.
+__device__ __forceinline__ u32x4 raw_desc(const void* base, unsigned nbytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4 r;
+  r[0] = (unsigned)p;
+  r[1] = (unsigned)(p >> 32) & 0xffffu;   // stride 0
+  r[2] = nbytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+// 32-bit LDS byte address of a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(RA_LDS const void*)p;
+}
+// 16 bytes per lane from a raw buffer straight into LDS (buffer_load ... lds): lane
+// i's bytes land at lds_base + 16 * i, whatever its global offset; lds_base is
+// wave-uniform and goes through M0, which nothing else in these kernels uses. It is
+// issued from asm so that the compiler does not hold its own LDS reads of other
+// buffers behind it. The data is visible only after wait_vmem() on the issuing wave
+// and a barrier.
+__device__ __forceinline__ void lds_load16(unsigned lds_base, unsigned byte_off, u32x4 desc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(byte_off), "s"(desc) : "memory");
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). As a builtin, the
+// compiler's own wait tracking sees it, so it adds no waits of its own later on.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);

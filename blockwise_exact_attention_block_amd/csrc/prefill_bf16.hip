@@ -19,8 +19,11 @@
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
 //     (v_permlane32_swap).
 //   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
-//     tiles fit in LDS) go HBM -> VGPR (raw buffer loads, prefetched two tiles
-//     ahead) -> LDS (double buffered, rows padded against bank conflicts).
+//     tiles fit in LDS) are double buffered in LDS. At D = 128 they go straight from
+//     HBM into LDS (buffer_load ... lds, one tile ahead) as unpadded 256-byte rows
+//     whose 16-byte chunks are XOR-swizzled against bank conflicts; the other head
+//     dims go HBM -> VGPR (raw buffer loads, two tiles ahead) -> LDS rows padded
+//     against bank conflicts.
 //   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
 //     blocks), the tile's row max, one correction factor, then exp2 and PV.
 //   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
@@ -30,6 +33,7 @@
 //   * The output accumulator O^T keeps one query per lane column, so rescaling by
 //     the running-max correction is a per-lane multiply.
 #include "common.hpp"
+#include <type_traits>
 
 namespace ra {
 
@@ -44,11 +48,14 @@ struct PCfg {
   static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
   static constexpr int KCH = BK * DQK / 8 / THREADS;  // 16-byte K chunks per thread per tile
   static constexpr int VCH = BK * DV / 8 / THREADS;
-  // LDS rows are padded so that each lane's reads are a per-lane base plus a
-  // compile-time offset, and consecutive K rows (16-byte reads) and V rows
-  // (transposed 8-byte reads) start on different banks.
-  static constexpr int KS = DQK + 8;
-  static constexpr int VS = DV + 32;
+  // D = 128: tiles go HBM -> LDS directly (buffer loads into LDS) as unpadded rows
+  // with an XOR swizzle of 16-byte chunks. Other head dims stage through VGPRs into
+  // LDS rows padded so that consecutive K rows (16-byte reads) and V rows
+  // (transposed 8-byte reads) start on different banks. Either way each lane's
+  // reads are a per-lane base plus a compile-time offset.
+  static constexpr bool DMA = DQK == 128 && DV == 128;
+  static constexpr int KS = DMA ? DQK : DQK + 8;
+  static constexpr int VS = DMA ? DV : DV + 32;
   static constexpr int K_TILE = BK * KS;
   static constexpr int V_TILE = BK * VS;
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
@@ -136,7 +143,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (kmax <= 0) return;  // no key of this block is visible: state stays as it is
     ntiles = (int)((kmax + BK - 1) / BK);
   }
-  auto tile_ref = [&](int n) -> TileRef {
+  auto tile_ref = [&](int n) __attribute__((always_inline)) -> TileRef {
     TileRef t;
     if (MODE == MODE_RING) {
       ring.tile(n, t.row0, t.pos0, t.nvalid);
@@ -150,7 +157,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- global -> register -> LDS staging ---------------------------------------
   uint4 kr[C::KCH], vr[C::VCH];
-  auto load_tile = [&](int n) {
+  auto load_tile = [&](int n) __attribute__((always_inline)) {
     const TileRef t = tile_ref(n);
 #pragma unroll
     for (int it = 0; it < C::KCH; ++it) {
@@ -165,7 +172,7 @@ prefill_bf16_kernel(PrefillArgs a) {
       vr[it] = buf_load16(vrs, (unsigned)((t.row0 + row) * DV + col * 8) * 2u);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < C::KCH; ++it) {
       const int c = it * C::THREADS + tid;
@@ -177,6 +184,45 @@ prefill_bf16_kernel(PrefillArgs a) {
       const int c = it * C::THREADS + tid;
       const int row = c / (DV / 8), col = c % (DV / 8);
       *(uint4*)&vs[buf][row * C::VS + col * 8] = vr[it];
+    }
+  };
+
+  // ---- direct HBM -> LDS tiles (D = 128) ---------------------------------------------
+  // A 256-byte row holds 16 chunks of 16 bytes; chunk c of row r sits in slot
+  // c ^ swz(r). swz is a bijection on 16 consecutive rows (conflict-free K reads of
+  // one chunk across 16 rows) and, on the 4 rows x 2 chunk pairs that a half wave's
+  // transposed V read touches, puts every pair on its own 8 banks.
+  auto swz = [](int r) __attribute__((always_inline)) {
+    const int x = r & 7;
+    return ((((x & 3) << 1) | (x >> 2)) << 1) | ((r >> 3) & 1);
+  };
+  constexpr int ROWB = DQK * 2;
+  constexpr int NI = C::DMA ? BK * ROWB / 1024 / NW : 1;   // 1 KB loads per wave per tile
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  unsigned dgo[NI];
+  if constexpr (C::DMA) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int row = wave * (BK / NW) + 4 * j + (lane >> 4);
+      dgo[j] = (unsigned)(row * ROWB + 16 * ((lane & 15) ^ swz(row)));
+    }
+  }
+  const unsigned kv_bytes_last = (unsigned)((size_t)a.kv_rows * ROWB - 16);
+  const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
+  const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
+  const unsigned k_lds = lds_addr(&ks[0][0]), v_lds = lds_addr(&vs[0][0]);
+  auto dma_tile = [&](int n, int buf) __attribute__((always_inline)) {
+    if constexpr (C::DMA) {
+      const TileRef t = tile_ref(n);
+      const unsigned base = (unsigned)t.row0 * ROWB;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        // rows past the slab re-read its last chunk: finite values under the mask
+        const unsigned off = min(base + dgo[j], kv_bytes_last);
+        const unsigned dst = (unsigned)((buf * C::K_TILE + (wave_u * (BK / NW) + 4 * j) * DQK) * 2);
+        lds_load16(k_lds + dst, off, kdesc);
+        lds_load16(v_lds + dst, off, vdesc);
+      }
     }
   };
 
@@ -218,7 +264,32 @@ prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- one KV tile: S for all its keys, one online-softmax update, then PV --------
   const int gg = lane >> 4, L = lane & 15;
-  auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) {
+  // swizzled LDS byte addresses inside a tile: K chunk 2s+h of row l32, and the
+  // transposed V read of row 8x + r4, column block mt
+  unsigned kra[C::DS], vra[2][C::MT];
+  if constexpr (C::DMA) {
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      kra[s] = k_lds + (unsigned)(l32 * ROWB + 16 * ((2 * s + h) ^ swz(l32)));
+      asm volatile("" : "+v"(kra[s]));   // keep the lane base in a register: tile offsets stay immediates
+    }
+    const int r4 = 4 * (gg >> 1) + (L >> 2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int c = 4 * mt + 2 * (gg & 1) + ((L >> 1) & 1);
+        vra[x][mt] = v_lds + (unsigned)((8 * x + r4) * ROWB + 16 * (c ^ swz(8 * x + r4)) + 8 * (L & 1));
+        asm volatile("" : "+v"(vra[x][mt]));
+      }
+  }
+  auto kfrag = [&](int buf, int krow0, int s) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (C::DMA)
+      return *(RA_LDS const bf16x8*)(uintptr_t)(kra[s] + (unsigned)(buf * C::K_TILE * 2 + krow0 * ROWB));
+    else
+      return *(const bf16x8*)&ks[buf][(krow0 + l32) * C::KS + 16 * s + 8 * h];
+  };
+  auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) __attribute__((always_inline)) {
     static_assert(NQ == 1, "one 32-row query block per wave");
     constexpr int NS = BK / 32;   // 32-key blocks of the S^T accumulator
     f32x16 sacc[NS];
@@ -226,16 +297,15 @@ prefill_bf16_kernel(PrefillArgs a) {
     // the current block's products have been issued
     bf16x8 kf[C::DS];
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][l32 * C::KS + 16 * s + 8 * h];
+    for (int s = 0; s < C::DS; ++s) kf[s] = kfrag(buf, 0, s);
 #pragma unroll
     for (int kt = 0; kt < NS; ++kt) {
       sacc[kt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) sacc[kt] = mfma32(kf[s], qf[0][s], sacc[kt]);
       if (kt + 1 < NS) {
-        const int krow = (kt + 1) * 32 + l32;
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) kf[s] = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h];
+        for (int s = 0; s < C::DS; ++s) kf[s] = kfrag(buf, (kt + 1) * 32, s);
       }
     }
     if (need_mask) {
@@ -308,8 +378,12 @@ prefill_bf16_kernel(PrefillArgs a) {
           bf16x4 half2[2];
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-            half2[x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
+            if constexpr (C::DMA) {
+              half2[x] = lds_read_tr16_at(vra[x][mt] + (unsigned)(buf * C::V_TILE * 2 + (kt * 32 + 16 * t2) * ROWB));
+            } else {
+              const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+              half2[x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
+            }
           }
           oacc[0][mt] = mfma32(cat(half2[0], half2[1]), pb[kt][t2], oacc[0][mt]);
         }
@@ -317,29 +391,56 @@ prefill_bf16_kernel(PrefillArgs a) {
   };
 
   // ---- pipelined tile loop -------------------------------------------------------
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if (ntiles > 1) load_tile(1);
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    const TileRef t = tile_ref(n);
-    const long long wave_pos1 = wave_pos0 + NQ * 32 - 1;
-    const bool skip = a.causal && t.pos0 > wave_pos1;
-    const bool need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
-    // With 64-key tiles the next tile's LDS store goes before this tile's work (its
-    // buffer was last read before the previous barrier), so it overlaps the
-    // products; with 128-key tiles it goes after (measured either way).
-    if (BK == 64 && n + 1 < ntiles) {
-      store_tile(buf ^ 1);
-      if (n + 2 < ntiles) load_tile(n + 2);
-    }
-    if (!skip) compute_tile(buf, t, need_mask);
-    if (BK != 64 && n + 1 < ntiles) {
-      store_tile(buf ^ 1);
-      if (n + 2 < ntiles) load_tile(n + 2);
-    }
+  const long long wave_pos1 = wave_pos0 + NQ * 32 - 1;
+  auto tile_flags = [&](const TileRef& t, bool& skip, bool& need_mask) __attribute__((always_inline)) {
+    skip = a.causal && t.pos0 > wave_pos1;
+    need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
+  };
+  if constexpr (C::DMA) {
+    // tile n+1 streams into the other buffer (last read before the previous
+    // barrier) while tile n is computed; the loop is unrolled by two so that every
+    // LDS address is a lane base plus an immediate
+    dma_tile(0, 0);
+    wait_vmem();
     __syncthreads();
+    auto step = [&](int n, auto bufc) __attribute__((always_inline)) {
+      constexpr int buf = decltype(bufc)::value;
+      const TileRef t = tile_ref(n);
+      bool skip, need_mask;
+      tile_flags(t, skip, need_mask);
+      if (n + 1 < ntiles) dma_tile(n + 1, buf ^ 1);
+      if (!skip) compute_tile(buf, t, need_mask);
+      wait_vmem();   // this wave's loads of tile n+1 have landed
+      __syncthreads();
+    };
+    for (int n = 0; n < ntiles; n += 2) {
+      step(n, std::integral_constant<int, 0>{});
+      if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    if (ntiles > 1) load_tile(1);
+    for (int n = 0; n < ntiles; ++n) {
+      const int buf = n & 1;
+      const TileRef t = tile_ref(n);
+      bool skip, need_mask;
+      tile_flags(t, skip, need_mask);
+      // With 64-key tiles the next tile's LDS store goes before this tile's work (its
+      // buffer was last read before the previous barrier), so it overlaps the
+      // products; with 128-key tiles it goes after (measured either way).
+      if (BK == 64 && n + 1 < ntiles) {
+        store_tile(buf ^ 1);
+        if (n + 2 < ntiles) load_tile(n + 2);
+      }
+      if (!skip) compute_tile(buf, t, need_mask);
+      if (BK != 64 && n + 1 < ntiles) {
+        store_tile(buf ^ 1);
+        if (n + 2 < ntiles) load_tile(n + 2);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------------
