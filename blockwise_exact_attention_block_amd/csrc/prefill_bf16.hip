@@ -17,7 +17,8 @@
 //   * Q rows of the wave are loaded once into VGPRs as the B operand of
 //     S^T = K Q^T, so each lane owns one query column of the score tile and the row
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
-//     (v_permlane32_swap).
+//     (v_permlane32_swap). They are multiplied by scale * log2(e) on loading
+//     (rounded to bf16), so the products are scores in the exp2 domain.
 //   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
 //     tiles fit in LDS) are double buffered in LDS. At D = 128 they go straight from
 //     HBM into LDS (buffer_load ... lds, one tile ahead) as unpadded 256-byte rows
@@ -25,19 +26,30 @@
 //     dims go HBM -> VGPR (raw buffer loads, two tiles ahead) -> LDS rows padded
 //     against bank conflicts.
 //   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
-//     blocks), the tile's row max, one correction factor, then exp2 and PV.
+//     blocks), the tile's row max, then exp2 and PV. Each row carries a reference
+//     shift m, and the products start from -m (the MFMA's C operand), so they come
+//     out as x - m and P = exp2 of the accumulator, with no per-score arithmetic.
+//     m is set to the row max on the row's first visible tile. After that it moves
+//     only when a score of the tile exceeds it by more than kLazyShift; then the
+//     accumulator and the exp-sum are rescaled once. Otherwise P <= 2^kLazyShift,
+//     far from fp32 and bf16 limits. Softmax does not depend on the shift, so the
+//     result is the same for any m.
 //   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
 //     (converted to bf16, round to nearest even). V^T operands come from the
 //     natural [key][d] LDS tile through ds_read_b64_tr_b16, with the key order
 //     inside each 16-key step matching the accumulator's row order.
 //   * The output accumulator O^T keeps one query per lane column, so rescaling by
-//     the running-max correction is a per-lane multiply.
+//     the shift's correction is a per-lane multiply.
 #include "common.hpp"
 #include <type_traits>
 
 namespace ra {
 
 enum { MODE_RING = 0, MODE_STEP = 1 };
+
+// Largest lead (log2 units) of a score over its row's reference shift before the
+// shift is moved: P stays below 2^8 between moves.
+constexpr float kLazyShift = 8.0f;
 
 template <int DQK, int DV, int NQ, int NW>
 struct PCfg {
@@ -231,6 +243,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   const long long wave_pos0 = pos_base + wave * NQ * 32;
   bf16x8 qf[NQ][C::DS];
   float m[NQ], l[NQ];
+  bool fresh[NQ];   // the row has no keys yet: its first visible tile sets m to the max
   f32x16 oacc[NQ][C::MT];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
@@ -239,8 +252,16 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < C::DS; ++s)
       qf[nq][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(row * DQK + 16 * s + 8 * h) * 2u));
-    m[nq] = kNegInf;
+    // scores come out of the products already in the exp2 domain: q * scale * log2(e)
+#pragma unroll
+    for (int s = 0; s < C::DS; ++s) {
+      f32x8 x = __builtin_convertvector(qf[nq][s], f32x8);
+      x *= a.scale_log2;
+      qf[nq][s] = to_bf16x8(x);
+    }
+    m[nq] = 0.f;   // reference shift (exp2 domain)
     l[nq] = 0.f;
+    fresh[nq] = true;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) oacc[nq][mt] = f32x16{};
     if (MODE == MODE_STEP && valid) {
@@ -250,6 +271,7 @@ prefill_bf16_kernel(PrefillArgs a) {
       if (lin != kNegInf) {
         m[nq] = lin * kLog2e;
         l[nq] = h == 0 ? 1.f : 0.f;
+        fresh[nq] = false;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -262,6 +284,10 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
+  // -m as the products' initial accumulator: scores come out as x - m
+  f32x16 cinit;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cinit[i] = -m[0];
   // ---- one KV tile: S for all its keys, one online-softmax update, then PV --------
   const int gg = lane >> 4, L = lane & 15;
   // swizzled LDS byte addresses inside a tile: K chunk 2s+h of row l32, and the
@@ -293,19 +319,27 @@ prefill_bf16_kernel(PrefillArgs a) {
     static_assert(NQ == 1, "one 32-row query block per wave");
     constexpr int NS = BK / 32;   // 32-key blocks of the S^T accumulator
     f32x16 sacc[NS];
-    // K fragments of key block kt; the next block's are read from LDS as soon as
-    // the current block's products have been issued
-    bf16x8 kf[C::DS];
+    // D step outer, key block inner: each step issues NS independent MFMAs, and the
+    // next step's NS K fragments are read from LDS while they run (the scheduling
+    // barriers keep the compiler from trading that lead for registers)
+    bf16x8 kc[NS], kn[NS];
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) kf[s] = kfrag(buf, 0, s);
+    for (int kt = 0; kt < NS; ++kt) kc[kt] = kfrag(buf, kt * 32, 0);
 #pragma unroll
-    for (int kt = 0; kt < NS; ++kt) {
-      sacc[kt] = f32x16{};
+    for (int kt = 0; kt < NS; ++kt) sacc[kt] = cinit;
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) sacc[kt] = mfma32(kf[s], qf[0][s], sacc[kt]);
-      if (kt + 1 < NS) {
+    for (int s = 0; s < C::DS; ++s) {
+      if (s + 1 < C::DS) {
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) kf[s] = kfrag(buf, (kt + 1) * 32, s);
+        for (int kt = 0; kt < NS; ++kt) kn[kt] = kfrag(buf, kt * 32, s + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < NS; ++kt) sacc[kt] = mfma32(kc[kt], qf[0][s], sacc[kt]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < C::DS) {
+#pragma unroll
+        for (int kt = 0; kt < NS; ++kt) kc[kt] = kn[kt];
       }
     }
     if (need_mask) {
@@ -327,19 +361,33 @@ prefill_bf16_kernel(PrefillArgs a) {
         }
       }
     }
-    // running max over the whole tile (raw scores; scale > 0), in the exp2 domain
+    // the tile's row max of x - m
     float mx = sacc[0][0];
 #pragma unroll
     for (int kt = 0; kt < NS; ++kt)
 #pragma unroll
       for (int i = (kt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
     mx = row_max_halves(mx);
-    const float mnew = fmaxf(m[0], mx * a.scale_log2);
-    const float muse = mnew == kNegInf ? 0.f : mnew;   // a row with nothing visible yet
-    const float alpha = exp2_hw(m[0] - muse);
-    m[0] = mnew;
-    // P = exp2(scale*log2e*S - m), its row sum, and P^T in bf16 (round to nearest
-    // even) straight from the accumulator registers
+    // the shift moves to the tile max for rows whose scores lead it by more than
+    // kLazyShift, and for rows seeing their first keys (so that a row's dominant
+    // first key has P = 1 exactly, as with a running max). The branch is taken by
+    // the whole wave; rows that keep their shift use sh = 0.
+    const bool move = mx > kLazyShift || (fresh[0] && mx != kNegInf);
+    fresh[0] = fresh[0] && mx == kNegInf;
+    if (__any(move)) {
+      const float sh = move ? mx : 0.f;
+      m[0] += sh;
+      const float alpha = exp2_hw(-sh);
+      l[0] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) oacc[0][mt] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < NS; ++kt) sacc[kt] -= sh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cinit[i] = -m[0];
+    }
+    // P = exp2(x - m), its row sum, and P^T in bf16 (round to nearest even) straight
+    // from the accumulator registers
     bf16x8 pb[NS][2];
     float rs = 0.f;
 #pragma unroll
@@ -347,8 +395,8 @@ prefill_bf16_kernel(PrefillArgs a) {
       f32x8 p0, p1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p0[i] = exp2_hw(fmaf(sacc[kt][i], a.scale_log2, -muse));
-        p1[i] = exp2_hw(fmaf(sacc[kt][8 + i], a.scale_log2, -muse));
+        p0[i] = exp2_hw(sacc[kt][i]);
+        p1[i] = exp2_hw(sacc[kt][8 + i]);
       }
       pb[kt][0] = to_bf16x8(p0);
       pb[kt][1] = to_bf16x8(p1);
@@ -357,13 +405,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) rs += p1[i];
     }
-    l[0] = l[0] * alpha + rs;
-    // alpha is exactly 1 unless this lane's running max grew: skip the rescale
-    // when that holds for the whole wave
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) oacc[0][mt] *= alpha;
-    }
+    l[0] += rs;
     // O^T += V^T P^T, 16 keys per MFMA step. Step t2 of block kt holds, in lane
     // half h, keys 32*kt + 16*t2 + 4*h + {0..3} and 32*kt + 16*t2 + 8 + 4*h + {0..3}
     // (the accumulator rows of S^T); 16-lane group gg reads those keys for columns
