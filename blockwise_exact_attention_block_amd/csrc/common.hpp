@@ -202,6 +202,43 @@ struct RingTiles {
     pos0 = striped ? (long long)(tt * BK + shift) : (long long)j * Sp + tt * BK;
     nvalid = min(BK, Sp - tt * BK);
   }
+  // The same schedule walked one tile at a time, without divisions: block j, tile
+  // tt of the ntt tiles taken from it, key shift of the striped causal case.
+  struct Cursor {
+    int j, tt, ntt, shift;
+  };
+  __device__ __forceinline__ Cursor start() const {
+    Cursor c;
+    c.j = i;
+    c.tt = 0;
+    c.ntt = causal ? na : n_full;
+    c.shift = 0;
+    return c;
+  }
+  // Moves to the next tile; only called while tiles remain.
+  __device__ __forceinline__ void advance(Cursor& c) const {
+    if (++c.tt < c.ntt) return;
+    c.tt = 0;
+    if (!causal) {
+      c.j = (c.j == 0 ? P : c.j) - 1;
+    } else if (!striped) {
+      c.j -= 1;
+      c.ntt = n_full;
+    } else if (c.shift == 0 && c.j > 0) {
+      c.j -= 1;
+    } else if (c.shift == 0) {
+      c.j = P - 1;          // steps i+1 .. P-1 visit blocks P-1 .. i+1, one key later
+      c.ntt = nb;
+      c.shift = 1;
+    } else {
+      c.j -= 1;
+    }
+  }
+  __device__ __forceinline__ void at(const Cursor& c, int& row0, long long& pos0, int& nvalid) const {
+    row0 = c.j * Sp + c.tt * BK;
+    pos0 = striped ? (long long)(c.tt * BK + c.shift) : (long long)c.j * Sp + c.tt * BK;
+    nvalid = min(BK, Sp - c.tt * BK);
+  }
 };
 
 // Arguments of the backward kernels: one (query block, KV block) pair's gradient

@@ -155,6 +155,27 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (kmax <= 0) return;  // no key of this block is visible: state stays as it is
     ntiles = (int)((kmax + BK - 1) / BK);
   }
+  // the same tiles in order, one step at a time (no divisions on the way)
+  RingTiles::Cursor cursor;
+  if (MODE == MODE_RING) cursor = ring.start();
+  int walk_n = 0;
+  auto walk_ref = [&]() __attribute__((always_inline)) -> TileRef {
+    TileRef t;
+    if (MODE == MODE_RING) {
+      ring.at(cursor, t.row0, t.pos0, t.nvalid);
+    } else {
+      t.row0 = walk_n * BK;
+      t.pos0 = a.k_pos0 + (long long)walk_n * BK;
+      t.nvalid = min(BK, a.Sk - walk_n * BK);
+    }
+    return t;
+  };
+  auto walk_next = [&]() __attribute__((always_inline)) {
+    if (MODE == MODE_RING)
+      ring.advance(cursor);
+    else
+      ++walk_n;
+  };
   auto tile_ref = [&](int n) __attribute__((always_inline)) -> TileRef {
     TileRef t;
     if (MODE == MODE_RING) {
@@ -223,9 +244,8 @@ prefill_bf16_kernel(PrefillArgs a) {
   const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
   const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
   const unsigned k_lds = lds_addr(&ks[0][0]), v_lds = lds_addr(&vs[0][0]);
-  auto dma_tile = [&](int n, int buf) __attribute__((always_inline)) {
+  auto dma_tile = [&](const TileRef& t, int buf) __attribute__((always_inline)) {
     if constexpr (C::DMA) {
-      const TileRef t = tile_ref(n);
       const unsigned base = (unsigned)t.row0 * ROWB;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
@@ -240,7 +260,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- stationary Q fragments and running state --------------------------------
   const int wave_row0 = row_base + wave * NQ * 32;
-  const long long wave_pos0 = pos_base + wave * NQ * 32;
+  const long long wave_pos0 = pos_base + __builtin_amdgcn_readfirstlane(wave) * NQ * 32;   // wave-uniform
   bf16x8 qf[NQ][C::DS];
   float m[NQ], l[NQ];
   bool fresh[NQ];   // the row has no keys yet: its first visible tile sets m to the max
@@ -442,16 +462,22 @@ prefill_bf16_kernel(PrefillArgs a) {
     // tile n+1 streams into the other buffer (last read before the previous
     // barrier) while tile n is computed; the loop is unrolled by two so that every
     // LDS address is a lane base plus an immediate
-    dma_tile(0, 0);
+    TileRef t = walk_ref();
+    dma_tile(t, 0);
     wait_vmem();
     __syncthreads();
     auto step = [&](int n, auto bufc) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
-      const TileRef t = tile_ref(n);
       bool skip, need_mask;
       tile_flags(t, skip, need_mask);
-      if (n + 1 < ntiles) dma_tile(n + 1, buf ^ 1);
+      TileRef tn = t;
+      if (n + 1 < ntiles) {
+        walk_next();
+        tn = walk_ref();
+        dma_tile(tn, buf ^ 1);
+      }
       if (!skip) compute_tile(buf, t, need_mask);
+      t = tn;
       wait_vmem();   // this wave's loads of tile n+1 have landed
       __syncthreads();
     };
