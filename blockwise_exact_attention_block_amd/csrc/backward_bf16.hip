@@ -15,6 +15,10 @@
 //
 // Three kernels:
 //   * bwd_delta_kernel: delta = rowsum(dO o O) per query row.
+//   * Both kernels put scale * log2(e) into their stationary score operand (Q for dQ,
+//     K for dK/dV, rounded to bf16) and start the S products from -LSE * log2(e), so
+//     the accumulator is the exp2 argument of P with no per-score arithmetic; the
+//     dK/dV products of dP likewise start from -delta.
 //   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
 //     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column);
 //     K and V tiles are staged in LDS (double buffered). Per 32 keys: S^T = K Q^T and
@@ -115,6 +119,13 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < C::DSV; ++s)
     of[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
+  // Q * scale * log2(e) (rounded to bf16) makes the products scores in the exp2 domain
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s) {
+    f32x8 x = __builtin_convertvector(qf[s], f32x8);
+    x *= a.scale_log2;
+    qf[s] = to_bf16x8(x);
+  }
   // a row past the block, or with no visible key at all, gets P = 0
   float lse2 = kPosInf, dlt = 0.f;
   if (my_row < a.Sq) {
@@ -122,6 +133,10 @@ bwd_dq_kernel(BwdArgs a) {
     if (l != kNegInf) lse2 = l * kLog2e;
     dlt = a.delta[(size_t)bh * a.Sq + my_row];
   }
+  // S^T starts from -LSE, so it arrives as the exp2 argument of P
+  f32x16 s_init;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_init[i] = -lse2;
   f32x16 dqacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) dqacc[mt] = f32x16{};
@@ -157,7 +172,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
       const int krow = kt * 32 + l32;
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      f32x16 st = s_init, dpt = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h], qf[s], st);
 #pragma unroll
@@ -183,8 +198,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          const float p = exp2_hw(fmaf(st[i], a.scale_log2, -lse2));
-          x[e] = p * (dpt[i] - dlt);
+          x[e] = exp2_hw(st[i]) * (dpt[i] - dlt);
         }
         dsb[t2] = to_bf16x8(x);
       }
@@ -293,6 +307,13 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < C::DS; ++s)
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
+  // K * scale * log2(e) (rounded to bf16): the products are scores in the exp2 domain
+#pragma unroll
+  for (int s = 0; s < C::DS; ++s) {
+    f32x8 x = __builtin_convertvector(kf[s], f32x8);
+    x *= a.scale_log2;
+    kf[s] = to_bf16x8(x);
+  }
   // the workgroup's V rows into LDS, once
 #pragma unroll
   for (int it = 0; it < VCH; ++it) {
@@ -306,7 +327,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   for (int mt = 0; mt < C::MTV; ++mt) dvacc[mt] = f32x16{};
 
   uint4 qr[QCH], orr[OCH];
-  float rowv = 0.f;   // threads 0..63: LSE * log2(e) of a row; 64..127: its delta
+  float rowv = 0.f;   // threads 0..63: -LSE * log2(e) of a row; 64..127: -delta
   auto tile_head = [&](int n) { return g * a.group + n / nqt; };
   auto tile_row0 = [&](int n) { return (qt0 + n % nqt) * BQ; };
   auto load_tile = [&](int n) {
@@ -327,13 +348,13 @@ bwd_dkdv_kernel(BwdArgs a) {
     if (tid < 2 * BQ) {
       const int r = row0 + (tid & (BQ - 1));
       if (tid < BQ) {
-        rowv = kPosInf;   // rows past the block, or with no visible key: P = 0
+        rowv = kNegInf;   // rows past the block, or with no visible key: P = 0
         if (r < a.Sq) {
           const float l = a.lse[bh * a.Sq + r];
-          if (l != kNegInf) rowv = l * kLog2e;
+          if (l != kNegInf) rowv = -l * kLog2e;
         }
       } else {
-        rowv = r < a.Sq ? a.delta[bh * a.Sq + r] : 0.f;
+        rowv = r < a.Sq ? -a.delta[bh * a.Sq + r] : 0.f;
       }
     }
   };
@@ -361,8 +382,24 @@ bwd_dkdv_kernel(BwdArgs a) {
       if (a.causal && qpos_s + 31 < wave_kpos0) continue;   // these queries precede all the wave's keys
       const bool need_mask = a.causal && qpos_s < wave_kpos0 + 31;
       const int qrow = qs * 32 + l32;
-      // S = Q K^T and dP = dO V^T: lane = key column, rows = queries 8*(i/4) + 4*h + i%4
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      // S = Q K^T and dP = dO V^T: lane = key column, rows = queries 8*(i/4) + 4*h + i%4.
+      // They start from the rows' -LSE * log2(e) and -delta, so S arrives as the exp2
+      // argument of P and dP as dP - delta.
+      f32x16 st, dpt;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
+        const f32x4 d0 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 d1 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st[8 * t2 + e] = l0[e];
+          st[8 * t2 + 4 + e] = l1[e];
+          dpt[8 * t2 + e] = d0[e];
+          dpt[8 * t2 + 4 + e] = d1[e];
+        }
+      }
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kf[s], st);
 #pragma unroll
@@ -380,18 +417,12 @@ bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
-        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
-        const f32x4 d0 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 4 * h];
-        const f32x4 d1 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
         f32x8 p, ds;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          const float lr = e < 4 ? l0[e] : l1[e - 4];
-          const float dr = e < 4 ? d0[e] : d1[e - 4];
-          p[e] = exp2_hw(fmaf(st[i], a.scale_log2, -lr));
-          ds[e] = p[e] * (dpt[i] - dr);
+          p[e] = exp2_hw(st[i]);
+          ds[e] = p[e] * dpt[i];
         }
         pb[t2] = to_bf16x8(p);
         dsb[t2] = to_bf16x8(ds);
