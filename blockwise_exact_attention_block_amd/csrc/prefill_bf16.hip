@@ -430,26 +430,38 @@ prefill_bf16_kernel(PrefillArgs a) {
     // half h, keys 32*kt + 16*t2 + 4*h + {0..3} and 32*kt + 16*t2 + 8 + 4*h + {0..3}
     // (the accumulator rows of S^T); 16-lane group gg reads those keys for columns
     // 32*mt + 16*(gg%2) + 0..15 of the V tile, transposed.
+    auto vread = [&](int it, bf16x4 (&f)[2][2]) __attribute__((always_inline)) {
+      const int kt = it / C::MT, mt = it % C::MT;
 #pragma unroll
-    for (int kt = 0; kt < NS; ++kt)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x4 half2[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            if constexpr (C::DMA) {
-              half2[x] = lds_read_tr16_at(vra[x][mt] + (unsigned)(buf * C::V_TILE * 2 + (kt * 32 + 16 * t2) * ROWB));
-            } else {
-              const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-              half2[x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
-            }
+        for (int x = 0; x < 2; ++x) {
+          if constexpr (C::DMA) {
+            f[t2][x] = lds_read_tr16_at(vra[x][mt] + (unsigned)(buf * C::V_TILE * 2 + (kt * 32 + 16 * t2) * ROWB));
+          } else {
+            const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+            const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            f[t2][x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
           }
-          oacc[0][mt] = mfma32(cat(half2[0], half2[1]), pb[kt][t2], oacc[0][mt]);
         }
-      }
+    };
+    // the V^T fragments of step (kt, mt) + 1 are read while the products of (kt, mt)
+    // run; the scheduling barriers keep that lead
+    bf16x4 vc[2][2], vn[2][2];
+    vread(0, vc);
+#pragma unroll
+    for (int it = 0; it < NS * C::MT; ++it) {
+      const int kt = it / C::MT, mt = it % C::MT;
+      if (it + 1 < NS * C::MT) vread(it + 1, vn);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) oacc[0][mt] = mfma32(cat(vc[t2][0], vc[t2][1]), pb[kt][t2], oacc[0][mt]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) vc[t2][x] = vn[t2][x];
+    }
   };
 
   // ---- pipelined tile loop -------------------------------------------------------
