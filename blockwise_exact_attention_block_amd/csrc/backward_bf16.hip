@@ -133,15 +133,34 @@ bwd_dq_kernel(BwdArgs a) {
     if (l != kNegInf) lse2 = l * kLog2e;
     dlt = a.delta[(size_t)bh * a.Sq + my_row];
   }
-  // S^T starts from -LSE, so it arrives as the exp2 argument of P
-  f32x16 s_init;
+  // S^T starts from -LSE, so it arrives as the exp2 argument of P; at D = 128, where
+  // the tiles bypass the registers, dP^T also starts from -delta
+  constexpr bool DMA = DQK == 128 && DV == 128;
+  f32x16 s_init, dp_init;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s_init[i] = -lse2;
+  for (int i = 0; i < 16; ++i) {
+    s_init[i] = -lse2;
+    dp_init[i] = DMA ? -dlt : 0.f;
+  }
   f32x16 dqacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) dqacc[mt] = f32x16{};
 
-  uint4 kr[KCH], vr[VCH];
+  // D = 128: tiles go straight from HBM into the padded LDS rows
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  PaddedTileDma<BK, DQK * 2, C::KS * 2, 8> kdma;
+  PaddedTileDma<BK, DV * 2, C::VS * 2, 8> vdma;
+  if constexpr (DMA) {
+    kdma.init(wave_u, lane);
+    vdma.init(wave_u, lane);
+  }
+  const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.Sk * DQK * 2));
+  const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.Sk * DV * 2));
+  auto dma_tile = [&](int n, int buf) {
+    kdma.issue(wave_u, lds_addr(&ks[buf][0]), (unsigned)(n * BK * DQK * 2), (unsigned)(a.Sk * DQK * 2 - 16), kdesc);
+    vdma.issue(wave_u, lds_addr(&vs[buf][0]), (unsigned)(n * BK * DV * 2), (unsigned)(a.Sk * DV * 2 - 16), vdesc);
+  };
+  uint4 kr[DMA ? 1 : KCH], vr[DMA ? 1 : VCH];
   auto load_tile = [&](int n) {
     const int row0 = n * BK;
 #pragma unroll
@@ -172,7 +191,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
       const int krow = kt * 32 + l32;
-      f32x16 st = s_init, dpt = f32x16{};
+      f32x16 st = s_init, dpt = dp_init;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h], qf[s], st);
 #pragma unroll
@@ -198,7 +217,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          x[e] = exp2_hw(st[i]) * (dpt[i] - dlt);
+          x[e] = exp2_hw(st[i]) * (DMA ? dpt[i] : dpt[i] - dlt);
         }
         dsb[t2] = to_bf16x8(x);
       }
@@ -221,18 +240,27 @@ bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  if constexpr (DMA) {
+    dma_tile(0, 0);
+    wait_vmem();
+  } else {
+    load_tile(0);
+    store_tile(0);
+  }
   __syncthreads();
-  if (ntiles > 1) load_tile(1);
+  if (!DMA && ntiles > 1) load_tile(1);
   for (int n = 0; n < ntiles; ++n) {
     const int buf = n & 1;
     const long long kpos0 = a.k_pos0 + (long long)n * BK;
     const int nvalid = min(BK, a.Sk - n * BK);
+    // the other buffer was last read before the previous barrier
+    if (DMA && n + 1 < ntiles) dma_tile(n + 1, buf ^ 1);
     const bool skip = a.causal && kpos0 > wave_pos0 + 31;
     const bool need_mask = nvalid < BK || (a.causal && kpos0 + BK - 1 > wave_pos0);
     if (!skip) compute_tile(buf, kpos0, nvalid, need_mask);
-    if (n + 1 < ntiles) {
+    if (DMA) {
+      wait_vmem();   // this wave's loads of tile n+1 have landed
+    } else if (n + 1 < ntiles) {
       store_tile(buf ^ 1);
       if (n + 2 < ntiles) load_tile(n + 2);
     }

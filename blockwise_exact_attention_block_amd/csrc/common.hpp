@@ -92,6 +92,38 @@ __device__ __forceinline__ void lds_load16(unsigned lds_base, unsigned byte_off,
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(byte_off), "s"(desc) : "memory");
 }
+// Direct HBM -> LDS loads of a tile of ROWS consecutive global rows of ROW_BYTES bytes
+// into LDS rows of LDS_STRIDE bytes (the row plus padding). The LDS tile is cut into
+// 1 KB pieces, and piece j is written by one wave-wide lds_load16, whose lane i fills
+// bytes [1024 j + 16 i, +16) of the tile. It fetches the 16 global bytes that belong
+// there, or, for a slot in a row's padding, a duplicate of that row's first bytes
+// (never read). Piece j goes to wave j % NW.
+template <int ROWS, int ROW_BYTES, int LDS_STRIDE, int NW>
+struct PaddedTileDma {
+  static constexpr int PIECES = ROWS * LDS_STRIDE / 1024;
+  static constexpr int PER_WAVE = (PIECES + NW - 1) / NW;
+  static_assert(PIECES * 1024 == ROWS * LDS_STRIDE, "tile must be whole 1 KB pieces");
+  static_assert(LDS_STRIDE % 16 == 0 && ROW_BYTES % 16 == 0 && LDS_STRIDE - ROW_BYTES <= ROW_BYTES, "layout");
+  unsigned off[PER_WAVE];   // per lane: global byte offset inside the tile, per piece
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int p = (wave + q * NW) * 1024 + lane * 16;
+      const int row = p / LDS_STRIDE, within = p - row * LDS_STRIDE;
+      off[q] = (unsigned)(row * ROW_BYTES + (within < ROW_BYTES ? within : within - ROW_BYTES));
+    }
+  }
+  // wave: wave-uniform index; gbase: global byte offset of the tile's first row;
+  // glast: last valid 16-byte offset of the buffer (rows past it re-read it).
+  __device__ __forceinline__ void issue(int wave, unsigned lds_tile, unsigned gbase, unsigned glast,
+                                        u32x4 desc) const {
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+      const int j = wave + q * NW;
+      if (j < PIECES) lds_load16(lds_tile + (unsigned)j * 1024u, min(gbase + off[q], glast), desc);
+    }
+  }
+};
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). As a builtin, the
 // compiler's own wait tracking sees it, so it adds no waits of its own later on.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
