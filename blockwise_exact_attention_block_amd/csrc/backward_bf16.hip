@@ -15,10 +15,9 @@
 //
 // Three kernels:
 //   * bwd_delta_kernel: delta = rowsum(dO o O) per query row.
-//   * Both kernels put scale * log2(e) into their stationary score operand (Q for dQ,
-//     K for dK/dV, rounded to bf16) and start the S products from -LSE * log2(e), so
-//     the accumulator is the exp2 argument of P with no per-score arithmetic; the
-//     dK/dV products of dP likewise start from -delta.
+//   * Scores are exact fp32 products of the bf16 inputs; P = exp2(scale * log2(e) * s
+//     - LSE * log2(e)). The dP products start from -delta (their C operand), so they
+//     come out as dP - delta.
 //   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
 //     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column);
 //     K and V tiles are staged in LDS (double buffered). Per 32 keys: S^T = K Q^T and
@@ -119,13 +118,6 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < C::DSV; ++s)
     of[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
-  // Q * scale * log2(e) (rounded to bf16) makes the products scores in the exp2 domain
-#pragma unroll
-  for (int s = 0; s < C::DS; ++s) {
-    f32x8 x = __builtin_convertvector(qf[s], f32x8);
-    x *= a.scale_log2;
-    qf[s] = to_bf16x8(x);
-  }
   // a row past the block, or with no visible key at all, gets P = 0
   float lse2 = kPosInf, dlt = 0.f;
   if (my_row < a.Sq) {
@@ -133,15 +125,11 @@ bwd_dq_kernel(BwdArgs a) {
     if (l != kNegInf) lse2 = l * kLog2e;
     dlt = a.delta[(size_t)bh * a.Sq + my_row];
   }
-  // S^T starts from -LSE, so it arrives as the exp2 argument of P; at D = 128, where
-  // the tiles bypass the registers, dP^T also starts from -delta
+  // dP^T starts from -delta, so it comes out as dP - delta
   constexpr bool DMA = DQK == 128 && DV == 128;
-  f32x16 s_init, dp_init;
+  f32x16 dp_init;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    s_init[i] = -lse2;
-    dp_init[i] = DMA ? -dlt : 0.f;
-  }
+  for (int i = 0; i < 16; ++i) dp_init[i] = -dlt;
   f32x16 dqacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) dqacc[mt] = f32x16{};
@@ -191,7 +179,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
       const int krow = kt * 32 + l32;
-      f32x16 st = s_init, dpt = dp_init;
+      f32x16 st = f32x16{}, dpt = dp_init;
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h], qf[s], st);
 #pragma unroll
@@ -217,7 +205,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          x[e] = exp2_hw(st[i]) * (DMA ? dpt[i] : dpt[i] - dlt);
+          x[e] = exp2_hw(fmaf(st[i], a.scale_log2, -lse2)) * dpt[i];
         }
         dsb[t2] = to_bf16x8(x);
       }
@@ -335,13 +323,6 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < C::DS; ++s)
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
-  // K * scale * log2(e) (rounded to bf16): the products are scores in the exp2 domain
-#pragma unroll
-  for (int s = 0; s < C::DS; ++s) {
-    f32x8 x = __builtin_convertvector(kf[s], f32x8);
-    x *= a.scale_log2;
-    kf[s] = to_bf16x8(x);
-  }
   // the workgroup's V rows into LDS, once
 #pragma unroll
   for (int it = 0; it < VCH; ++it) {
@@ -411,19 +392,14 @@ bwd_dkdv_kernel(BwdArgs a) {
       const bool need_mask = a.causal && qpos_s < wave_kpos0 + 31;
       const int qrow = qs * 32 + l32;
       // S = Q K^T and dP = dO V^T: lane = key column, rows = queries 8*(i/4) + 4*h + i%4.
-      // They start from the rows' -LSE * log2(e) and -delta, so S arrives as the exp2
-      // argument of P and dP as dP - delta.
-      f32x16 st, dpt;
+      // dP starts from the rows' -delta, so it comes out as dP - delta.
+      f32x16 st = f32x16{}, dpt;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
-        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
         const f32x4 d0 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 4 * h];
         const f32x4 d1 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          st[8 * t2 + e] = l0[e];
-          st[8 * t2 + 4 + e] = l1[e];
           dpt[8 * t2 + e] = d0[e];
           dpt[8 * t2 + 4 + e] = d1[e];
         }
@@ -445,11 +421,14 @@ bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
+        // the rows' -LSE * log2(e)
+        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
         f32x8 p, ds;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          p[e] = exp2_hw(st[i]);
+          p[e] = exp2_hw(fmaf(st[i], a.scale_log2, e < 4 ? l0[e] : l1[e - 4]));
           ds[e] = p[e] * dpt[i];
         }
         pb[t2] = to_bf16x8(p);

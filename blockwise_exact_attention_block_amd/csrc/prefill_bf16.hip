@@ -17,8 +17,7 @@
 //   * Q rows of the wave are loaded once into VGPRs as the B operand of
 //     S^T = K Q^T, so each lane owns one query column of the score tile and the row
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
-//     (v_permlane32_swap). They are multiplied by scale * log2(e) on loading
-//     (rounded to bf16), so the products are scores in the exp2 domain.
+//     (v_permlane32_swap).
 //   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
 //     tiles fit in LDS) are double buffered in LDS. At D = 128 they go straight from
 //     HBM into LDS (buffer_load ... lds, one tile ahead) as unpadded 256-byte rows
@@ -26,14 +25,13 @@
 //     dims go HBM -> VGPR (raw buffer loads, two tiles ahead) -> LDS rows padded
 //     against bank conflicts.
 //   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
-//     blocks), the tile's row max, then exp2 and PV. Each row carries a reference
-//     shift m, and the products start from -m (the MFMA's C operand), so they come
-//     out as x - m and P = exp2 of the accumulator, with no per-score arithmetic.
-//     m is set to the row max on the row's first visible tile. After that it moves
-//     only when a score of the tile exceeds it by more than kLazyShift; then the
-//     accumulator and the exp-sum are rescaled once. Otherwise P <= 2^kLazyShift,
-//     far from fp32 and bf16 limits. Softmax does not depend on the shift, so the
-//     result is the same for any m.
+//     blocks, exact fp32 scores of the bf16 inputs), the tile's row max, then
+//     P = exp2(scale * log2(e) * s - m) and PV. Each row carries a reference shift m
+//     (exp2 domain). It is set to the row's max on its first visible tile. After
+//     that it moves only when a scaled score of the tile exceeds it by more than
+//     kLazyShift; then the accumulator and the exp-sum are rescaled once. Otherwise
+//     P <= 2^kLazyShift, far from fp32 and bf16 limits. Softmax does not depend on
+//     the shift, so the result is the same for any m.
 //   * P^T for O^T += V^T P^T is taken straight from the S^T accumulator registers
 //     (converted to bf16, round to nearest even). V^T operands come from the
 //     natural [key][d] LDS tile through ds_read_b64_tr_b16, with the key order
@@ -66,6 +64,7 @@ struct PCfg {
   // (transposed 8-byte reads) start on different banks. Either way each lane's
   // reads are a per-lane base plus a compile-time offset.
   static constexpr bool DMA = DQK == 128 && DV == 128;
+  static_assert(!DMA || DQK == DV, "the direct loads share one row layout between K and V");
   static constexpr int KS = DMA ? DQK : DQK + 8;
   static constexpr int VS = DMA ? DV : DV + 32;
   static constexpr int K_TILE = BK * KS;
@@ -251,9 +250,10 @@ prefill_bf16_kernel(PrefillArgs a) {
       for (int j = 0; j < NI; ++j) {
         // rows past the slab re-read its last chunk: finite values under the mask
         const unsigned off = min(base + dgo[j], kv_bytes_last);
-        const unsigned dst = (unsigned)((buf * C::K_TILE + (wave_u * (BK / NW) + 4 * j) * DQK) * 2);
-        lds_load16(k_lds + dst, off, kdesc);
-        lds_load16(v_lds + dst, off, vdesc);
+        // K and V rows are both 256 bytes here, so one row offset serves both tiles
+        const unsigned row_off = (unsigned)((wave_u * (BK / NW) + 4 * j) * ROWB);
+        lds_load16(k_lds + (unsigned)(buf * C::K_TILE * 2) + row_off, off, kdesc);
+        lds_load16(v_lds + (unsigned)(buf * C::V_TILE * 2) + row_off, off, vdesc);
       }
     }
   };
@@ -272,13 +272,6 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < C::DS; ++s)
       qf[nq][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(row * DQK + 16 * s + 8 * h) * 2u));
-    // scores come out of the products already in the exp2 domain: q * scale * log2(e)
-#pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
-      f32x8 x = __builtin_convertvector(qf[nq][s], f32x8);
-      x *= a.scale_log2;
-      qf[nq][s] = to_bf16x8(x);
-    }
     m[nq] = 0.f;   // reference shift (exp2 domain)
     l[nq] = 0.f;
     fresh[nq] = true;
@@ -304,10 +297,6 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // -m as the products' initial accumulator: scores come out as x - m
-  f32x16 cinit;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) cinit[i] = -m[0];
   // ---- one KV tile: S for all its keys, one online-softmax update, then PV --------
   const int gg = lane >> 4, L = lane & 15;
   // swizzled LDS byte addresses inside a tile: K chunk 2s+h of row l32, and the
@@ -346,7 +335,7 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kt = 0; kt < NS; ++kt) kc[kt] = kfrag(buf, kt * 32, 0);
 #pragma unroll
-    for (int kt = 0; kt < NS; ++kt) sacc[kt] = cinit;
+    for (int kt = 0; kt < NS; ++kt) sacc[kt] = f32x16{};
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       if (s + 1 < C::DS) {
@@ -381,7 +370,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         }
       }
     }
-    // the tile's row max of x - m
+    // the tile's row max of the raw scores (scale > 0)
     float mx = sacc[0][0];
 #pragma unroll
     for (int kt = 0; kt < NS; ++kt)
@@ -392,22 +381,19 @@ prefill_bf16_kernel(PrefillArgs a) {
     // kLazyShift, and for rows seeing their first keys (so that a row's dominant
     // first key has P = 1 exactly, as with a running max). The branch is taken by
     // the whole wave; rows that keep their shift use sh = 0.
-    const bool move = mx > kLazyShift || (fresh[0] && mx != kNegInf);
+    const float lead = mx * a.scale_log2 - m[0];   // -inf for a row with nothing visible
+    const bool move = lead > kLazyShift || (fresh[0] && mx != kNegInf);
     fresh[0] = fresh[0] && mx == kNegInf;
     if (__any(move)) {
-      const float sh = move ? mx : 0.f;
+      const float sh = move ? lead : 0.f;
       m[0] += sh;
       const float alpha = exp2_hw(-sh);
       l[0] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) oacc[0][mt] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < NS; ++kt) sacc[kt] -= sh;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cinit[i] = -m[0];
     }
-    // P = exp2(x - m), its row sum, and P^T in bf16 (round to nearest even) straight
-    // from the accumulator registers
+    // P = exp2(scale * log2(e) * s - m), its row sum, and P^T in bf16 (round to
+    // nearest even) straight from the accumulator registers
     bf16x8 pb[NS][2];
     float rs = 0.f;
 #pragma unroll
@@ -415,8 +401,8 @@ prefill_bf16_kernel(PrefillArgs a) {
       f32x8 p0, p1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p0[i] = exp2_hw(sacc[kt][i]);
-        p1[i] = exp2_hw(sacc[kt][8 + i]);
+        p0[i] = exp2_hw(fmaf(sacc[kt][i], a.scale_log2, -m[0]));
+        p1[i] = exp2_hw(fmaf(sacc[kt][8 + i], a.scale_log2, -m[0]));
       }
       pb[kt][0] = to_bf16x8(p0);
       pb[kt][1] = to_bf16x8(p1);
