@@ -19,11 +19,10 @@
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
 //     (v_permlane32_swap).
 //   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
-//     tiles fit in LDS) are double buffered in LDS. At D = 128 they go straight from
-//     HBM into LDS (buffer_load ... lds, one tile ahead) as unpadded 256-byte rows
-//     whose 16-byte chunks are XOR-swizzled against bank conflicts; the other head
-//     dims go HBM -> VGPR (raw buffer loads, two tiles ahead) -> LDS rows padded
-//     against bank conflicts.
+//     tiles fit in LDS) are double buffered in LDS and go straight from HBM into it
+//     (buffer_load ... lds, one tile ahead). At D = 128 the rows are unpadded
+//     256-byte rows whose 16-byte chunks are XOR-swizzled against bank conflicts;
+//     the other head dims keep rows padded against bank conflicts.
 //   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
 //     blocks, exact fp32 scores of the bf16 inputs), the tile's row max, then
 //     P = exp2(scale * log2(e) * s - m) and PV. Each row carries a reference shift m
@@ -56,13 +55,10 @@ struct PCfg {
   static constexpr int BK = DQK <= 128 ? 128 : 64;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
-  static constexpr int KCH = BK * DQK / 8 / THREADS;  // 16-byte K chunks per thread per tile
-  static constexpr int VCH = BK * DV / 8 / THREADS;
-  // D = 128: tiles go HBM -> LDS directly (buffer loads into LDS) as unpadded rows
-  // with an XOR swizzle of 16-byte chunks. Other head dims stage through VGPRs into
-  // LDS rows padded so that consecutive K rows (16-byte reads) and V rows
-  // (transposed 8-byte reads) start on different banks. Either way each lane's
-  // reads are a per-lane base plus a compile-time offset.
+  // D = 128: unpadded rows with an XOR swizzle of 16-byte chunks. Other head dims:
+  // rows padded so that consecutive K rows (16-byte reads) and V rows (transposed
+  // 8-byte reads) start on different banks. Either way each lane's reads are a
+  // per-lane base plus a compile-time offset.
   static constexpr bool DMA = DQK == 128 && DV == 128;
   static_assert(!DMA || DQK == DV, "the direct loads share one row layout between K and V");
   static constexpr int KS = DMA ? DQK : DQK + 8;
@@ -71,7 +67,6 @@ struct PCfg {
   static constexpr int V_TILE = BK * VS;
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
   static constexpr int MT = DV / 32;                  // 32-row output tiles along D_v
-  static_assert(KCH * THREADS * 8 == BK * DQK && VCH * THREADS * 8 == BK * DV, "tile split");
 };
 
 struct TileRef {
@@ -135,12 +130,11 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int last_row = min(row_base + C::BQ, row_end) - 1;
   const long long last_pos = pos_base + (last_row - row_base);
 
-  // Per-(batch, head) slabs as raw buffers: rows past the slab read as zero.
+  // the query slab as a raw buffer (rows past it read as zero); K / V slabs of one
+  // (batch, KV head) start at kvh rows
   const size_t kvh = (size_t)(b * a.Hkv + g) * a.kv_rows;
   const auto qrs = make_rsrc((const __bf16*)a.q + (size_t)bh * a.q_rows * DQK,
                              (unsigned)((size_t)a.q_rows * DQK * 2));
-  const auto krs = make_rsrc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
-  const auto vrs = make_rsrc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
 
   // ---- tile schedule -------------------------------------------------------------
   RingTiles ring;
@@ -175,50 +169,6 @@ prefill_bf16_kernel(PrefillArgs a) {
     else
       ++walk_n;
   };
-  auto tile_ref = [&](int n) __attribute__((always_inline)) -> TileRef {
-    TileRef t;
-    if (MODE == MODE_RING) {
-      ring.tile(n, t.row0, t.pos0, t.nvalid);
-    } else {
-      t.row0 = n * BK;
-      t.pos0 = a.k_pos0 + (long long)n * BK;
-      t.nvalid = min(BK, a.Sk - n * BK);
-    }
-    return t;
-  };
-
-  // ---- global -> register -> LDS staging ---------------------------------------
-  uint4 kr[C::KCH], vr[C::VCH];
-  auto load_tile = [&](int n) __attribute__((always_inline)) {
-    const TileRef t = tile_ref(n);
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int c = it * C::THREADS + tid;
-      const int row = c / (DQK / 8), col = c % (DQK / 8);
-      kr[it] = buf_load16(krs, (unsigned)((t.row0 + row) * DQK + col * 8) * 2u);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VCH; ++it) {
-      const int c = it * C::THREADS + tid;
-      const int row = c / (DV / 8), col = c % (DV / 8);
-      vr[it] = buf_load16(vrs, (unsigned)((t.row0 + row) * DV + col * 8) * 2u);
-    }
-  };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int c = it * C::THREADS + tid;
-      const int row = c / (DQK / 8), col = c % (DQK / 8);
-      *(uint4*)&ks[buf][row * C::KS + col * 8] = kr[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VCH; ++it) {
-      const int c = it * C::THREADS + tid;
-      const int row = c / (DV / 8), col = c % (DV / 8);
-      *(uint4*)&vs[buf][row * C::VS + col * 8] = vr[it];
-    }
-  };
-
   // ---- direct HBM -> LDS tiles (D = 128) ---------------------------------------------
   // A 256-byte row holds 16 chunks of 16 bytes; chunk c of row r sits in slot
   // c ^ swz(r). swz is a bijection on 16 consecutive rows (conflict-free K reads of
@@ -243,8 +193,20 @@ prefill_bf16_kernel(PrefillArgs a) {
   const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
   const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
   const unsigned k_lds = lds_addr(&ks[0][0]), v_lds = lds_addr(&vs[0][0]);
+  // other head dims: the same direct loads into the padded rows, 1 KB piece by piece
+  PaddedTileDma<BK, DQK * 2, C::KS * 2, NW> kpad;
+  PaddedTileDma<BK, DV * 2, C::VS * 2, NW> vpad;
+  if constexpr (!C::DMA) {
+    kpad.init(wave_u, lane);
+    vpad.init(wave_u, lane);
+  }
   auto dma_tile = [&](const TileRef& t, int buf) __attribute__((always_inline)) {
-    if constexpr (C::DMA) {
+    if constexpr (!C::DMA) {
+      kpad.issue(wave_u, k_lds + (unsigned)(buf * C::K_TILE * 2), (unsigned)t.row0 * (DQK * 2),
+                 (unsigned)((size_t)a.kv_rows * DQK * 2 - 16), kdesc);
+      vpad.issue(wave_u, v_lds + (unsigned)(buf * C::V_TILE * 2), (unsigned)t.row0 * (DV * 2),
+                 (unsigned)((size_t)a.kv_rows * DV * 2 - 16), vdesc);
+    } else {
       const unsigned base = (unsigned)t.row0 * ROWB;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
@@ -456,57 +418,31 @@ prefill_bf16_kernel(PrefillArgs a) {
     skip = a.causal && t.pos0 > wave_pos1;
     need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
   };
-  if constexpr (C::DMA) {
-    // tile n+1 streams into the other buffer (last read before the previous
-    // barrier) while tile n is computed; the loop is unrolled by two so that every
-    // LDS address is a lane base plus an immediate
-    TileRef t = walk_ref();
-    dma_tile(t, 0);
-    wait_vmem();
-    __syncthreads();
-    auto step = [&](int n, auto bufc) __attribute__((always_inline)) {
-      constexpr int buf = decltype(bufc)::value;
-      bool skip, need_mask;
-      tile_flags(t, skip, need_mask);
-      TileRef tn = t;
-      if (n + 1 < ntiles) {
-        walk_next();
-        tn = walk_ref();
-        dma_tile(tn, buf ^ 1);
-      }
-      if (!skip) compute_tile(buf, t, need_mask);
-      t = tn;
-      wait_vmem();   // this wave's loads of tile n+1 have landed
-      __syncthreads();
-    };
-    for (int n = 0; n < ntiles; n += 2) {
-      step(n, std::integral_constant<int, 0>{});
-      if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
+  // tile n+1 streams into the other buffer (last read before the previous
+  // barrier) while tile n is computed; the loop is unrolled by two so that every
+  // LDS address is a lane base plus an immediate
+  TileRef t = walk_ref();
+  dma_tile(t, 0);
+  wait_vmem();
+  __syncthreads();
+  auto step = [&](int n, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    bool skip, need_mask;
+    tile_flags(t, skip, need_mask);
+    TileRef tn = t;
+    if (n + 1 < ntiles) {
+      walk_next();
+      tn = walk_ref();
+      dma_tile(tn, buf ^ 1);
     }
-  } else {
-    load_tile(0);
-    store_tile(0);
+    if (!skip) compute_tile(buf, t, need_mask);
+    t = tn;
+    wait_vmem();   // this wave's loads of tile n+1 have landed
     __syncthreads();
-    if (ntiles > 1) load_tile(1);
-    for (int n = 0; n < ntiles; ++n) {
-      const int buf = n & 1;
-      const TileRef t = tile_ref(n);
-      bool skip, need_mask;
-      tile_flags(t, skip, need_mask);
-      // With 64-key tiles the next tile's LDS store goes before this tile's work (its
-      // buffer was last read before the previous barrier), so it overlaps the
-      // products; with 128-key tiles it goes after (measured either way).
-      if (BK == 64 && n + 1 < ntiles) {
-        store_tile(buf ^ 1);
-        if (n + 2 < ntiles) load_tile(n + 2);
-      }
-      if (!skip) compute_tile(buf, t, need_mask);
-      if (BK != 64 && n + 1 < ntiles) {
-        store_tile(buf ^ 1);
-        if (n + 2 < ntiles) load_tile(n + 2);
-      }
-      __syncthreads();
-    }
+  };
+  for (int n = 0; n < ntiles; n += 2) {
+    step(n, std::integral_constant<int, 0>{});
+    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ------------------------------------------------------------------
