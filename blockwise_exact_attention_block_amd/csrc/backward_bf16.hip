@@ -180,11 +180,25 @@ bwd_dq_kernel(BwdArgs a) {
     for (int kt = 0; kt < BK / 32; ++kt) {
       const int krow = kt * 32 + l32;
       f32x16 st = f32x16{}, dpt = dp_init;
+      // S^T and dP^T as two chains, each step's K and V fragments read while the
+      // previous step's products run
+      static_assert(C::DS == C::DSV, "one step count for both chains");
+      bf16x8 kc = *(const bf16x8*)&ks[buf][krow * C::KS + 8 * h];
+      bf16x8 vc = *(const bf16x8*)&vs[buf][krow * C::VS + 8 * h];
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&ks[buf][krow * C::KS + 16 * s + 8 * h], qf[s], st);
-#pragma unroll
-      for (int s = 0; s < C::DSV; ++s)
-        dpt = mfma32(*(const bf16x8*)&vs[buf][krow * C::VS + 16 * s + 8 * h], of[s], dpt);
+      for (int s = 0; s < C::DS; ++s) {
+        bf16x8 kn = kc, vn = vc;
+        if (s + 1 < C::DS) {
+          kn = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * (s + 1) + 8 * h];
+          vn = *(const bf16x8*)&vs[buf][krow * C::VS + 16 * (s + 1) + 8 * h];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        st = mfma32(kc, qf[s], st);
+        dpt = mfma32(vc, of[s], dpt);
+        __builtin_amdgcn_sched_barrier(0);
+        kc = kn;
+        vc = vn;
+      }
       if (need_mask) {
         // last visible key of this 32-key block for the lane's query, minus 4*h
         int lim = nvalid - 1 - kt * 32;
@@ -211,19 +225,30 @@ bwd_dq_kernel(BwdArgs a) {
       }
       // dQ^T += K^T dS^T: step t2 holds keys 16*t2 + 4*h + {0..3} and
       // 16*t2 + 8 + 4*h + {0..3} in lane half h; K^T rows d = 32*mt + lane%32
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
+      auto ktread = [&](int mt, bf16x4 (&f)[2][2]) {
         const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x4 half2[2];
+        for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-            half2[x] = lds_read_tr16(&ks[buf][key * C::KS + dcol]);
+            f[t2][x] = lds_read_tr16(&ks[buf][key * C::KS + dcol]);
           }
-          dqacc[mt] = mfma32(cat(half2[0], half2[1]), dsb[t2], dqacc[mt]);
-        }
+      };
+      // K^T fragments of output tile mt + 1 read while the products of mt run
+      bf16x4 fc[2][2], fn[2][2];
+      ktread(0, fc);
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        if (mt + 1 < C::MT) ktread(mt + 1, fn);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) dqacc[mt] = mfma32(cat(fc[t2][0], fc[t2][1]), dsb[t2], dqacc[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) fc[t2][x] = fn[t2][x];
       }
     }
   };
@@ -435,34 +460,40 @@ bwd_dkdv_kernel(BwdArgs a) {
         dsb[t2] = to_bf16x8(ds);
       }
       // dV^T += dO^T P and dK^T += Q^T dS: step t2 holds queries 16*t2 + 4*h + {0..3}
-      // and 16*t2 + 8 + 4*h + {0..3} in lane half h; dO^T / Q^T rows = 32*mt + lane%32
-#pragma unroll
-      for (int mt = 0; mt < C::MTV; ++mt) {
+      // and 16*t2 + 8 + 4*h + {0..3} in lane half h; dO^T / Q^T rows = 32*mt + lane%32.
+      // One flattened loop (dV tiles, then dK tiles), each step's transposed reads
+      // issued while the previous step's products run.
+      constexpr int NST = C::MTV + C::MT;
+      auto trread = [&](int it, bf16x4 (&f)[2][2]) {
+        const bool is_v = it < C::MTV;
+        const int mt = is_v ? it : it - C::MTV;
         const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x4 half2[2];
+        for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             const int r = qs * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-            half2[x] = lds_read_tr16(&osm[buf][r * OS + dcol]);
+            f[t2][x] = is_v ? lds_read_tr16(&osm[buf][r * OS + dcol]) : lds_read_tr16(&qsm[buf][r * QS + dcol]);
           }
-          dvacc[mt] = mfma32(cat(half2[0], half2[1]), pb[t2], dvacc[mt]);
-        }
-      }
+      };
+      bf16x4 fc[2][2], fn[2][2];
+      trread(0, fc);
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
+      for (int it = 0; it < NST; ++it) {
+        if (it + 1 < NST) trread(it + 1, fn);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x4 half2[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int r = qs * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-            half2[x] = lds_read_tr16(&qsm[buf][r * QS + dcol]);
-          }
-          dkacc[mt] = mfma32(cat(half2[0], half2[1]), dsb[t2], dkacc[mt]);
+          if (it < C::MTV)
+            dvacc[it] = mfma32(cat(fc[t2][0], fc[t2][1]), pb[t2], dvacc[it]);
+          else
+            dkacc[it - C::MTV] = mfma32(cat(fc[t2][0], fc[t2][1]), dsb[t2], dkacc[it - C::MTV]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) fc[t2][x] = fn[t2][x];
       }
     }
   };
