@@ -132,8 +132,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned b
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 // Non-temporal 16-byte load (cache policy nt): for data read exactly once, such as
-// a KV cache streamed by decode. Measured on 16-byte loads only: for 8-byte loads
-// the policy made the fp8 decode slower.
+// a KV cache streamed by decode. (8-byte loads with this policy measured slower.)
 __device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
   return make_uint4(v[0], v[1], v[2], v[3]);

@@ -16,9 +16,12 @@
 //   * O^T += V^T P^T: P^T is the S^T accumulator converted to bf16; V goes HBM ->
 //     VGPR -> a wave-private LDS tile and is read back transposed with
 //     ds_read_b64_tr_b16 in the accumulator's key order.
-// The four waves' states are merged through LDS at the end. The cache's 16-byte
-// loads use the non-temporal policy: every byte is read once, and streaming it
-// that way measured faster (the fp8 path's 8-byte K loads keep the default).
+// The four waves' states are merged through LDS at the end. The cache is read with
+// 16-byte loads in the non-temporal policy: every byte is read once, and streaming
+// it that way measured faster. With an fp8 cache a lane's K fragments (8 values
+// per MFMA step) are taken from one contiguous run of the row, d = 8 * DSTEP * gg
+// + 8 s (the query fragments use the same mapping), so that they too come in
+// 16-byte loads.
 //
 // FP8 KV (KV8): the cache holds e4m3 values with one dequantisation scale for K and
 // one for V (1 byte per value, [CH] §挑战 2 KV-size equation with b = 1). K and V
@@ -62,7 +65,7 @@ decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < DSTEP; ++s) {
       if (valid)
-        qf[s] = *(const bf16x8*)(qp + 32 * s + 8 * gg);
+        qf[s] = *(const bf16x8*)(qp + (KV8 ? 8 * DSTEP * gg + 8 * s : 32 * s + 8 * gg));
       else
         qf[s] = bf16x8{};
     }
@@ -72,20 +75,23 @@ decode_partial_kernel(DecodeArgs a) {
   const int iters = (nchunks + NW - 1) / NW;
 
   uint4 kreg[2][DSTEP], vreg[VCH];       // bf16 cache
-  uint2 kreg8[2][DSTEP];                  // fp8 cache: 8 values of one K row
+  uint4 kreg8[2][DSTEP / 2];              // fp8 cache: 16 values of one K row (two steps)
   uint4 vreg8[VCH8];                      // fp8 cache: 16 values of one V row
   auto load_chunk = [&](int it) {
     const int key0 = key_begin + (it * NW + wave) * CK;   // may lie past the split: masked later
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      if (KV8) {
+        // fp8: the lane's DSTEP fragments are one run of 8 * DSTEP bytes
 #pragma unroll
-      for (int s = 0; s < DSTEP; ++s) {
-        const unsigned off = (unsigned)((key0 + 16 * kt + L16) * D + 32 * s + 8 * gg) * (unsigned)EB;
-        if (KV8)
-          kreg8[kt][s] = buf_load8(krs, off);
-        else
-          kreg[kt][s] = buf_load16_nt(krs, off);
+        for (int j = 0; j < DSTEP / 2; ++j)
+          kreg8[kt][j] = buf_load16_nt(krs, (unsigned)((key0 + 16 * kt + L16) * D + 8 * DSTEP * gg + 16 * j));
+      } else {
+#pragma unroll
+        for (int s = 0; s < DSTEP; ++s)
+          kreg[kt][s] = buf_load16_nt(krs, (unsigned)((key0 + 16 * kt + L16) * D + 32 * s + 8 * gg) * 2u);
       }
+    }
     if (KV8) {
 #pragma unroll
       for (int c = 0; c < VCH8; ++c) {
@@ -136,7 +142,8 @@ decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < DSTEP; ++s) {
         if (KV8) {
-          const uint2 lo = fp8x4_to_bf16x4(kreg8[kt][s].x), hi = fp8x4_to_bf16x4(kreg8[kt][s].y);
+          const uint4 w = kreg8[kt][s / 2];
+          const uint2 lo = fp8x4_to_bf16x4(s % 2 ? w.z : w.x), hi = fp8x4_to_bf16x4(s % 2 ? w.w : w.y);
           kcur[kt][s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
           kcur[kt][s] = kreg[kt][s];
