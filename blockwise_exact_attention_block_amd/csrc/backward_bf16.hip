@@ -56,19 +56,28 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
   if (row < rows && L == 0) delta[row] = acc;
 }
 
-// LDS row strides (elements). K (dQ kernel), Q and dO (dK/dV kernel) are read both
-// as 16-byte rows and transposed; a pad of 16 elements suits the mix (measured).
-// V is only read as rows: a pad of 8 starts 16 consecutive rows on different banks.
+// LDS row strides (elements): every tile row is padded by 8 elements, so 16
+// consecutive rows start on 16 different 4-bank groups (16-byte row reads are free
+// of bank conflicts). K (dQ kernel), Q and dO (dK/dV kernel) are also read
+// transposed; for those the row order below keeps the transposed reads conflict-free.
 template <int DQK, int DV>
 struct BCfg {
   static constexpr int THREADS = 512;               // 8 waves
   static constexpr int ROWS = 256;                  // query rows (dQ) / keys (dK, dV) per workgroup
   static constexpr int BK = 128;                    // keys per LDS tile (dQ kernel)
   static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
-  static constexpr int KS = DQK + 16, VS = DV + 8, OS = DV + 16;
+  static constexpr int KS = DQK + 8, VS = DV + 8, OS = DV + 8;
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
   static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
 };
+
+// Row order inside each 16-row block of a tile read both as rows and transposed: the
+// MFMA row (accumulator row) 4a + b reads LDS row 4b + a (an involution). A half
+// wave's transposed read takes 64 bytes from each of 4 consecutive accumulator rows
+// 4a .. 4a+3; they sit in LDS rows a, a+4, a+8, a+12, which with (D + 8)-element rows
+// start 16 banks apart, so the 4 x 64 bytes cover all 64 banks once. The 16-byte row
+// reads of 16 consecutive accumulator rows still touch 16 distinct LDS rows.
+__device__ __forceinline__ int perm16(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // ---- dQ -------------------------------------------------------------------------------
 template <int DQK, int DV>
@@ -178,7 +187,7 @@ bwd_dq_kernel(BwdArgs a) {
   auto compute_tile = [&](int buf, long long kpos0, int nvalid, bool need_mask) {
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
-      const int krow = kt * 32 + l32;
+      const int krow = kt * 32 + perm16(l32);   // the key of accumulator row l32
       f32x16 st = f32x16{}, dpt = dp_init;
       // S^T and dP^T as two chains, each step's K and V fragments read while the
       // previous step's products run
@@ -200,16 +209,18 @@ bwd_dq_kernel(BwdArgs a) {
         vc = vn;
       }
       if (need_mask) {
-        // last visible key of this 32-key block for the lane's query, minus 4*h
+        // last visible key of this 32-key block for the lane's query, minus h;
+        // element i holds accumulator row 8*(i/4) + 4*h + i%4, i.e. the key at
+        // perm16 of it: 16*(i/8) + 4*(i%4) + 2*((i/4)%2) + h
         int lim = nvalid - 1 - kt * 32;
         if (a.causal) {
           const long long rel = wave_pos0 + l32 - (kpos0 + kt * 32);
           lim = (int)min((long long)lim, max(rel, -1LL));
         }
-        lim -= 4 * h;
+        lim -= h;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + (i & 3) > lim) st[i] = kNegInf;
+          if (16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) > lim) st[i] = kNegInf;
       }
       // dS^T = P^T o (dP^T - delta), rounded to bf16 as the B operand of dQ^T
       bf16x8 dsb[2];
@@ -223,15 +234,17 @@ bwd_dq_kernel(BwdArgs a) {
         }
         dsb[t2] = to_bf16x8(x);
       }
-      // dQ^T += K^T dS^T: step t2 holds keys 16*t2 + 4*h + {0..3} and
-      // 16*t2 + 8 + 4*h + {0..3} in lane half h; K^T rows d = 32*mt + lane%32
+      // dQ^T += K^T dS^T: step t2 holds accumulator rows 16*t2 + 4*h + {0..3} and
+      // 16*t2 + 8 + 4*h + {0..3} in lane half h; K^T rows d = 32*mt + lane%32. The
+      // transposed read of accumulator row 16*t2 + 8*x + 4*(gg/2) + L/4 takes its
+      // key's LDS row, perm16 of it.
       auto ktread = [&](int mt, bf16x4 (&f)[2][2]) {
         const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            const int key = kt * 32 + 16 * t2 + 4 * (L >> 2) + 2 * x + (gg >> 1);
             f[t2][x] = lds_read_tr16(&ks[buf][key * C::KS + dcol]);
           }
       };
@@ -403,10 +416,11 @@ bwd_dkdv_kernel(BwdArgs a) {
       const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
       *(uint4*)&osm[buf][row * OS + col * 8] = orr[it];
     }
+    // LSE and delta are kept in accumulator-row order (perm16 is its own inverse)
     if (tid < BQ)
-      lsm[buf][tid] = rowv;
+      lsm[buf][perm16(tid)] = rowv;
     else if (tid < 2 * BQ)
-      dsm[buf][tid - BQ] = rowv;
+      dsm[buf][perm16(tid - BQ)] = rowv;
   };
 
   auto compute_tile = [&](int buf, long long qpos_t) {
@@ -415,9 +429,10 @@ bwd_dkdv_kernel(BwdArgs a) {
       const long long qpos_s = qpos_t + qs * 32;
       if (a.causal && qpos_s + 31 < wave_kpos0) continue;   // these queries precede all the wave's keys
       const bool need_mask = a.causal && qpos_s < wave_kpos0 + 31;
-      const int qrow = qs * 32 + l32;
-      // S = Q K^T and dP = dO V^T: lane = key column, rows = queries 8*(i/4) + 4*h + i%4.
-      // dP starts from the rows' -delta, so it comes out as dP - delta.
+      const int qrow = qs * 32 + perm16(l32);   // the query of accumulator row l32
+      // S = Q K^T and dP = dO V^T: lane = key column, accumulator rows 8*(i/4) + 4*h +
+      // i%4 (their queries at perm16 of that). dP starts from the rows' -delta, so it
+      // comes out as dP - delta.
       f32x16 st = f32x16{}, dpt;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -437,11 +452,12 @@ bwd_dkdv_kernel(BwdArgs a) {
         dpt = mfma32(*(const bf16x8*)&osm[buf][qrow * OS + 16 * s + 8 * h], vb, dpt);
       }
       if (need_mask) {
-        // key visible iff key_pos <= query_pos: row offset >= key_pos - qpos_s (minus 4*h)
-        const int lim = (int)(wave_kpos0 + l32 - qpos_s) - 4 * h;
+        // key visible iff key_pos <= query_pos: element i's query offset
+        // 16*(i/8) + 4*(i%4) + 2*((i/4)%2) + h >= key_pos - qpos_s
+        const int lim = (int)(wave_kpos0 + l32 - qpos_s) - h;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + (i & 3) < lim) st[i] = kNegInf;
+          if (16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) < lim) st[i] = kNegInf;
       }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -459,8 +475,9 @@ bwd_dkdv_kernel(BwdArgs a) {
         pb[t2] = to_bf16x8(p);
         dsb[t2] = to_bf16x8(ds);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS: step t2 holds queries 16*t2 + 4*h + {0..3}
-      // and 16*t2 + 8 + 4*h + {0..3} in lane half h; dO^T / Q^T rows = 32*mt + lane%32.
+      // dV^T += dO^T P and dK^T += Q^T dS: step t2 holds accumulator rows 16*t2 + 4*h +
+      // {0..3} and 16*t2 + 8 + 4*h + {0..3} in lane half h; dO^T / Q^T rows = 32*mt +
+      // lane%32.
       // One flattened loop (dV tiles, then dK tiles), each step's transposed reads
       // issued while the previous step's products run.
       constexpr int NST = C::MTV + C::MT;
@@ -472,7 +489,8 @@ bwd_dkdv_kernel(BwdArgs a) {
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            const int r = qs * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
+            // LDS row of accumulator row 16*t2 + 8*x + 4*(gg/2) + L/4
+            const int r = qs * 32 + 16 * t2 + 4 * (L >> 2) + 2 * x + (gg >> 1);
             f[t2][x] = is_v ? lds_read_tr16(&osm[buf][r * OS + dcol]) : lds_read_tr16(&qsm[buf][r * QS + dcol]);
           }
       };
