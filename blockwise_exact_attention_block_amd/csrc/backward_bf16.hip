@@ -25,9 +25,9 @@
 //     K^T read through ds_read_b64_tr_b16. K / V tiles are 128 keys.
 //   * bwd_dkdv_kernel: one workgroup per 256 keys of one (batch, KV head), 8 waves
 //     of 32 keys, looping over the group's query heads and the visible query tiles
-//     (64 rows, staged in LDS with their LSE and delta). K rows stay in VGPRs as the
-//     B operand of S = Q K^T (lane = key column); the workgroup's V rows sit in LDS
-//     for dP = dO V^T. dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T through
+//     (64 rows, loaded straight from HBM into LDS, with their LSE and delta). K and V
+//     rows stay in VGPRs as the B operands of S = Q K^T and dP = dO V^T (lane = key
+//     column). dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T through
 //     ds_read_b64_tr_b16. Rows past the query block carry LSE = +inf, so their P
 //     and dS are exactly 0 with no row mask.
 #include "common.hpp"
@@ -315,16 +315,13 @@ bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<DQK, DV>;
   constexpr int BQ = C::BQ;
   constexpr int QS = C::KS, OS = C::OS;   // Q rows like K rows
-  constexpr int QCH = BQ * DQK / 8 / C::THREADS, OCH = BQ * DV / 8 / C::THREADS;
-  constexpr int VCH = C::ROWS * DV / 8 / C::THREADS;
-  static_assert(QCH * C::THREADS * 8 == BQ * DQK && OCH * C::THREADS * 8 == BQ * DV, "tile split");
   __shared__ __attribute__((aligned(16))) __bf16 qsm[2][BQ * QS];
   __shared__ __attribute__((aligned(16))) __bf16 osm[2][BQ * OS];
-  __shared__ __attribute__((aligned(16))) __bf16 vsm[C::ROWS * C::VS];
   __shared__ __attribute__((aligned(16))) float lsm[2][BQ];
   __shared__ __attribute__((aligned(16))) float dsm[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: derived positions stay scalar
   const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
   // XCD-aware order: XCD x runs the x-th eighth of the work list (batch, KV head,
   // key tile), so its co-resident workgroups stream the same Q / dO tiles through
@@ -361,37 +358,29 @@ bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int s = 0; s < C::DS; ++s)
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
-  // the workgroup's V rows into LDS, once
+  // V row of the lane's key as the B operand of dP = dO V^T
+  bf16x8 vf[C::DSV];
 #pragma unroll
-  for (int it = 0; it < VCH; ++it) {
-    const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
-    *(uint4*)&vsm[row * C::VS + col * 8] = buf_load16(vrs, (unsigned)((key_base + row) * DV + col * 8) * 2u);
-  }
+  for (int s = 0; s < C::DSV; ++s)
+    vf[s] = __builtin_bit_cast(bf16x8, buf_load16(vrs, (unsigned)(my_key * DV + 16 * s + 8 * h) * 2u));
   f32x16 dkacc[C::MT], dvacc[C::MTV];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) dkacc[mt] = f32x16{};
 #pragma unroll
   for (int mt = 0; mt < C::MTV; ++mt) dvacc[mt] = f32x16{};
 
-  uint4 qr[QCH], orr[OCH];
+  // Q / dO tiles go straight from HBM into the padded LDS rows (rows past the block
+  // re-read the slab's last 16 bytes: finite values whose P is 0); the rows' LSE and
+  // delta go through a register of threads 0..127
   float rowv = 0.f;   // threads 0..63: -LSE * log2(e) of a row; 64..127: -delta
+  static_assert(DQK == DV && QS == OS, "Q and dO tiles share one load layout");
+  PaddedTileDma<BQ, DQK * 2, QS * 2, 8> tdma;
+  tdma.init(wave, lane);
   auto tile_head = [&](int n) { return g * a.group + n / nqt; };
   auto tile_row0 = [&](int n) { return (qt0 + n % nqt) * BQ; };
-  auto load_tile = [&](int n) {
+  auto load_tile = [&](int n, int buf) {
     const int hq = tile_head(n), row0 = tile_row0(n);
     const size_t bh = (size_t)b * a.Hq + hq;
-    const auto qrs = make_rsrc((const __bf16*)a.q + bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 2));
-    const auto ors = make_rsrc((const __bf16*)a.dout + bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 2));
-#pragma unroll
-    for (int it = 0; it < QCH; ++it) {
-      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
-      qr[it] = buf_load16(qrs, (unsigned)((row0 + row) * DQK + col * 8) * 2u);
-    }
-#pragma unroll
-    for (int it = 0; it < OCH; ++it) {
-      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
-      orr[it] = buf_load16(ors, (unsigned)((row0 + row) * DV + col * 8) * 2u);
-    }
     if (tid < 2 * BQ) {
       const int r = row0 + (tid & (BQ - 1));
       if (tid < BQ) {
@@ -404,18 +393,12 @@ bwd_dkdv_kernel(BwdArgs a) {
         rowv = r < a.Sq ? -a.delta[bh * a.Sq + r] : 0.f;
       }
     }
+    const u32x4 qdesc = raw_desc((const __bf16*)a.q + bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 2));
+    const u32x4 odesc = raw_desc((const __bf16*)a.dout + bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 2));
+    tdma.issue(wave, lds_addr(&qsm[buf][0]), (unsigned)(row0 * DQK * 2), (unsigned)(a.Sq * DQK * 2 - 16), qdesc);
+    tdma.issue(wave, lds_addr(&osm[buf][0]), (unsigned)(row0 * DV * 2), (unsigned)(a.Sq * DV * 2 - 16), odesc);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < QCH; ++it) {
-      const int c = it * C::THREADS + tid, row = c / (DQK / 8), col = c % (DQK / 8);
-      *(uint4*)&qsm[buf][row * QS + col * 8] = qr[it];
-    }
-#pragma unroll
-    for (int it = 0; it < OCH; ++it) {
-      const int c = it * C::THREADS + tid, row = c / (DV / 8), col = c % (DV / 8);
-      *(uint4*)&osm[buf][row * OS + col * 8] = orr[it];
-    }
+  auto store_rows = [&](int buf) {
     // LSE and delta are kept in accumulator-row order (perm16 is its own inverse)
     if (tid < BQ)
       lsm[buf][perm16(tid)] = rowv;
@@ -448,8 +431,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kf[s], st);
 #pragma unroll
       for (int s = 0; s < C::DSV; ++s) {
-        const bf16x8 vb = *(const bf16x8*)&vsm[(wave * 32 + l32) * C::VS + 16 * s + 8 * h];
-        dpt = mfma32(*(const bf16x8*)&osm[buf][qrow * OS + 16 * s + 8 * h], vb, dpt);
+        dpt = mfma32(*(const bf16x8*)&osm[buf][qrow * OS + 16 * s + 8 * h], vf[s], dpt);
       }
       if (need_mask) {
         // key visible iff key_pos <= query_pos: element i's query offset
@@ -516,17 +498,17 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();   // also publishes the V rows
-  if (ntiles > 1) load_tile(1);
+  load_tile(0, 0);
+  store_rows(0);
+  wait_vmem();
+  __syncthreads();
   for (int n = 0; n < ntiles; ++n) {
     const int buf = n & 1;
+    // the other buffer was last read before the previous barrier
+    if (n + 1 < ntiles) load_tile(n + 1, buf ^ 1);
     compute_tile(buf, a.q_pos0 + tile_row0(n));
-    if (n + 1 < ntiles) {
-      store_tile(buf ^ 1);
-      if (n + 2 < ntiles) load_tile(n + 2);
-    }
+    if (n + 1 < ntiles) store_rows(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
