@@ -7,7 +7,7 @@
 //
 // Workgroup = (batch b, KV head g, split p), 4 waves. The split's keys are dealt to
 // the waves in chunks of 32 keys (chunk c goes to wave c % 4), every wave running
-// the same number of iterations so the workgroup barriers always match.
+// the same number of iterations (keys past the split are masked).
 // Per chunk, on v_mfma_f32_16x16x32_bf16 with the G = Hq/Hkv heads as the 16-wide
 // N dimension (heads >= G are zero queries):
 //   * S^T = K Q^T: K comes straight from HBM into the A operand (lane = key,
@@ -15,7 +15,9 @@
 //   * online softmax per head (lane column): running max / exp-sum, rescale.
 //   * O^T += V^T P^T: P^T is the S^T accumulator converted to bf16; V goes HBM ->
 //     VGPR -> a wave-private LDS tile and is read back transposed with
-//     ds_read_b64_tr_b16 in the accumulator's key order.
+//     ds_read_b64_tr_b16 in the accumulator's key order. The tile is private, so
+//     the waves need no barrier until the merge (a per-chunk workgroup barrier
+//     measured 3 % slower on an fp8 cache).
 // The four waves' states are merged through LDS at the end. The cache is read with
 // 16-byte loads in the non-temporal policy: every byte is read once, and streaming
 // it that way measured faster. With an fp8 cache a lane's K fragments (8 values
@@ -150,7 +152,10 @@ decode_partial_kernel(DecodeArgs a) {
         }
       }
     if (it + 1 < iters) load_chunk(it + 1);
-    __syncthreads();  // V tile visible (the other buffer was drained before the last barrier)
+    // No barrier: the V tile is private to the wave, and one wave's LDS operations
+    // complete in the order they are issued, so the reads below see these writes
+    // and the next chunk's writes (to the other buffer) come after them. The waves
+    // run at their own pace until the merge.
 
     const int key0 = (it * NW + wave) * CK;   // relative to the split
     f32x4 sacc[2];
