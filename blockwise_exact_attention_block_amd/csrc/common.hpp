@@ -97,12 +97,15 @@ __device__ __forceinline__ void lds_load16(unsigned lds_base, unsigned byte_off,
 // 1 KB pieces, and piece j is written by one wave-wide lds_load16, whose lane i fills
 // bytes [1024 j + 16 i, +16) of the tile. It fetches the 16 global bytes that belong
 // there, or, for a slot in a row's padding, a duplicate of that row's first bytes
-// (never read). Piece j goes to wave j % NW.
+// (never read). Piece j goes to wave j % NW. The tile's LDS allocation is a whole
+// number of KB (padded_tile_bytes); when ROWS * LDS_STRIDE is not, the last piece's
+// slots past the tile fetch the following global rows (clamped like every offset)
+// into that slack, which is never read.
+constexpr int padded_tile_bytes(int rows, int lds_stride) { return (rows * lds_stride + 1023) / 1024 * 1024; }
 template <int ROWS, int ROW_BYTES, int LDS_STRIDE, int NW>
 struct PaddedTileDma {
-  static constexpr int PIECES = ROWS * LDS_STRIDE / 1024;
+  static constexpr int PIECES = padded_tile_bytes(ROWS, LDS_STRIDE) / 1024;
   static constexpr int PER_WAVE = (PIECES + NW - 1) / NW;
-  static_assert(PIECES * 1024 == ROWS * LDS_STRIDE, "tile must be whole 1 KB pieces");
   static_assert(LDS_STRIDE % 16 == 0 && ROW_BYTES % 16 == 0 && LDS_STRIDE - ROW_BYTES <= ROW_BYTES, "layout");
   unsigned off[PER_WAVE];   // per lane: global byte offset inside the tile, per piece
   __device__ __forceinline__ void init(int wave, int lane) {

@@ -50,9 +50,9 @@ constexpr float kLazyShift = 8.0f;
 
 template <int DQK, int DV, int NQ, int NW>
 struct PCfg {
-  // keys per tile: 128 where two double-buffered tiles fit in LDS, else 64; all of
+  // keys per tile: 128 where two double-buffered tiles fit in LDS, else 96; all of
   // a tile's keys go through one online-softmax update
-  static constexpr int BK = DQK <= 128 ? 128 : 64;
+  static constexpr int BK = DQK <= 128 ? 128 : 96;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
   // D = 128: unpadded rows with an XOR swizzle of 16-byte chunks. Other head dims:
@@ -63,8 +63,8 @@ struct PCfg {
   static_assert(!DMA || DQK == DV, "the direct loads share one row layout between K and V");
   static constexpr int KS = DMA ? DQK : DQK + 8;
   static constexpr int VS = DMA ? DV : DV + 32;
-  static constexpr int K_TILE = BK * KS;
-  static constexpr int V_TILE = BK * VS;
+  static constexpr int K_TILE = padded_tile_bytes(BK, KS * 2) / 2;   // elements, whole KB
+  static constexpr int V_TILE = padded_tile_bytes(BK, VS * 2) / 2;
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
   static constexpr int MT = DV / 32;                  // 32-row output tiles along D_v
 };

@@ -3,8 +3,9 @@
 The kernels' LDS addressing is restated here from the sources and checked
 against two properties:
   * the direct HBM -> LDS tile loads (PaddedTileDma in common.hpp) put every
-    16-byte chunk of every row where the reads expect it, never write outside
-    the tile and never fetch outside the tile's rows;
+    16-byte chunk of every row where the reads expect it and never write outside
+    the tile's whole-KB allocation; only slots in the slack past the last row
+    fetch bytes beyond the tile's rows;
   * the reads are free of bank conflicts under the LDS model the counters
     confirm on gfx950: 64 banks of 4 bytes, a 16-byte read served 16 lanes per
     pass and an 8-byte (transposed) read 32 lanes per pass. Under this model the
@@ -56,9 +57,11 @@ def tr_read_passes(addr):
 # ---- PaddedTileDma --------------------------------------------------------------
 
 def padded_tile_dma_map(rows, row_bytes, stride, nw):
-    """LDS byte -> global byte of the tile, as PaddedTileDma::init / issue compute it."""
-    pieces = rows * stride // 1024
-    assert pieces * 1024 == rows * stride
+    """LDS byte -> global byte of the tile, as PaddedTileDma::init / issue compute it.
+    The LDS tile is allocated in whole KB (padded_tile_bytes); slots past the tile's
+    rows land in that slack and fetch the next global rows (clamped by the kernel)."""
+    alloc = (rows * stride + 1023) // 1024 * 1024
+    pieces = alloc // 1024
     per = (pieces + nw - 1) // nw
     lds = {}
     for wave in range(nw):
@@ -70,19 +73,21 @@ def padded_tile_dma_map(rows, row_bytes, stride, nw):
                 p = j * 1024 + lane * 16
                 row, within = divmod(p, stride)
                 off = row * row_bytes + (within if within < row_bytes else within - row_bytes)
-                assert p not in lds and p + 16 <= rows * stride
-                assert 0 <= off and off + 16 <= rows * row_bytes
+                assert p not in lds and p + 16 <= alloc
+                assert 0 <= off and (row >= rows or off + 16 <= rows * row_bytes)
                 lds[p] = off
+    assert len(lds) == pieces * 64
     return lds
 
 
 @pytest.mark.parametrize("rows,row_bytes,stride", [
     (128, 128, 144), (128, 128, 192),    # prefill D = 64: K, V
-    (64, 384, 400), (64, 256, 320),      # prefill D_qk = 192, D_v = 128: K, V
+    (96, 384, 400), (96, 256, 320),      # prefill D_qk = 192, D_v = 128: K (37.5 KB), V
     (128, 256, 272),                     # dQ kernel D = 128: K and V
     (64, 256, 272), (64, 128, 144),      # dK/dV kernel Q and dO, D = 128 and 64
 ])
 def test_padded_tile_dma_places_every_chunk(rows, row_bytes, stride):
+    """Every 16-byte chunk of every row lands at its row's LDS offset."""
     lds = padded_tile_dma_map(rows, row_bytes, stride, 8)
     for r in range(rows):
         for c in range(0, row_bytes, 16):
@@ -116,7 +121,7 @@ def test_prefill_swizzle_reads_are_conflict_free():
 @pytest.mark.parametrize("stride,kind", [(144, "row"), (400, "row"), (192, "tr"), (320, "tr")])
 def test_prefill_padded_rows_are_conflict_free(stride, kind):
     if kind == "row":   # K rows of D = 64 (144 B) and D_qk = 192 (400 B)
-        worst = max(banks_max(p, 16) for p in row_read_passes(lambda r, c: r * stride + 16 * c, 64, stride // 16 - 1))
+        worst = max(banks_max(p, 16) for p in row_read_passes(lambda r, c: r * stride + 16 * c, 96, stride // 16 - 1))
     else:               # V rows padded by 32 elements, read transposed
         worst = max(banks_max(p, 8) for p in tr_read_passes(lambda rho, col: rho * stride + 2 * col))
     assert worst == 1
