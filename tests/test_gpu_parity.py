@@ -356,6 +356,35 @@ def test_splitkv_decode_fp8_small(ra, D, Hq, Hkv, L, n):
     assert torch.equal(op2, op) and torch.equal(lp2, lp)
 
 
+@pytest.mark.parametrize("kv8", [False, True])
+@pytest.mark.parametrize("D,Hq,Hkv,L,n", [
+    (128, 32, 2, 40, 8),    # 16 heads per group, 5 keys per split: three waves see only masked keys
+    (64, 16, 1, 33, 1),     # 16 heads per group, a last chunk of one key
+    (128, 16, 1, 96, 3),    # one whole chunk per split
+])
+def test_splitkv_decode_edges(ra, kv8, D, Hq, Hkv, L, n):
+    """The largest supported group and splits shorter than the four waves' chunks."""
+    B = 2
+    say(f"splitkv_decode edges kv8={kv8} B{B} Hq{Hq} Hkv{Hkv} L{L} n{n} D{D}")
+    q = randn_np((B, Hq, D), 191, "bf16")
+    if kv8:
+        kc = fp8_cache_torch((B, Hkv, L, D), 192, DEV)
+        vc = fp8_cache_torch((B, Hkv, L, D), 193, DEV)
+        op, lp, o, l = ra.splitkv_decode_fp8(to_dev(q, torch.bfloat16), kc, vc, k_scale=FP8_K_SCALE,
+                                             v_scale=FP8_V_SCALE, n_splits=n)
+        k = oracle.dequantize(fp8_codes(kc), FP8_K_SCALE)
+        v = oracle.dequantize(fp8_codes(vc), FP8_V_SCALE)
+    else:
+        k = randn_np((B, Hkv, L, D), 192, "bf16")
+        v = randn_np((B, Hkv, L, D), 193, "bf16")
+        op, lp, o, l = ra.splitkv_decode(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                                         to_dev(v, torch.bfloat16), n_splits=n)
+    torch.cuda.synchronize()
+    op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
+    assert_close(np64(op), np64(lp), op_r, lp_r, "bf16", "decode partials")
+    assert_close(np64(o), np64(l), o_r, l_r, "bf16", "decode merged")
+
+
 def test_splitkv_decode_fp8_equals_bf16_path_on_the_widened_cache(ra):
     """The fp8 path widens codes exactly to bf16 and folds the scales into the
     score scale and the output: with scales 1 it reproduces the bf16 decode of the
