@@ -141,6 +141,34 @@ def run_striped(args, ra, torch, stream, cfg, q, k, v):
     return res
 
 
+def run_ring_step(args, ra, torch, stream, cfg, q, k, v):
+    """One full ring step through the step API, as one rank runs it when a KV block
+    arrives: the queries of a partition against a whole earlier block (every pair
+    visible), merged into the running fp32 (O, LSE) state read from and written
+    back to HBM. FLOPs count the block's pairs."""
+    if cfg.q_part0 != 0 or cfg.n_qparts < 2:
+        return None                                      # needs partitions 0 and 1 in the launch
+    Sp = cfg.Sp
+    qi = q[:, :, Sp:2 * Sp].contiguous()                  # queries of partition 1
+    kb = k[:, :, :Sp].contiguous()                        # KV block 0
+    vb = v[:, :, :Sp].contiguous()
+    o_acc, l_acc = ra.init_state(qi, cfg.Dv)
+    steps, warm = max(2, min(args.steps, 5)), 1
+    log(f"[bench] ring step: {warm} warmup + {steps} timed steps")
+    w, ev = timed(lambda: ra.block_attn_step(qi, kb, vb, o_acc, l_acc, q_pos0=Sp, k_pos0=0, causal=cfg.causal,
+                                             scale=cfg.scale), steps, warm, stream, torch)
+    f = 2 * (cfg.Dqk + cfg.Dv) * Sp * Sp * cfg.Hq * cfg.B
+    del qi, kb, vb, o_acc, l_acc
+    return {
+        "workload": f"{cfg.name}: one full ring step (partition 1 against KV block 0), "
+                    "fp32 running state in HBM",
+        "launch_ms": round(ev, 4),
+        "flops": f,
+        "tflops": round(f / (ev * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(f / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+
+
 def backward_flops(cfg) -> int:
     """Algorithmic FLOPs of the backward pass: the five products per visible pair
     (S = Q K^T, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K), 2 (3 D_qk + 2 D_v)
@@ -436,6 +464,9 @@ def main():
     del out, lse
     if not args.no_striped and cfg.causal:
         line["striped"] = run_striped(args, ra, torch, stream, cfg, q, k, v)
+    step = run_ring_step(args, ra, torch, stream, cfg, q, k, v)
+    if step is not None:
+        line["ring_step"] = step
     if not args.no_backward:
         bwd = run_backward(args, ra, torch, stream, cfg, q, k, v)
         if bwd is not None:
