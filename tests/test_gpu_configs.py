@@ -94,6 +94,44 @@ def test_c3_sampled_rows_and_closed_form(ra):
     check_zero_query_closed_form(ra, cfg, k, v)
 
 
+@pytest.mark.timeout(900)
+def test_c3_ring_step_sampled_rows(ra):
+    """The step API at the C3 partition size, as bench.py times it (partition 1
+    against KV block 0, fp32 state), then the diagonal block 1: after the first
+    step the state is attention over block 0 alone, after the second it is the
+    partition's causal attention. Sampled rows against the oracle, both times."""
+    cfg = CONFIGS["C3"]
+    Sp, group = cfg.Sp, cfg.Hq // cfg.Hkv
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    qi = q[:, :, Sp:2 * Sp].contiguous()
+    del q
+    o_acc, l_acc = ra.init_state(qi, cfg.Dv)
+    rng = np.random.default_rng(cfg.seed + 17)
+    rows = sorted({(0, int(h), int(r)) for h, r in zip(rng.integers(0, cfg.Hq, 192), rng.integers(0, Sp, 192))}
+                  | {(0, 0, 0), (0, cfg.Hq - 1, Sp - 1), (0, 5, 255), (0, 5, 256)})
+    for nblk in (1, 2):
+        j = nblk - 1
+        say(f"block_attn_step {cfg.name}: partition 1 x KV block {j}")
+        ra.block_attn_step(qi, k[:, :, j * Sp:(j + 1) * Sp].contiguous(), v[:, :, j * Sp:(j + 1) * Sp].contiguous(),
+                           o_acc, l_acc, q_pos0=Sp, k_pos0=j * Sp, causal=True, scale=cfg.scale)
+        torch.cuda.synchronize()
+        by_kv = defaultdict(list)
+        for b, h, r in rows:
+            by_kv[(b, h // group)].append((h, r))
+        worst_o = worst_l = 0.0
+        for (b, g), hr in sorted(by_kv.items()):
+            k_np = k[b, g, :nblk * Sp].float().cpu().numpy()
+            v_np = v[b, g, :nblk * Sp].float().cpu().numpy()
+            hs = torch.tensor([x[0] for x in hr], device=DEV)
+            rs = torch.tensor([x[1] for x in hr], device=DEV)
+            o_ref, l_ref = oracle.attention_rows(qi[b, hs, rs].float().cpu().numpy(), Sp + rs.cpu().numpy(), k_np,
+                                                 v_np, scale=cfg.scale, causal=True, k_pos0=0)
+            do, dl = assert_close(np64(o_acc[b, hs, rs]), np64(l_acc[b, hs, rs]), o_ref, l_ref, "bf16",
+                                  f"{cfg.name} step {nblk} kv head {g}")
+            worst_o, worst_l = max(worst_o, do), max(worst_l, dl)
+        say(f"{cfg.name} after {nblk} step(s): {len(rows)} rows, max|dO| {worst_o:.3e}, max|dLSE| {worst_l:.3e}")
+
+
 @pytest.mark.timeout(1200)
 def test_c4_sampled_rows_and_closed_form(ra):
     cfg = CONFIGS["C4"]
