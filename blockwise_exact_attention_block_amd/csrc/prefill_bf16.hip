@@ -18,11 +18,12 @@
 //     S^T = K Q^T, so each lane owns one query column of the score tile and the row
 //     maximum / sum are in-lane plus one exchange with the lane 32 apart
 //     (v_permlane32_swap).
-//   * K and V tiles of BK keys (128 for head dims up to 128, else 64, so that two
-//     tiles fit in LDS) are double buffered in LDS and go straight from HBM into it
-//     (buffer_load ... lds, one tile ahead). At D = 128 the rows are unpadded
-//     256-byte rows whose 16-byte chunks are XOR-swizzled against bank conflicts;
-//     the other head dims keep rows padded against bank conflicts.
+//   * K and V tiles of BK keys are double buffered in LDS and go straight from HBM
+//     into it (buffer_load ... lds, one tile ahead). At D = 128 and at D_qk = 192,
+//     D_v = 128 the tiles are 128 keys of unpadded rows whose 16-byte chunks are
+//     XOR-swizzled against bank conflicts (two such tiles take 128 KB and exactly
+//     160 KB of LDS); D = 64 keeps 128-key tiles of rows padded against bank
+//     conflicts.
 //   * One online-softmax update per tile: S^T for all BK keys (BK/32 accumulator
 //     blocks, exact fp32 scores of the bf16 inputs), the tile's row max, then
 //     P = exp2(scale * log2(e) * s - m) and PV. Each row carries a reference shift m
@@ -50,21 +51,23 @@ constexpr float kLazyShift = 8.0f;
 
 template <int DQK, int DV, int NQ, int NW>
 struct PCfg {
-  // keys per tile: 128 where two double-buffered tiles fit in LDS, else 96; all of
-  // a tile's keys go through one online-softmax update
-  static constexpr int BK = DQK <= 128 ? 128 : 96;
+  // 128 keys per tile, all through one online-softmax update. Two double-buffered
+  // tiles take 128 KB of LDS at D = 128, exactly 160 KB at D_qk = 192 / D_v = 128
+  // (unpadded rows) and 84 KB at D = 64 (padded rows).
+  static constexpr int BK = 128;
   static constexpr int THREADS = NW * 64;
   static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
-  // D = 128: unpadded rows with an XOR swizzle of 16-byte chunks. Other head dims:
-  // rows padded so that consecutive K rows (16-byte reads) and V rows (transposed
-  // 8-byte reads) start on different banks. Either way each lane's reads are a
-  // per-lane base plus a compile-time offset.
-  static constexpr bool DMA = DQK == 128 && DV == 128;
-  static_assert(!DMA || DQK == DV, "the direct loads share one row layout between K and V");
-  static constexpr int KS = DMA ? DQK : DQK + 8;
-  static constexpr int VS = DMA ? DV : DV + 32;
+  // D = 128 (DMA) and D_qk = 192 (DMAW): unpadded rows with an XOR swizzle of
+  // 16-byte chunks. D = 64: rows padded so that consecutive K rows (16-byte reads)
+  // and V rows (transposed 8-byte reads) start on different banks. Either way each
+  // lane's reads are a per-lane base plus a compile-time offset.
+  static constexpr bool DMA = DQK == 128 && DV == 128;     // one 256-byte row layout for K and V
+  static constexpr bool DMAW = DQK == 192 && DV == 128;    // 384-byte K rows, 256-byte V rows
+  static constexpr int KS = (DMA || DMAW) ? DQK : DQK + 8;
+  static constexpr int VS = (DMA || DMAW) ? DV : DV + 32;
   static constexpr int K_TILE = padded_tile_bytes(BK, KS * 2) / 2;   // elements, whole KB
   static constexpr int V_TILE = padded_tile_bytes(BK, VS * 2) / 2;
+  static_assert(2 * (K_TILE + V_TILE) * 2 <= 160 * 1024, "two tiles of K and V must fit in LDS");
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
   static constexpr int MT = DV / 32;                  // 32-row output tiles along D_v
 };
@@ -169,7 +172,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     else
       ++walk_n;
   };
-  // ---- direct HBM -> LDS tiles (D = 128) ---------------------------------------------
+  // ---- direct HBM -> LDS tiles (unpadded, swizzled rows) ---------------------------
   // A 256-byte row holds 16 chunks of 16 bytes; chunk c of row r sits in slot
   // c ^ swz(r). swz is a bijection on 16 consecutive rows (conflict-free K reads of
   // one chunk across 16 rows) and, on the 4 rows x 2 chunk pairs that a half wave's
@@ -178,30 +181,57 @@ prefill_bf16_kernel(PrefillArgs a) {
     const int x = r & 7;
     return ((((x & 3) << 1) | (x >> 2)) << 1) | ((r >> 3) & 1);
   };
-  constexpr int ROWB = DQK * 2;
-  constexpr int NI = C::DMA ? BK * ROWB / 1024 / NW : 1;   // 1 KB loads per wave per tile
+  constexpr int ROWB = DQK * 2, ROWBV = DV * 2;
+  constexpr bool SWZ = C::DMA || C::DMAW;
+  constexpr int NI = SWZ ? BK * ROWBV / 1024 / NW : 1;    // 1 KB V loads per wave per tile
+  constexpr int NIK = C::DMAW ? BK * ROWB / 1024 / NW : 1; // 1 KB K loads per wave per tile (384-byte rows)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  unsigned dgo[NI];
-  if constexpr (C::DMA) {
+  // 384-byte K rows (D_qk = 192): the low three bits of chunk c of row r are XORed
+  // with (r >> 1) & 7, which keeps c within its group of 8 chunks. Consecutive rows
+  // start 32 banks apart, so the 16 rows of a 16-byte read of one chunk fall on 16
+  // distinct 4-bank groups. A 1 KB load covers 2 2/3 rows, so each lane's global
+  // offset is precomputed per load.
+  auto kswz = [](int r) __attribute__((always_inline)) { return (r >> 1) & 7; };
+  unsigned dgo[NI], dgok[NIK];
+  if constexpr (SWZ) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int row = wave * (BK / NW) + 4 * j + (lane >> 4);
-      dgo[j] = (unsigned)(row * ROWB + 16 * ((lane & 15) ^ swz(row)));
+      dgo[j] = (unsigned)(row * ROWBV + 16 * ((lane & 15) ^ swz(row)));
     }
   }
-  const unsigned kv_bytes_last = (unsigned)((size_t)a.kv_rows * ROWB - 16);
+  if constexpr (C::DMAW) {
+#pragma unroll
+    for (int q = 0; q < NIK; ++q) {
+      const int b = 1024 * (wave * NIK + q) + 16 * lane;
+      const int row = b / ROWB, slot = (b - row * ROWB) / 16;
+      dgok[q] = (unsigned)(row * ROWB + 16 * (slot ^ kswz(row)));
+    }
+  }
+  const unsigned kv_bytes_last = (unsigned)((size_t)a.kv_rows * ROWBV - 16);
+  const unsigned k_bytes_last = (unsigned)((size_t)a.kv_rows * ROWB - 16);
   const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
   const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
   const unsigned k_lds = lds_addr(&ks[0][0]), v_lds = lds_addr(&vs[0][0]);
   // other head dims: the same direct loads into the padded rows, 1 KB piece by piece
   PaddedTileDma<BK, DQK * 2, C::KS * 2, NW> kpad;
   PaddedTileDma<BK, DV * 2, C::VS * 2, NW> vpad;
-  if constexpr (!C::DMA) {
+  if constexpr (!SWZ) {
     kpad.init(wave_u, lane);
     vpad.init(wave_u, lane);
   }
   auto dma_tile = [&](const TileRef& t, int buf) __attribute__((always_inline)) {
-    if constexpr (!C::DMA) {
+    if constexpr (C::DMAW) {
+      const unsigned kbase = (unsigned)t.row0 * ROWB, vbase = (unsigned)t.row0 * ROWBV;
+#pragma unroll
+      for (int q = 0; q < NIK; ++q)
+        lds_load16(k_lds + (unsigned)(buf * C::K_TILE * 2 + 1024 * (wave_u * NIK + q)), min(kbase + dgok[q], k_bytes_last),
+                   kdesc);
+#pragma unroll
+      for (int j = 0; j < NI; ++j)
+        lds_load16(v_lds + (unsigned)(buf * C::V_TILE * 2 + (wave_u * (BK / NW) + 4 * j) * ROWBV),
+                   min(vbase + dgo[j], kv_bytes_last), vdesc);
+    } else if constexpr (!C::DMA) {
       kpad.issue(wave_u, k_lds + (unsigned)(buf * C::K_TILE * 2), (unsigned)t.row0 * (DQK * 2),
                  (unsigned)((size_t)a.kv_rows * DQK * 2 - 16), kdesc);
       vpad.issue(wave_u, v_lds + (unsigned)(buf * C::V_TILE * 2), (unsigned)t.row0 * (DV * 2),
@@ -263,26 +293,41 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int gg = lane >> 4, L = lane & 15;
   // swizzled LDS byte addresses inside a tile: K chunk 2s+h of row l32, and the
   // transposed V read of row 8x + r4, column block mt
-  unsigned kra[C::DS], vra[2][C::MT];
+  unsigned kra[C::DMAW ? 8 : C::DS], vra[2][C::MT];
   if constexpr (C::DMA) {
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       kra[s] = k_lds + (unsigned)(l32 * ROWB + 16 * ((2 * s + h) ^ swz(l32)));
       asm volatile("" : "+v"(kra[s]));   // keep the lane base in a register: tile offsets stay immediates
     }
+  }
+  if constexpr (C::DMAW) {
+    // chunk 2s + h = 8 (s / 4) + (2 (s % 4) + h): the XOR only touches the low three
+    // bits, so four bases per buffer cover all twelve D steps
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kra[4 * b + u] = k_lds + (unsigned)(b * C::K_TILE * 2 + l32 * ROWB + 16 * ((2 * u + h) ^ kswz(l32)));
+        asm volatile("" : "+v"(kra[4 * b + u]));
+      }
+  }
+  if constexpr (SWZ) {
     const int r4 = 4 * (gg >> 1) + (L >> 2);
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         const int c = 4 * mt + 2 * (gg & 1) + ((L >> 1) & 1);
-        vra[x][mt] = v_lds + (unsigned)((8 * x + r4) * ROWB + 16 * (c ^ swz(8 * x + r4)) + 8 * (L & 1));
+        vra[x][mt] = v_lds + (unsigned)((8 * x + r4) * ROWBV + 16 * (c ^ swz(8 * x + r4)) + 8 * (L & 1));
         asm volatile("" : "+v"(vra[x][mt]));
       }
   }
   auto kfrag = [&](int buf, int krow0, int s) __attribute__((always_inline)) -> bf16x8 {
     if constexpr (C::DMA)
       return *(RA_LDS const bf16x8*)(uintptr_t)(kra[s] + (unsigned)(buf * C::K_TILE * 2 + krow0 * ROWB));
+    else if constexpr (C::DMAW)
+      return *(RA_LDS const bf16x8*)(uintptr_t)(kra[4 * buf + (s & 3)] + (unsigned)(128 * (s >> 2) + krow0 * ROWB));
     else
       return *(const bf16x8*)&ks[buf][(krow0 + l32) * C::KS + 16 * s + 8 * h];
   };
@@ -384,8 +429,8 @@ prefill_bf16_kernel(PrefillArgs a) {
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          if constexpr (C::DMA) {
-            f[t2][x] = lds_read_tr16_at(vra[x][mt] + (unsigned)(buf * C::V_TILE * 2 + (kt * 32 + 16 * t2) * ROWB));
+          if constexpr (SWZ) {
+            f[t2][x] = lds_read_tr16_at(vra[x][mt] + (unsigned)(buf * C::V_TILE * 2 + (kt * 32 + 16 * t2) * ROWBV));
           } else {
             const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
             const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);

@@ -12,8 +12,9 @@ against two properties:
     backward's former layout (rows padded by 16, natural order) is 2-way
     conflicted, which the counters showed as 38-40 % of LDS-active cycles.
 The layouts checked: the prefill's XOR-swizzled 256-byte rows (prefill_bf16.hip,
-D = 128), its padded rows for the other head dims, and the backward's
-(D + 8)-element rows read in the perm16 row order (backward_bf16.hip)."""
+D = 128, and V at D_qk = 192), its 384-byte K rows at D_qk = 192, its padded rows
+at D = 64, and the backward's (D + 8)-element rows read in the perm16 row order
+(backward_bf16.hip)."""
 import pytest
 
 
@@ -82,7 +83,7 @@ def padded_tile_dma_map(rows, row_bytes, stride, nw):
 
 @pytest.mark.parametrize("rows,row_bytes,stride", [
     (128, 128, 144), (128, 128, 192),    # prefill D = 64: K, V
-    (96, 384, 400), (96, 256, 320),      # prefill D_qk = 192, D_v = 128: K (37.5 KB), V
+    (96, 384, 400),                      # a tile that is not whole KB (37.5 KB): slack
     (128, 256, 272),                     # dQ kernel D = 128: K and V
     (64, 256, 272), (64, 128, 144),      # dK/dV kernel Q and dO, D = 128 and 64
 ])
@@ -118,13 +119,49 @@ def test_prefill_swizzle_reads_are_conflict_free():
     assert max(banks_max(p, 8) for p in tr_read_passes(v_addr)) == 1
 
 
-@pytest.mark.parametrize("stride,kind", [(144, "row"), (400, "row"), (192, "tr"), (320, "tr")])
+@pytest.mark.parametrize("stride,kind", [(144, "row"), (192, "tr")])
 def test_prefill_padded_rows_are_conflict_free(stride, kind):
-    if kind == "row":   # K rows of D = 64 (144 B) and D_qk = 192 (400 B)
+    if kind == "row":   # K rows of D = 64 (144 B)
         worst = max(banks_max(p, 16) for p in row_read_passes(lambda r, c: r * stride + 16 * c, 96, stride // 16 - 1))
     else:               # V rows padded by 32 elements, read transposed
         worst = max(banks_max(p, 8) for p in tr_read_passes(lambda rho, col: rho * stride + 2 * col))
     assert worst == 1
+
+
+# ---- prefill, D_qk = 192: 384-byte K rows, low three chunk bits XORed -----------
+
+def kswz(r):
+    return (r >> 1) & 7
+
+
+def test_prefill_wide_k_tile_loads_and_reads():
+    """The 1 KB direct loads of a 128-key tile of 384-byte K rows (6 per wave, each
+    lane's global offset precomputed) fill every slot with the chunk the reads take:
+    chunk 2 s + h of row krow0 + l32 at lane base kra[4 buf + s % 4] + 128 (s / 4)
+    + krow0 * 384, an immediate offset below 64 KB. The reads are conflict-free."""
+    rowb, bk, nw, nik = 384, 128, 8, 6
+    lds = {}
+    for wave in range(nw):
+        for q in range(nik):
+            for lane in range(64):
+                b = 1024 * (wave * nik + q) + 16 * lane
+                row, slot = b // rowb, (b % rowb) // 16
+                lds[b] = row * rowb + 16 * (slot ^ kswz(row))
+    assert sorted(lds) == list(range(0, bk * rowb, 16)) and sorted(lds.values()) == sorted(lds)
+
+    def addr(krow0, s, l32, h):
+        return l32 * rowb + 16 * ((2 * (s & 3) + h) ^ kswz(l32)) + 128 * (s >> 2) + krow0 * rowb
+
+    for krow0 in range(0, bk, 32):
+        for s in range(12):
+            for l32 in range(32):
+                for h in range(2):
+                    a = addr(krow0, s, l32, h)
+                    assert a - l32 * rowb - 16 * ((2 * (s & 3) + h) ^ kswz(l32)) < 65536
+                    assert lds[a] == (krow0 + l32) * rowb + 16 * (2 * s + h)
+            for h in range(2):
+                for half in range(2):
+                    assert banks_max([addr(krow0, s, l, h) for l in range(16 * half, 16 * half + 16)], 16) == 1
 
 
 # ---- backward: (D + 8)-element rows read in the perm16 order -------------------
