@@ -394,7 +394,13 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (__any(move)) {
       const float sh = move ? lead : 0.f;
       m[0] += sh;
-      const float alpha = exp2_hw(-sh);
+      // A row that had keys before moves only by sh > kLazyShift, so its correction
+      // 2^-sh is below one. A row seeing its first keys has l = 0 and a zero
+      // accumulator, and its shift may move by any amount, also far downwards
+      // (every score of the tile strongly negative), where 2^-sh would overflow
+      // to +inf and 0 * inf would be NaN. Capping the exponent at 0 keeps the
+      // correction finite for every row and changes nothing for the others.
+      const float alpha = exp2_hw(fminf(-sh, 0.f));
       l[0] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) oacc[0][mt] *= alpha;

@@ -6,7 +6,15 @@ inputs that almost never happens after a row's first tile. These cases make it
 happen often:
   * q scaled by 8 (exact in bf16): scores with a standard deviation of about 8;
   * a key ramp: key rows scaled up along the sequence, so a row's maximum keeps
-    growing and the shift moves many times within a row.
+    growing and the shift moves many times within a row;
+  * strongly negative scores ("neg"): queries and keys share one direction u with
+    opposite signs, q = 4u + noise and k = -4u + noise, so every scaled score is
+    about -16 D / sqrt(D) (-128 at D = 64, -181 at D = 128, -222 at D = 192) with a
+    spread of a few units. A row's first visible tile then moves its shift far
+    downwards (below -128 in log2 units, where 2^-shift overflows fp32);
+  * the same with only some keys anti-aligned ("negmix": 64-key runs, chosen at
+    random, keep N(0,1) keys): rows start on a strongly negative tile and later
+    meet ordinary scores, so the shift moves down and then far up again.
 Gates (the N(0,1) ones do not apply: these outputs are not small):
   * O: |err| <= 2e-2 + 2^-7 |O_ref| per element. The kernel's O is
     round_bf16(sum_k bf16(P_k) v_k / l): P's rounding (relative 2^-9 per key)
@@ -20,7 +28,13 @@ Gates (the N(0,1) ones do not apply: these outputs are not small):
   * Gradients: max |err| <= 2e-2 max|ref| and mean |err| <= 1e-2 mean|ref|. Emulating
     the backward's roundings in fp64 (P and dS in bf16, delta from the bf16 output)
     on the ramp case gives a mean dQ error of 0.47 % of the mean |ref|. It comes
-    from the cancellation dP - delta on a dominant key; the gate is twice that."""
+    from the cancellation dP - delta on a dominant key; the gate is twice that.
+    On the strongly negative inputs dQ = scale dS K cancels more: every key carries
+    the shared component -4u, whose contribution sum_c dS_rc (-4u) is exactly zero
+    (the rows of dS sum to zero) but only up to dS's bf16 rounding, while the true
+    dQ is made of the small noise part. The same emulation gives a mean dQ error of
+    1.6 % (D = 64) and 2.4 % (D = 128) of the mean |ref| there, so that case gates
+    dQ's mean at 5e-2; dK and dV keep the gates above."""
 import math
 
 import numpy as np
@@ -52,10 +66,21 @@ def sharp_inputs(B, Hq, Hkv, S, Dqk, Dv, *, seed, kind):
     q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, Dqk, Dv, seed=seed, dtype="bf16")
     if kind == "q8":
         q = q * 8.0                                             # exact: a power of two
-    else:                                                       # "ramp"
+    elif kind == "ramp":
         q = q * 2.0
         ramp = (1.0 + 5.0 * np.arange(S) / S).astype(np.float32)
         k = _bf16_round_np(k * ramp[None, None, :, None])
+    else:                                                       # "neg", "negmix"
+        u = np.sign(randn_np((Dqk,), seed + 40)).astype(np.float32)
+        q = _bf16_round_np(q + 4.0 * u)
+        kn = _bf16_round_np(k - 4.0 * u)
+        if kind == "neg":
+            k = kn
+        else:
+            g = np.random.default_rng(seed + 41)
+            runs = g.random((B, Hkv, (S + 63) // 64)) < 0.5
+            anti = np.repeat(runs, 64, axis=2)[:, :, :S, None]
+            k = np.where(anti, kn, k)
     return q, k, v
 
 
@@ -81,7 +106,7 @@ def grad_close(got, ref, what, rmax=2e-2, rmean=1e-2):
     assert err.mean() <= rmean * np.abs(ref).mean() + 1e-7, what
 
 
-@pytest.mark.parametrize("kind", ["q8", "ramp"])
+@pytest.mark.parametrize("kind", ["q8", "ramp", "neg", "negmix"])
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
@@ -103,7 +128,7 @@ def test_ring_sharp(ra, kind, dims, causal, layout):
     sharp_close(np64(o), np64(lse), o_ref, l_ref, f"sharp {kind} {layout}")
 
 
-@pytest.mark.parametrize("kind", ["q8", "ramp"])
+@pytest.mark.parametrize("kind", ["q8", "ramp", "neg", "negmix"])
 def test_step_chain_sharp(ra, kind):
     """Block steps carrying the running state: each step may have to move a shift
     that arrived from the previous block (the state's m is its LSE)."""
@@ -128,7 +153,7 @@ def test_step_chain_sharp(ra, kind):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("kind", ["q8", "ramp"])
+@pytest.mark.parametrize("kind", ["q8", "ramp", "neg"])
 def test_backward_sharp(ra, D, kind):
     """Forward on the GPU, then the whole backward: exact gradients of the same bf16
     inputs."""
@@ -143,7 +168,7 @@ def test_backward_sharp(ra, D, kind):
     gq, gk, gv = ra.attn_bwd(dq_, dk_, dv_, o, lse, to_dev(do), causal=True)
     torch.cuda.synchronize()
     rq, rk, rv, _, _ = oracle.attention_bwd(q, k, v, do, scale=1 / math.sqrt(D), causal=True)
-    grad_close(gq, rq, "dq")
+    grad_close(gq, rq, "dq", rmean=5e-2 if kind == "neg" else 1e-2)
     grad_close(gk, rk, "dk")
     grad_close(gv, rv, "dv")
 
@@ -158,3 +183,59 @@ def test_decode_sharp(ra):
     torch.cuda.synchronize()
     op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
     sharp_close(np64(o), np64(l), o_r, l_r, "decode sharp")
+
+
+@pytest.mark.parametrize("kind", ["neg", "negmix"])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_step_chain_from_empty_negative(ra, kind, dims, causal, layout):
+    """Every partition's ring run as block steps from the empty state (O = 0,
+    LSE = -inf), with strongly negative scores: the first step of each row starts
+    from LSE = -inf and sees only scores far below zero. Striped steps use the
+    virtual positions of the striped mask (query: local row; key: local index plus
+    [j > i])."""
+    B, Hq, Hkv, Sp, P = 1, 4, 2, 160, 3
+    Dqk, Dv = dims
+    S = Sp * P
+    say(f"block_attn_step from empty, {kind} D{Dqk}/{Dv} causal={causal} {layout}")
+    q, k, v = sharp_inputs(B, Hq, Hkv, S, Dqk, Dv, seed=1100 + Dqk, kind=kind)
+    scale = 1 / math.sqrt(Dqk)
+    # row r of the stored arrays is global token pos[r]
+    pos = np.concatenate([oracle.partition_positions(P, Sp, p, layout) for p in range(P)])
+    o_ref, l_ref = oracle.attention(q, k, v, scale=scale, causal=causal, q_pos=pos, k_pos=pos)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    for i in range(P):
+        qi = qd[:, :, i * Sp:(i + 1) * Sp].contiguous()
+        o_acc, l_acc = ra.init_state(qi, Dv)
+        for j, kind_j in ra.ring_schedule(P, i, causal, layout):
+            if kind_j == "skip":
+                continue
+            if layout == "contiguous":
+                qp, kp = i * Sp, j * Sp
+            else:
+                qp, kp = 0, (1 if j > i else 0)
+            ra.block_attn_step(qi, kd[:, :, j * Sp:(j + 1) * Sp].contiguous(),
+                               vd[:, :, j * Sp:(j + 1) * Sp].contiguous(), o_acc, l_acc,
+                               q_pos0=qp, k_pos0=kp, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        sl = slice(i * Sp, (i + 1) * Sp)
+        sharp_close(np64(o_acc), np64(l_acc), o_ref[:, :, sl], l_ref[:, :, sl],
+                    f"step chain from empty, part {i}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_negative(ra, D):
+    """Split-KV decode where every score of the token is strongly negative."""
+    B, Hq, Hkv, L, n = 2, 16, 2, 1000, 4
+    say(f"splitkv_decode negative scores D{D}")
+    u = np.sign(randn_np((D,), 1200 + D)).astype(np.float32)
+    q = _bf16_round_np(randn_np((B, Hq, D), 1201 + D, "bf16") + 4.0 * u)
+    k = _bf16_round_np(randn_np((B, Hkv, L, D), 1202 + D, "bf16") - 4.0 * u)
+    v = randn_np((B, Hkv, L, D), 1203 + D, "bf16")
+    op, lp, o, l = ra.splitkv_decode(to_dev(q), to_dev(k), to_dev(v), n_splits=n)
+    torch.cuda.synchronize()
+    op_r, lp_r, o_r, l_r = oracle.splitkv_decode(q, k, v, n_splits=n, scale=1 / math.sqrt(D))
+    assert float(np.max(l_r)) < -100.0          # the case is what it claims to be
+    sharp_close(np64(o), np64(l), o_r, l_r, "decode negative")
+    sharp_close(np64(op), np64(lp), op_r, lp_r, "decode negative partials")
