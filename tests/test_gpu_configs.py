@@ -192,11 +192,14 @@ def test_c5f_fp8_cache_every_row_and_partial(ra):
 
 @pytest.mark.timeout(900)
 def test_c3_backward_sampled_rows_and_keys(ra):
-    """Backward at the full C3 shape, in the launch configuration bench.py times.
-    dQ rows: exact gradients (the oracle's forward statistics of each sampled row
-    over its whole causal key range). dK / dV keys: the definition of one key's
-    gradient summed over every query of its group that sees it, given the GPU's
-    saved row LSE and delta (the step's inputs, checked themselves above)."""
+    """Backward at the full C3 shape, in the launch configuration bench.py times,
+    against references computed from the inputs alone (no GPU output enters them).
+    dQ rows: exact gradients, with the oracle's forward statistics of each sampled
+    row over its whole causal key range. dK / dV keys: keys in the sequence's last
+    tiles (its last key, the tile boundaries around it and random ones), whose
+    gradients sum over only the few hundred query rows at or after them; each of
+    those rows' LSE and delta = dO . O comes from the oracle's forward over the
+    row's whole causal range."""
     cfg = CONFIGS["C3"]
     q, k, v = prefill_inputs_torch(cfg, DEV)
     o, lse = run_prefill(ra, cfg, q, k, v)
@@ -204,20 +207,19 @@ def test_c3_backward_sampled_rows_and_keys(ra):
     dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
     say(f"attn_bwd {cfg.name} (whole sequence)")
     dq, dk, dv = ra.attn_bwd(q, k, v, o, lse, dout, causal=True, scale=cfg.scale)
-    delta = ra.attn_bwd_preprocess(o, dout)
     torch.cuda.synchronize()
-    del o
+    del o, lse
     group = cfg.Hq // cfg.Hkv
     rng = np.random.default_rng(cfg.seed + 11)
     worst = 0.0
     # dQ of sampled rows, exact
     for g in (0, cfg.Hkv - 1):
-        k_np, v_np = k[0, g].float().cpu().numpy(), v[0, g].float().cpu().numpy()
+        k_np, v_np = k[0, g].double().cpu().numpy(), v[0, g].double().cpu().numpy()
         for h in (g * group, g * group + group - 1):
             rows = np.unique(np.concatenate([rng.integers(0, cfg.Sq, 6), [0, cfg.Sq - 1, cfg.Sp, cfg.Sp - 1]]))
             rt = torch.as_tensor(rows, device=DEV)
-            qr = q[0, h, rt].float().cpu().numpy()
-            dr = dout[0, h, rt].float().cpu().numpy()
+            qr = q[0, h, rt].double().cpu().numpy()
+            dr = dout[0, h, rt].double().cpu().numpy()
             o_r, l_r = oracle.attention_rows(qr, rows, k_np, v_np, scale=cfg.scale, causal=True)
             d_r = (dr * o_r).sum(-1)
             ref, _, _ = oracle.block_bwd(qr[None, None], k_np[None, None], v_np[None, None], dr[None, None],
@@ -227,25 +229,64 @@ def test_c3_backward_sampled_rows_and_keys(ra):
             err = np.abs(got - ref[0, 0]).max() / np.abs(ref[0, 0]).max()
             worst = max(worst, err)
             assert err <= 2e-2, (g, h, err)
-    # dK, dV of sampled keys, given the saved row statistics
+    # dK, dV of keys in the last 256 positions: every query row that sees them
+    S = cfg.S
     for g in (0, cfg.Hkv // 2):
-        keys = np.unique(np.concatenate([rng.integers(0, cfg.S, 3), [0, cfg.S - 1]]))
-        kt = torch.as_tensor(keys, device=DEV)
-        k_s = k[0, g, kt].float().cpu().numpy()
-        v_s = v[0, g, kt].float().cpu().numpy()
-        ref_k = np.zeros_like(k_s, dtype=np.float64)
-        ref_v = np.zeros_like(v_s, dtype=np.float64)
+        keys = np.unique(np.concatenate([S - 1 - rng.integers(0, 256, 3),
+                                         [S - 1, S - 2, S - 64, S - 127, S - 128, S - 129, S - 256]]))
+        r0 = int(keys.min())
+        rows = np.arange(r0, S)
+        k_np, v_np = k[0, g].double().cpu().numpy(), v[0, g].double().cpu().numpy()
+        k_s, v_s = k_np[keys], v_np[keys]
+        ref_k = np.zeros_like(k_s)
+        ref_v = np.zeros_like(v_s)
         for h in range(g * group, (g + 1) * group):
-            qh = q[0, h].float().cpu().numpy()
-            dh = dout[0, h].float().cpu().numpy()
+            qh = q[0, h, r0:].double().cpu().numpy()
+            dh = dout[0, h, r0:].double().cpu().numpy()
+            o_ref, l_ref = oracle.attention_rows(qh, rows, k_np, v_np, scale=cfg.scale, causal=True)
+            d_ref = (dh * o_ref).sum(-1)
             _, gk, gv = oracle.block_bwd(qh[None, None], k_s[None, None], v_s[None, None], dh[None, None],
-                                         lse[0, h].double().cpu().numpy()[None, None],
-                                         delta[0, h].double().cpu().numpy()[None, None], scale=cfg.scale,
-                                         causal=True, q_pos0=0, k_pos=keys)
+                                         l_ref[None, None], d_ref[None, None], scale=cfg.scale, causal=True,
+                                         q_pos=rows, k_pos=keys)
             ref_k += gk[0, 0]
             ref_v += gv[0, 0]
+        kt = torch.as_tensor(keys, device=DEV)
         for got, ref, name in ((dk[0, g, kt], ref_k, "dk"), (dv[0, g, kt], ref_v, "dv")):
             err = np.abs(got.double().cpu().numpy() - ref).max() / np.abs(ref).max()
             worst = max(worst, err)
             assert err <= 2e-2, (name, g, err)
     say(f"C3 backward: worst relative max error {worst:.3e}")
+
+
+@pytest.mark.timeout(900)
+def test_c3_backward_zero_query_closed_form(ra):
+    """Q = 0 at the full C3 shape: every visible probability is 1 / (r + 1) for
+    query row r (causal), so dV at key c is sum_{r >= c} dO_r / (r + 1), summed over
+    the KV head's query heads -- a reverse cumulative sum, taken here in float64
+    with torch on the device (no kernel of this library) -- and dK = scale dS^T Q
+    is exactly zero. Checked at every key of every KV head, through the GPU
+    forward and the whole backward."""
+    cfg = CONFIGS["C3"]
+    _, k, v = prefill_inputs_torch(cfg, DEV)
+    q0 = torch.zeros((cfg.B, cfg.Hq, cfg.Sq, cfg.Dqk), dtype=torch.bfloat16, device=DEV)
+    o, lse = run_prefill(ra, cfg, q0, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 8)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    say(f"attn_bwd {cfg.name} with Q = 0 (whole sequence)")
+    dq, dk, dv = ra.attn_bwd(q0, k, v, o, lse, dout, causal=True, scale=cfg.scale)
+    torch.cuda.synchronize()
+    del o, lse, dq
+    assert torch.count_nonzero(dk).item() == 0, "dK must be exactly zero when Q = 0"
+    group = cfg.Hq // cfg.Hkv
+    inv = 1.0 / torch.arange(1, cfg.S + 1, device=DEV, dtype=torch.float64)
+    worst_max = worst_mean = 0.0
+    for g in range(cfg.Hkv):
+        x = dout[0, g * group:(g + 1) * group].double().sum(0) * inv[:, None]
+        ref = torch.flip(torch.cumsum(torch.flip(x, (0,)), 0), (0,))
+        err = (dv[0, g].double() - ref).abs()
+        rmax = float(err.max()) / float(ref.abs().max())
+        rmean = float(err.mean()) / float(ref.abs().mean())
+        worst_max, worst_mean = max(worst_max, rmax), max(worst_mean, rmean)
+        del x, ref, err
+    say(f"C3 backward Q=0: dV worst relative max error {worst_max:.3e}, mean {worst_mean:.3e}")
+    assert worst_max <= 2e-2 and worst_mean <= 5e-3, (worst_max, worst_mean)
