@@ -136,6 +136,32 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _expect(t: torch.Tensor, shape, name: str, dtype=None) -> None:
+    """Raise RingAttnError unless t is a tensor of exactly `shape` (and `dtype`).
+    The C ABI sees only pointers, so a tensor smaller than the sizes passed with it
+    would be read or written past its end; every wrapper checks every tensor here
+    before any pointer crosses the boundary."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise RingAttnError(1, f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise RingAttnError(1, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _ndim(t: torch.Tensor, n: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != n:
+        raise RingAttnError(1, f"{name} must have {n} dimensions, not {t.dim()}")
+
+
+def _same_device(ref: torch.Tensor, *named) -> None:
+    for t, name in named:
+        if t.device != ref.device:
+            raise RingAttnError(1, f"{name} is on {t.device}, not on {ref.device} with the others")
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -172,8 +198,15 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, 
     Returns (o [B,Hq,nq*Sp,Dv] in q's dtype, lse [B,Hq,nq*Sp] fp32)."""
     lib = load_library()
     fn = lib.ra_ring_attn_fwd_striped if _layout(layout) else lib.ra_ring_attn_fwd
+    _ndim(q, 4, "q")
+    _ndim(k, 4, "k")
+    _ndim(v, 4, "v")
     B, Hq, Sq, Dqk = q.shape
     Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    _expect(k, (B, Hkv, Skv, Dqk), "k")
+    _expect(v, (B, Hkv, Skv, Dv), "v")
+    if P <= 0:
+        raise RingAttnError(1, f"P must be positive, not {P}")
     if Skv % P:
         raise RingAttnError(1, f"KV length {Skv} is not P={P} equal blocks")
     Sp = Skv // P
@@ -188,6 +221,9 @@ def ring_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, P: int, 
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype or lse.dtype != torch.float32:
         raise RingAttnError(1, "q, k, v, out must share one dtype and lse must be fp32")
+    _expect(out, (B, Hq, Sq, Dv), "out")
+    _expect(lse, (B, Hq, Sq), "lse")
+    _same_device(q, (k, "k"), (v, "v"), (out, "out"), (lse, "lse"))
     _check(fn(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
               _dev(lse, "lse"), B, Hq, Hkv, Sp, int(P), int(q_part0), nq, Dqk, Dv,
               float(scale), int(bool(causal)), _stream(q)))
@@ -208,8 +244,14 @@ def block_attn_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, o
     """Merge one KV block (keys at k_pos0..) into the running fp32 state of the
     queries at q_pos0.., in place."""
     lib = load_library()
+    _ndim(q, 4, "q")
+    _ndim(k_blk, 4, "k_blk")
+    _ndim(v_blk, 4, "v_blk")
     B, Hq, Sq, Dqk = q.shape
     Hkv, Sk, Dv = k_blk.shape[1], k_blk.shape[2], v_blk.shape[3]
+    _expect(k_blk, (B, Hkv, Sk, Dqk), "k_blk")
+    _expect(v_blk, (B, Hkv, Sk, Dv), "v_blk")
+    _same_device(q, (k_blk, "k_blk"), (v_blk, "v_blk"), (o_acc, "o_acc"), (lse_acc, "lse_acc"))
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     if o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32:
@@ -239,6 +281,9 @@ def lse_merge(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: 
             raise RingAttnError(1, "lse_merge works on fp32 tensors")
     if o_b.shape != o_a.shape or lse_b.shape != lse_a.shape or o_a.numel() != rows * Dv:
         raise RingAttnError(1, "shape mismatch")
+    _expect(out, o_a.shape, "out")
+    _expect(lse_out, lse_a.shape, "lse_out")
+    _same_device(o_a, (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b"), (out, "out"), (lse_out, "lse_out"))
     _check(lib.ra_lse_merge(rows, Dv, _dev(o_a, "o_a"), _dev(lse_a, "lse_a"), _dev(o_b, "o_b"),
                             _dev(lse_b, "lse_b"), _dev(out, "out"), _dev(lse_out, "lse_out"), _stream(o_a)))
     return out, lse_out
@@ -252,6 +297,9 @@ def lse_merge_n(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torch.
     rows = int(math.prod(lead))
     if tuple(lse_parts.shape) != lead + (n,):
         raise RingAttnError(1, "lse_parts shape must be o_parts.shape[:-1]")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise RingAttnError(1, "o_parts and lse_parts must be fp32")
+    _same_device(o_parts, (lse_parts, "lse_parts"))
     o = torch.empty(lead + (Dv,), dtype=out_dtype, device=o_parts.device)
     lse = torch.empty(lead, dtype=torch.float32, device=o_parts.device)
     _check(lib.ra_lse_merge_n(_dtype_code(o), rows, n, Dv, _dev(o_parts, "o_parts"),
@@ -259,13 +307,33 @@ def lse_merge_n(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype=torch.
     return o, lse
 
 
+def _decode_shapes(q, k_cache, v_cache, n_splits, o_part=None, lse_part=None):
+    """Checks the decode tensors against each other; returns (B, Hq, Dqk, Hkv, L, Dv)."""
+    _ndim(q, 3, "q")
+    _ndim(k_cache, 4, "k_cache")
+    _ndim(v_cache, 4, "v_cache")
+    B, Hq, Dqk = q.shape
+    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    _expect(k_cache, (B, Hkv, L, Dqk), "k_cache")
+    _expect(v_cache, (B, Hkv, L, Dv), "v_cache")
+    if int(n_splits) <= 0:
+        raise RingAttnError(1, f"n_splits must be positive, not {n_splits}")
+    if o_part is not None:
+        _expect(o_part, (B, Hq, n_splits, Dv), "o_part", torch.float32)
+    if lse_part is not None:
+        _expect(lse_part, (B, Hq, n_splits), "lse_part", torch.float32)
+    named = [(k_cache, "k_cache"), (v_cache, "v_cache")]
+    named += [(t, n) for t, n in ((o_part, "o_part"), (lse_part, "lse_part")) if t is not None]
+    _same_device(q, *named)
+    return B, Hq, Dqk, Hkv, L, Dv
+
+
 def splitkv_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_splits: int,
                    scale: Optional[float] = None):
     """One query token per sequence: q [B,Hq,D], caches [B,Hkv,L,D]. Returns
     (o_part [B,Hq,n,D] fp32, lse_part [B,Hq,n] fp32, o [B,Hq,D] q.dtype, lse [B,Hq] fp32)."""
     lib = load_library()
-    B, Hq, Dqk = q.shape
-    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    B, Hq, Dqk, Hkv, L, Dv = _decode_shapes(q, k_cache, v_cache, n_splits)
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     dev = q.device
@@ -288,8 +356,7 @@ def splitkv_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     """Partial attention of each of the n_splits chunks: returns (o_part [B,Hq,n,D]
     fp32, lse_part [B,Hq,n] fp32); reduce them with lse_merge_n."""
     lib = load_library()
-    B, Hq, Dqk = q.shape
-    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    B, Hq, Dqk, Hkv, L, Dv = _decode_shapes(q, k_cache, v_cache, n_splits, o_part, lse_part)
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     if o_part is None:
@@ -319,8 +386,7 @@ def splitkv_partial_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     v_scale * v_cache; q is bf16. Returns (o_part, lse_part) fp32."""
     lib = load_library()
     ks, vs = _fp8_args(q, k_cache, v_cache, k_scale, v_scale)
-    B, Hq, Dqk = q.shape
-    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    B, Hq, Dqk, Hkv, L, Dv = _decode_shapes(q, k_cache, v_cache, n_splits, o_part, lse_part)
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     if o_part is None:
@@ -339,8 +405,7 @@ def splitkv_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     (o_part, lse_part, o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
     lib = load_library()
     ks, vs = _fp8_args(q, k_cache, v_cache, k_scale, v_scale)
-    B, Hq, Dqk = q.shape
-    Hkv, L, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    B, Hq, Dqk, Hkv, L, Dv = _decode_shapes(q, k_cache, v_cache, n_splits)
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     dev = q.device
@@ -364,6 +429,8 @@ def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, delta: Optional[tor
     rows = o.numel() // Dv
     if delta is None:
         delta = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    _expect(delta, o.shape[:-1], "delta", torch.float32)
+    _same_device(o, (dout, "dout"), (delta, "delta"))
     _check(lib.ra_attn_bwd_preprocess(_dtype_code(o), _dev(o, "o"), _dev(dout, "dout"), rows, Dv,
                                       _dev(delta, "delta"), _stream(o)))
     return delta
@@ -377,6 +444,9 @@ def block_attn_bwd_step(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, 
     accumulators dq_acc [B,Hq,Sq,Dqk], dk_acc [B,Hkv,Sk,Dqk], dv_acc [B,Hkv,Sk,Dv].
     lse / delta are the queries' full-row values."""
     lib = load_library()
+    _ndim(q, 4, "q")
+    _ndim(k_blk, 4, "k_blk")
+    _ndim(v_blk, 4, "v_blk")
     B, Hq, Sq, Dqk = q.shape
     Hkv, Sk, Dv = k_blk.shape[1], k_blk.shape[2], v_blk.shape[3]
     if scale is None:
@@ -384,6 +454,18 @@ def block_attn_bwd_step(q: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, 
     for t, name in ((dq_acc, "dq_acc"), (dk_acc, "dk_acc"), (dv_acc, "dv_acc"), (lse, "lse"), (delta, "delta")):
         if t.dtype != torch.float32:
             raise RingAttnError(1, f"{name} must be fp32")
+    _expect(k_blk, (B, Hkv, Sk, Dqk), "k_blk")
+    _expect(v_blk, (B, Hkv, Sk, Dv), "v_blk")
+    _expect(dout, (B, Hq, Sq, Dv), "dout", q.dtype)
+    _expect(lse, (B, Hq, Sq), "lse")
+    _expect(delta, (B, Hq, Sq), "delta")
+    _expect(dq_acc, (B, Hq, Sq, Dqk), "dq_acc")
+    _expect(dk_acc, (B, Hkv, Sk, Dqk), "dk_acc")
+    _expect(dv_acc, (B, Hkv, Sk, Dv), "dv_acc")
+    if k_blk.dtype != q.dtype or v_blk.dtype != q.dtype:
+        raise RingAttnError(1, "q, k_blk, v_blk must share one dtype")
+    _same_device(q, (dout, "dout"), (lse, "lse"), (delta, "delta"), (k_blk, "k_blk"), (v_blk, "v_blk"),
+                 (dq_acc, "dq_acc"), (dk_acc, "dk_acc"), (dv_acc, "dv_acc"))
     _check(lib.ra_block_attn_bwd_step(_dtype_code(q), _dev(q, "q"), _dev(dout, "dout"), _dev(lse, "lse"),
                                       _dev(delta, "delta"), int(q_pos0), Sq, _dev(k_blk, "k_blk"),
                                       _dev(v_blk, "v_blk"), int(k_pos0), Sk, B, Hq, Hkv, Dqk, Dv, float(scale),

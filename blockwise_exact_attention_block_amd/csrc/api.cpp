@@ -213,7 +213,9 @@ int ra_lse_merge(long long rows, int Dv, const float* o_a, const float* lse_a, c
   if (rows < 0 || Dv <= 0 || Dv % 4) return fail(RA_EINVAL, "need rows >= 0 and Dv a positive multiple of 4");
   if (rows == 0) return ok();
   if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return fail(RA_EINVAL, "ra_lse_merge: null pointer");
-  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return fail(RA_EINVAL, "o pointers must be 16-byte aligned");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out) || !aligned16(lse_a) || !aligned16(lse_b) ||
+      !aligned16(lse_out))
+    return fail(RA_EINVAL, "ra_lse_merge: pointers must be 16-byte aligned");
   return hip_status(ra::lse_merge2(rows, Dv, o_a, lse_a, o_b, lse_b, o_out, lse_out, (hipStream_t)stream),
                     "ra_lse_merge launch");
 }
@@ -224,6 +226,8 @@ int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_
   if (rows < 0 || n <= 0 || Dv <= 0 || Dv % 4) return fail(RA_EINVAL, "need rows >= 0, n > 0, Dv a positive multiple of 4");
   if (rows == 0) return ok();
   if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(RA_EINVAL, "ra_lse_merge_n: null pointer");
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o_out) || !aligned16(lse_out))
+    return fail(RA_EINVAL, "ra_lse_merge_n: pointers must be 16-byte aligned");
   return hip_status(ra::lse_merge_n(out_dtype == RA_BF16, rows, n, Dv, o_parts, lse_parts, o_out, lse_out,
                                     (hipStream_t)stream),
                     "ra_lse_merge_n launch");
@@ -248,8 +252,8 @@ int splitkv_launch(int dtype, const void* q, const void* k_cache, const void* v_
     return fail(RA_EINVAL, "k_scale and v_scale must be finite and > 0");
   if (!std::isfinite(scale * k_scale * ra::kLog2e))
     return fail(RA_EINVAL, "scale * k_scale overflows");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part))
-    return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) || !aligned16(lse_part))
+    return fail(RA_EINVAL, "%s: pointers must be 16-byte aligned", who);
   if (dtype != RA_BF16 || Dqk != Dv || (Dqk != 64 && Dqk != 128) || Hq / Hkv > 16)
     return fail(RA_EUNSUPPORTED, "split-KV decode supports bf16 with Dqk == Dv in {64, 128} and Hq/Hkv <= 16");
   if (int r = check_slab(L, Dqk, kv8 ? 1 : 2, "k/v cache")) return r;
@@ -286,7 +290,7 @@ int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void*
                       int L, int Dqk, int Dv, int n_splits, float scale, float* o_part, float* lse_part, void* o,
                       float* lse, void* stream) {
   if (!o || !lse) return fail(RA_EINVAL, "ra_splitkv_decode: null pointer");
-  if (!aligned16(o)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (!aligned16(o) || !aligned16(lse)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
   if (int r = splitkv_launch(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part,
                              lse_part, (hipStream_t)stream, "ra_splitkv_decode"))
     return r;
@@ -306,7 +310,7 @@ int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cach
                           int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                           float* o_part, float* lse_part, void* o, float* lse, void* stream) {
   if (!o || !lse) return fail(RA_EINVAL, "ra_splitkv_decode_fp8: null pointer");
-  if (!aligned16(o)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (!aligned16(o) || !aligned16(lse)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
   if (int r = splitkv_launch(RA_BF16, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part,
                              lse_part, (hipStream_t)stream, "ra_splitkv_decode_fp8", 1, k_scale, v_scale))
     return r;
@@ -320,7 +324,8 @@ int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long
   if (!o || !dout || !delta) return fail(RA_EINVAL, "ra_attn_bwd_preprocess: null pointer");
   if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ra_attn_bwd_preprocess: bf16 only");
   if (rows < 0 || Dv <= 0 || Dv % 8 != 0) return fail(RA_EINVAL, "need rows >= 0 and Dv a positive multiple of 8");
-  if (!aligned16(o) || !aligned16(dout)) return fail(RA_EINVAL, "pointers must be 16-byte aligned");
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta))
+    return fail(RA_EINVAL, "ra_attn_bwd_preprocess: pointers must be 16-byte aligned");
   return hip_status(ra::bwd_delta((const __bf16*)o, (const __bf16*)dout, delta, rows, Dv, (hipStream_t)stream),
                     "ra_attn_bwd_preprocess launch");
 }
@@ -337,7 +342,7 @@ int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const flo
   if (Sq <= 0 || Sk <= 0) return fail(RA_EINVAL, "Sq and Sk must be positive");
   if (q_pos0 < 0 || k_pos0 < 0) return fail(RA_EINVAL, "positions must be >= 0");
   if (!aligned16(q) || !aligned16(dout) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(dq_acc) ||
-      !aligned16(dk_acc) || !aligned16(dv_acc))
+      !aligned16(dk_acc) || !aligned16(dv_acc) || !aligned16(lse) || !aligned16(delta))
     return fail(RA_EINVAL, "pointers must be 16-byte aligned");
   if (int r = check_slab(Sq, Dqk > Dv ? Dqk : Dv, 2, "q/dout")) return r;
   if (int r = check_slab(Sk, Dqk > Dv ? Dqk : Dv, 2, "k/v")) return r;

@@ -72,7 +72,10 @@ const char* ra_last_error(void);
  * Returns P, or -RA_EINVAL on bad arguments. */
 int ra_ring_schedule(int P, int i, int causal, int* kv_block, int* kind);
 
-/* Ring prefill for nq consecutive query partitions, all in one launch.
+/* Ring prefill for nq consecutive query partitions, all in one launch ([RING]
+ * §"KV 在 Ring 中如何流动": every device keeps its query block while the KV blocks
+ * travel round the ring, so partition i meets block (i - s) mod P at step s, and
+ * under a causal mask blocks holding only future tokens contribute nothing).
  * The sequence has P * Sp tokens cut into P contiguous partitions of Sp tokens.
  *   q   device [B, Hq,  nq*Sp, Dqk]  queries of partitions q_part0 .. q_part0+nq-1
  *   k   device [B, Hkv, P*Sp,  Dqk]  all P KV blocks (block j = tokens j*Sp ..)
@@ -125,7 +128,10 @@ int ra_block_attn_step(int dtype, const void* q, long long q_pos0, int Sq,
                        int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal,
                        float* o_acc, float* lse_acc, void* stream);
 
-/* Two-way merge of normalised partial results over disjoint key sets, per row:
+/* Two-way merge of normalised partial results over disjoint key sets, per row
+ * ([IMPL] §"Ring Attention实现代码与通信重叠": the new lse of the union and the two
+ * weights that rescale the old output and the block output; [RING]
+ * §"最容易被忽略的细节": per-block softmax results cannot simply be added):
  * L = log(e^{La} + e^{Lb}); O = e^{La-L} O_a + e^{Lb-L} O_b. A side with -inf
  * LSE contributes nothing; two empty sides give O = 0, L = -inf.
  *   o_a, o_b, o_out  device [rows, Dv] fp32;  lse_a, lse_b, lse_out device [rows] fp32.
@@ -140,7 +146,8 @@ int ra_lse_merge(long long rows, int Dv, const float* o_a, const float* lse_a,
  *   lse_parts device [rows, n] fp32
  *   o_out     device [rows, Dv] in out_dtype (RA_F32 or RA_BF16)
  *   lse_out   device [rows] fp32
- * Errors: RA_EINVAL for null pointers, rows < 0, n <= 0, Dv <= 0, Dv % 4 != 0. */
+ * Errors: RA_EINVAL for null pointers, rows < 0, n <= 0, Dv <= 0, Dv % 4 != 0,
+ * pointers not 16-byte aligned. rows == 0 is a no-op. */
 int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_parts,
                    const float* lse_parts, void* o_out, float* lse_out, void* stream);
 
@@ -159,7 +166,8 @@ int ra_lse_merge_n(int out_dtype, long long rows, int n, int Dv, const float* o_
  * Supported: RA_BF16 with Dqk == Dv in {64, 128} and Hq / Hkv <= 16 (the query
  * heads of one KV head share one matrix-core tile); anything else returns
  * RA_EUNSUPPORTED. Errors: RA_EINVAL for null pointers, non-positive sizes,
- * Hq % Hkv != 0, L % n_splits != 0, misaligned pointers. */
+ * Hq % Hkv != 0, L % n_splits != 0, pointers (the partials and lse included) not
+ * 16-byte aligned. */
 int ra_splitkv_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                       int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                       float* o_part, float* lse_part, void* o, float* lse, void* stream);
@@ -202,8 +210,9 @@ int ra_splitkv_partial_fp8(const void* q, const void* k_cache, const void* v_cac
  *
  * delta[r] = sum_d dout[r, d] * o[r, d] in fp32, for `rows` rows of Dv values
  * (o: the forward output, dout: its incoming gradient; bf16, device, [rows, Dv]).
- * Errors: RA_EINVAL for null or misaligned pointers, rows < 0, Dv not a positive
- * multiple of 8; RA_EUNSUPPORTED for a dtype other than RA_BF16. */
+ * Errors: RA_EINVAL for null pointers or pointers (delta included) not 16-byte
+ * aligned, rows < 0, Dv not a positive multiple of 8; RA_EUNSUPPORTED for a dtype
+ * other than RA_BF16. */
 int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,
                            void* stream);
 

@@ -148,3 +148,100 @@ def test_step_merge_decode_validation(ra):
     assert dec(Dqk=192, Dv=128) == 2
     assert dec(Hq=64, Hkv=2) == 2   # group of 32 heads is more than one MFMA tile
     assert dec(k=None) == 1
+
+
+def test_alignment_of_every_pointer(ra):
+    """Every pointer, the LSE-like fp32 vectors included, must be 16-byte aligned."""
+    lib = ra.load_library()
+    bad = FAKE + 4
+    # two-way merge: each of the six pointers in turn
+    for pos in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[pos] = bad
+        assert lib.ra_lse_merge(10, 128, *ptrs, None) == 1, pos
+    # n-way merge
+    for pos in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[pos] = bad
+        assert lib.ra_lse_merge_n(1, 4, 8, 128, *ptrs, None) == 1, pos
+    # decode partials and outputs
+    dec = lambda **kw: lib.ra_splitkv_decode(*dict(
+        dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, B=2, Hq=16, Hkv=2, L=1024, Dqk=128, Dv=128, n=8, scale=0.1,
+             op=FAKE, lp=FAKE, o=FAKE, l=FAKE, st=None), **kw).values())
+    assert dec(lp=bad) == 1
+    assert dec(l=bad) == 1
+    assert dec(op=bad) == 1
+    assert lib.ra_splitkv_partial(1, FAKE, FAKE, FAKE, 2, 16, 2, 1024, 128, 128, 8, 0.1, FAKE, bad, None) == 1
+    assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1.0, 1.0, 2, 16, 2, 1024, 128, 128, 8, 0.1, FAKE, bad,
+                                      None) == 1
+    # backward: delta of the preprocess; lse and delta of the step
+    assert lib.ra_attn_bwd_preprocess(1, FAKE, FAKE, 10, 128, bad, None) == 1
+    bw = lambda **kw: lib.ra_block_attn_bwd_step(*dict(dict(
+        dtype=1, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, q_pos0=0, Sq=64, k=FAKE, v=FAKE, k_pos0=0, Sk=64, B=1,
+        Hq=2, Hkv=2, Dqk=128, Dv=128, scale=0.1, causal=1, dq=FAKE, dk=FAKE, dv=FAKE, stream=None), **kw).values())
+    assert bw(lse=bad) == 1
+    assert bw(delta=bad) == 1
+    assert b"aligned" in lib.ra_last_error()
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _raises_shape(ra, fn, *a, **kw):
+    with pytest.raises(ra.RingAttnError) as e:
+        fn(*a, **kw)
+    msg = str(e.value)
+    assert "shape" in msg or "dimensions" in msg or "dtype" in msg, msg
+    return msg
+
+
+def test_binding_checks_shapes_before_the_abi(ra):
+    """The Python wrappers compare every tensor's shape with q's before any pointer
+    crosses the C ABI (CPU tensors here: a shape error must come first; tensors of
+    the right shapes then fail only because they are not on the device)."""
+    import torch
+    f32 = torch.float32
+    q, k, v = _cpu(1, 4, 64, 128), _cpu(1, 2, 128, 128), _cpu(1, 2, 128, 128)
+    # ring prefill: k / v against q, and user-supplied outputs
+    _raises_shape(ra, ra.ring_attn_fwd, q, _cpu(1, 2, 128, 64), v, P=2, causal=True)
+    _raises_shape(ra, ra.ring_attn_fwd, q, k, _cpu(1, 2, 64, 128), P=2, causal=True)
+    _raises_shape(ra, ra.ring_attn_fwd, q, k, v, P=2, causal=True, out=_cpu(1, 4, 32, 128))
+    _raises_shape(ra, ra.ring_attn_fwd, q, k, v, P=2, causal=True, lse=_cpu(1, 4, 65, dtype=f32))
+    _raises_shape(ra, ra.ring_attn_fwd, q[0], k, v, P=2, causal=True)
+    with pytest.raises(ra.RingAttnError, match="device"):
+        ra.ring_attn_fwd(q, k, v, P=2, causal=True)
+    # block step: k_blk / v_blk against q, state shapes
+    o_acc, l_acc = _cpu(1, 4, 64, 128, dtype=f32), _cpu(1, 4, 64, dtype=f32)
+    _raises_shape(ra, ra.block_attn_step, q, _cpu(1, 2, 100, 64), v, o_acc, l_acc, q_pos0=0, k_pos0=0, causal=True)
+    _raises_shape(ra, ra.block_attn_step, q, k, v, _cpu(1, 4, 63, 128, dtype=f32), l_acc, q_pos0=0, k_pos0=0,
+                  causal=True)
+    # merges
+    oa, la = _cpu(8, 128, dtype=f32), _cpu(8, dtype=f32)
+    _raises_shape(ra, ra.lse_merge, oa, la, oa, la, out=_cpu(4, 128, dtype=f32))
+    _raises_shape(ra, ra.lse_merge, oa, la, oa, la, lse_out=_cpu(7, dtype=f32))
+    _raises_shape(ra, ra.lse_merge_n, _cpu(8, 4, 128, dtype=f32), _cpu(8, 3, dtype=f32))
+    # decode: caches against q, user partial buffers
+    qd, kc, vc = _cpu(2, 16, 128), _cpu(2, 2, 1024, 128), _cpu(2, 2, 1024, 128)
+    _raises_shape(ra, ra.splitkv_decode, qd, _cpu(2, 2, 1024, 64), vc, n_splits=8)
+    _raises_shape(ra, ra.splitkv_decode, qd, kc, _cpu(2, 3, 1024, 128), n_splits=8)
+    _raises_shape(ra, ra.splitkv_partial, qd, kc, vc, n_splits=8, o_part=_cpu(2, 16, 4, 128, dtype=f32))
+    _raises_shape(ra, ra.splitkv_partial, qd, kc, vc, n_splits=8, lse_part=_cpu(2, 16, 4, dtype=f32))
+    _raises_shape(ra, ra.splitkv_partial, qd, kc, vc, n_splits=8, lse_part=_cpu(2, 16, 8))   # bf16, not fp32
+    with pytest.raises(ra.RingAttnError, match="device"):
+        ra.splitkv_partial(qd, kc, vc, n_splits=8)
+    # backward: every accumulator, dout, lse and delta
+    dq, dk, dv = _cpu(1, 4, 64, 128, dtype=f32), _cpu(1, 2, 128, 128, dtype=f32), _cpu(1, 2, 128, 128, dtype=f32)
+    lse, dl, do = _cpu(1, 4, 64, dtype=f32), _cpu(1, 4, 64, dtype=f32), _cpu(1, 4, 64, 128)
+    kw = dict(q_pos0=0, k_pos0=0, causal=True)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, do, lse, dl, k, v, _cpu(1, 4, 64, 64, dtype=f32), dk, dv, **kw)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, do, lse, dl, k, v, dq, _cpu(1, 4, 128, 128, dtype=f32), dv, **kw)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, do, lse, dl, k, v, dq, dk, _cpu(1, 2, 127, 128, dtype=f32), **kw)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, _cpu(1, 4, 64, 64), lse, dl, k, v, dq, dk, dv, **kw)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, do, _cpu(1, 4, 32, dtype=f32), dl, k, v, dq, dk, dv, **kw)
+    _raises_shape(ra, ra.block_attn_bwd_step, q, do, lse, _cpu(1, 4, 65, dtype=f32), k, v, dq, dk, dv, **kw)
+    with pytest.raises(ra.RingAttnError, match="device"):
+        ra.block_attn_bwd_step(q, do, lse, dl, k, v, dq, dk, dv, **kw)
+    _raises_shape(ra, ra.attn_bwd_preprocess, do, do, _cpu(1, 4, 63, dtype=f32))
+
