@@ -337,8 +337,8 @@ int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const flo
   if (!q || !dout || !lse || !delta || !k_blk || !v_blk || !dq_acc || !dk_acc || !dv_acc)
     return fail(RA_EINVAL, "ra_block_attn_bwd_step: null pointer");
   if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
-  if (dtype != RA_BF16 || !((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)))
-    return fail(RA_EUNSUPPORTED, "the backward step supports bf16 with (Dqk, Dv) in {(64,64), (128,128)}");
+  if (dtype != RA_BF16 || !bf16_dims_ok(Dqk, Dv))
+    return fail(RA_EUNSUPPORTED, "the backward step supports bf16 with (Dqk, Dv) in {(64,64), (128,128), (192,128)}");
   if (Sq <= 0 || Sk <= 0) return fail(RA_EINVAL, "Sq and Sk must be positive");
   if (q_pos0 < 0 || k_pos0 < 0) return fail(RA_EINVAL, "positions must be >= 0");
   if (!aligned16(q) || !aligned16(dout) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(dq_acc) ||

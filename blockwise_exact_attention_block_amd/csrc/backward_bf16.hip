@@ -60,16 +60,29 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
 // consecutive rows start on 16 different 4-bank groups (16-byte row reads are free
 // of bank conflicts). K (dQ kernel), Q and dO (dK/dV kernel) are also read
 // transposed; for those the row order below keeps the transposed reads conflict-free.
-template <int DQK, int DV>
+// (D + 8)-element rows start 4 (D = 64, 128) or 36 (D = 192) banks apart, which
+// serves both reads below alike.
+//
+// NW waves of 32 rows (dQ) or keys (dK, dV) per workgroup. At D_qk = 192, D_v = 128
+// a wave's accumulators alone (dK^T and dV^T of its 32 keys: 160 registers) and its
+// K and V rows (80) leave no room at two waves per SIMD, and the dQ kernel's Q and
+// dO rows (80) and dQ^T accumulators (96) do not fit either, so both kernels run
+// four waves there, one per SIMD, each with the whole register file.
+template <int DQK, int DV, int NW>
 struct BCfg {
-  static constexpr int THREADS = 512;               // 8 waves
-  static constexpr int ROWS = 256;                  // query rows (dQ) / keys (dK, dV) per workgroup
-  static constexpr int BK = 128;                    // keys per LDS tile (dQ kernel)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int ROWS = NW * 32;              // query rows (dQ) / keys (dK, dV) per workgroup
+  static constexpr int BK = DQK > 128 ? 64 : 128;   // keys per LDS tile (dQ kernel): two K + V tiles fit
   static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
   static constexpr int KS = DQK + 8, VS = DV + 8, OS = DV + 8;
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
   static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
 };
+// Waves per workgroup of the two kernels.
+template <int DQK, int DV>
+constexpr int dkdv_waves() { return DQK > 128 ? 4 : 8; }
+template <int DQK, int DV>
+constexpr int dq_waves() { return DQK > 128 ? 4 : 8; }
 
 // Row order inside each 16-row block of a tile read both as rows and transposed: the
 // MFMA row (accumulator row) 4a + b reads LDS row 4b + a (an involution). A half
@@ -80,10 +93,10 @@ struct BCfg {
 __device__ __forceinline__ int perm16(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // ---- dQ -------------------------------------------------------------------------------
-template <int DQK, int DV>
-__global__ void __launch_bounds__(512)
+template <int DQK, int DV, int NW>
+__global__ void __launch_bounds__(NW * 64)
 bwd_dq_kernel(BwdArgs a) {
-  using C = BCfg<DQK, DV>;
+  using C = BCfg<DQK, DV, NW>;
   constexpr int BK = C::BK;
   constexpr int KCH = BK * DQK / 8 / C::THREADS, VCH = BK * DV / 8 / C::THREADS;
   static_assert(KCH * C::THREADS * 8 == BK * DQK && VCH * C::THREADS * 8 == BK * DV, "tile split");
@@ -134,19 +147,15 @@ bwd_dq_kernel(BwdArgs a) {
     if (l != kNegInf) lse2 = l * kLog2e;
     dlt = a.delta[(size_t)bh * a.Sq + my_row];
   }
-  // dP^T starts from -delta, so it comes out as dP - delta
-  constexpr bool DMA = DQK == 128 && DV == 128;
-  f32x16 dp_init;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dp_init[i] = -dlt;
+  constexpr bool DMA = (DQK == 128 && DV == 128) || DQK == 192;
   f32x16 dqacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) dqacc[mt] = f32x16{};
 
   // D = 128: tiles go straight from HBM into the padded LDS rows
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  PaddedTileDma<BK, DQK * 2, C::KS * 2, 8> kdma;
-  PaddedTileDma<BK, DV * 2, C::VS * 2, 8> vdma;
+  PaddedTileDma<BK, DQK * 2, C::KS * 2, NW> kdma;
+  PaddedTileDma<BK, DV * 2, C::VS * 2, NW> vdma;
   if constexpr (DMA) {
     kdma.init(wave_u, lane);
     vdma.init(wave_u, lane);
@@ -188,22 +197,24 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < BK / 32; ++kt) {
       const int krow = kt * 32 + perm16(l32);   // the key of accumulator row l32
-      f32x16 st = f32x16{}, dpt = dp_init;
-      // S^T and dP^T as two chains, each step's K and V fragments read while the
-      // previous step's products run
-      static_assert(C::DS == C::DSV, "one step count for both chains");
+      // dP^T starts from -delta, so it comes out as dP - delta
+      f32x16 st = f32x16{}, dpt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dpt[i] = -dlt;
+      // S^T and dP^T as two chains (DS and DSV steps; the longer one runs on
+      // alone), each step's K and V fragments read while the previous step's
+      // products run
+      constexpr int NSTEP = C::DS > C::DSV ? C::DS : C::DSV;
       bf16x8 kc = *(const bf16x8*)&ks[buf][krow * C::KS + 8 * h];
       bf16x8 vc = *(const bf16x8*)&vs[buf][krow * C::VS + 8 * h];
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
+      for (int s = 0; s < NSTEP; ++s) {
         bf16x8 kn = kc, vn = vc;
-        if (s + 1 < C::DS) {
-          kn = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * (s + 1) + 8 * h];
-          vn = *(const bf16x8*)&vs[buf][krow * C::VS + 16 * (s + 1) + 8 * h];
-        }
+        if (s + 1 < C::DS) kn = *(const bf16x8*)&ks[buf][krow * C::KS + 16 * (s + 1) + 8 * h];
+        if (s + 1 < C::DSV) vn = *(const bf16x8*)&vs[buf][krow * C::VS + 16 * (s + 1) + 8 * h];
         __builtin_amdgcn_sched_barrier(0);
-        st = mfma32(kc, qf[s], st);
-        dpt = mfma32(vc, of[s], dpt);
+        if (s < C::DS) st = mfma32(kc, qf[s], st);
+        if (s < C::DSV) dpt = mfma32(vc, of[s], dpt);
         __builtin_amdgcn_sched_barrier(0);
         kc = kn;
         vc = vn;
@@ -309,10 +320,10 @@ bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---- dK, dV ---------------------------------------------------------------------------
-template <int DQK, int DV>
-__global__ void __launch_bounds__(512)
+template <int DQK, int DV, int NW>
+__global__ void __launch_bounds__(NW * 64)
 bwd_dkdv_kernel(BwdArgs a) {
-  using C = BCfg<DQK, DV>;
+  using C = BCfg<DQK, DV, NW>;
   constexpr int BQ = C::BQ;
   constexpr int QS = C::KS, OS = C::OS;   // Q rows like K rows
   __shared__ __attribute__((aligned(16))) __bf16 qsm[2][BQ * QS];
@@ -373,9 +384,11 @@ bwd_dkdv_kernel(BwdArgs a) {
   // re-read the slab's last 16 bytes: finite values whose P is 0); the rows' LSE and
   // delta go through a register of threads 0..127
   float rowv = 0.f;   // threads 0..63: -LSE * log2(e) of a row; 64..127: -delta
-  static_assert(DQK == DV && QS == OS, "Q and dO tiles share one load layout");
-  PaddedTileDma<BQ, DQK * 2, QS * 2, 8> tdma;
-  tdma.init(wave, lane);
+  static_assert(C::THREADS >= 2 * BQ, "threads 0 .. 2 BQ - 1 carry the rows' LSE and delta");
+  PaddedTileDma<BQ, DQK * 2, QS * 2, NW> qdma;
+  PaddedTileDma<BQ, DV * 2, OS * 2, NW> odma;
+  qdma.init(wave, lane);
+  odma.init(wave, lane);
   auto tile_head = [&](int n) { return g * a.group + n / nqt; };
   auto tile_row0 = [&](int n) { return (qt0 + n % nqt) * BQ; };
   auto load_tile = [&](int n, int buf) {
@@ -395,8 +408,8 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     const u32x4 qdesc = raw_desc((const __bf16*)a.q + bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 2));
     const u32x4 odesc = raw_desc((const __bf16*)a.dout + bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 2));
-    tdma.issue(wave, lds_addr(&qsm[buf][0]), (unsigned)(row0 * DQK * 2), (unsigned)(a.Sq * DQK * 2 - 16), qdesc);
-    tdma.issue(wave, lds_addr(&osm[buf][0]), (unsigned)(row0 * DV * 2), (unsigned)(a.Sq * DV * 2 - 16), odesc);
+    qdma.issue(wave, lds_addr(&qsm[buf][0]), (unsigned)(row0 * DQK * 2), (unsigned)(a.Sq * DQK * 2 - 16), qdesc);
+    odma.issue(wave, lds_addr(&osm[buf][0]), (unsigned)(row0 * DV * 2), (unsigned)(a.Sq * DV * 2 - 16), odesc);
   };
   auto store_rows = [&](int buf) {
     // LSE and delta are kept in accumulator-row order (perm16 is its own inverse)
@@ -549,20 +562,25 @@ hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long lon
 
 template <int DQK, int DV>
 static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
-  using C = BCfg<DQK, DV>;
-  // dK, dV first: one workgroup per 256 keys of a (batch, KV head)
+  using CK = BCfg<DQK, DV, dkdv_waves<DQK, DV>()>;
+  using CQ = BCfg<DQK, DV, dq_waves<DQK, DV>()>;
+  // dK, dV first: one workgroup per CK::ROWS keys of a (batch, KV head)
   BwdArgs b = a;
-  b.n_tiles = (a.Sk + C::ROWS - 1) / C::ROWS;
+  b.n_tiles = (a.Sk + CK::ROWS - 1) / CK::ROWS;
   long long grid = 8 * (((long long)a.B * a.Hkv * b.n_tiles + 7) / 8);   // whole rounds of the 8 XCDs
   if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
-  if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, dkdv_waves<DQK, DV>()>), dim3((unsigned)grid),
+                       dim3(CK::THREADS), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dQ: one workgroup per 256 query rows of a (batch, head)
-  b.n_tiles = (a.Sq + C::ROWS - 1) / C::ROWS;
+  // dQ: one workgroup per CQ::ROWS query rows of a (batch, head)
+  b.n_tiles = (a.Sq + CQ::ROWS - 1) / CQ::ROWS;
   grid = 8 * (((long long)a.B * a.Hq * b.n_tiles + 7) / 8);
   if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
-  if (grid > 0) hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, dq_waves<DQK, DV>()>), dim3((unsigned)grid), dim3(CQ::THREADS),
+                       0, st, b);
   return hipGetLastError();
 }
 
@@ -570,6 +588,7 @@ static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
 hipError_t bwd_bf16(const BwdArgs& a, int dqk, int dv, hipStream_t st) {
   if (dqk == 128 && dv == 128) return bwd_launch<128, 128>(a, st);
   if (dqk == 64 && dv == 64) return bwd_launch<64, 64>(a, st);
+  if (dqk == 192 && dv == 128) return bwd_launch<192, 128>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -229,7 +229,7 @@ int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long
  * A ring backward is this step for every (query block, KV block) pair, in any
  * order, with dk_acc / dv_acc travelling with their block. Two launches (dK/dV,
  * then dQ) on the stream. Supported: RA_BF16 with (Dqk, Dv) in {(64,64),
- * (128,128)}. Errors as ra_block_attn_step. The accumulators must not overlap the
+ * (128,128), (192,128)}. Errors as ra_block_attn_step. The accumulators must not overlap the
  * inputs or each other. */
 int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
                            long long q_pos0, int Sq, const void* k_blk, const void* v_blk, long long k_pos0, int Sk,

@@ -125,7 +125,7 @@ def test_step_merge_decode_validation(ra):
     bw = lambda **kw: lib.ra_block_attn_bwd_step(*dict(dict(
         dtype=1, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, q_pos0=0, Sq=64, k=FAKE, v=FAKE, k_pos0=0, Sk=64, B=1,
         Hq=2, Hkv=2, Dqk=128, Dv=128, scale=0.1, causal=1, dq=FAKE, dk=FAKE, dv=FAKE, stream=None), **kw).values())
-    assert bw(Dqk=192, Dv=128) == 2
+    assert bw(Dqk=96, Dv=96) == 2
     assert bw(dtype=0) == 2
     assert bw(Sq=0) == 1
     assert bw(q=None) == 1

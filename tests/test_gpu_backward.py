@@ -46,14 +46,18 @@ def grad_close(got, ref, what, rmax=2e-2, rmean=5e-3):
     return float(err.max())
 
 
-@pytest.mark.parametrize("D", [64, 128])
+DIMS = [(64, 64), (128, 128), (192, 128)]
+
+
+@pytest.mark.parametrize("dims", DIMS)
 @pytest.mark.parametrize("causal,q_pos0,k_pos0", [(False, 0, 0), (True, 0, 0), (True, 300, 0), (True, 100, 180)])
 @pytest.mark.parametrize("Sq,Sk", [(300, 257), (64, 520)])
-def test_bwd_step_against_oracle(ra, D, causal, q_pos0, k_pos0, Sq, Sk):
+def test_bwd_step_against_oracle(ra, dims, causal, q_pos0, k_pos0, Sq, Sk):
     B, Hq, Hkv = 2, 4, 2
-    say(f"block_attn_bwd_step D{D} causal={causal} q_pos0={q_pos0} k_pos0={k_pos0} Sq{Sq} Sk{Sk}")
-    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, D, seed=500 + Sq + Sk + D, dtype="bf16")
-    do = randn_np((B, Hq, Sq, D), 600 + D, "bf16")
+    D, Dv = dims
+    say(f"block_attn_bwd_step D{D}/{Dv} causal={causal} q_pos0={q_pos0} k_pos0={k_pos0} Sq{Sq} Sk{Sk}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=500 + Sq + Sk + D, dtype="bf16")
+    do = randn_np((B, Hq, Sq, Dv), 600 + D, "bf16")
     scale = 1 / math.sqrt(D)
     # full-row statistics: the block is part of a longer key range starting at 0
     kf, vf = (np.concatenate([x, x[:, :, :7]], axis=2) for x in (k, v))   # 7 more keys after the block
@@ -64,7 +68,7 @@ def test_bwd_step_against_oracle(ra, D, causal, q_pos0, k_pos0, Sq, Sk):
                                   k_pos0=k_pos0)
     dq = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=DEV)
     dk = torch.zeros((B, Hkv, Sk, D), dtype=torch.float32, device=DEV)
-    dv = torch.zeros((B, Hkv, Sk, D), dtype=torch.float32, device=DEV)
+    dv = torch.zeros((B, Hkv, Sk, Dv), dtype=torch.float32, device=DEV)
     lse_d = to_dev(np.where(np.isfinite(lse), lse, -np.inf), torch.float32)
     ra.block_attn_bwd_step(to_dev(q), to_dev(do), lse_d, to_dev(delta, torch.float32), to_dev(k), to_dev(v),
                            dq, dk, dv, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
@@ -101,15 +105,16 @@ def test_bwd_preprocess(ra):
     assert np.max(np.abs(np64(delta) - ref)) <= 1e-4 * (1 + np.abs(ref).max())
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dims", DIMS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_whole_backward_after_gpu_forward(ra, D, causal):
+def test_whole_backward_after_gpu_forward(ra, dims, causal):
     """ring_attn_fwd on the GPU, then attn_bwd: the exact gradients of the exact
     attention of the same bf16 inputs, GQA 4:1, ragged length."""
     B, Hq, Hkv, S = 1, 8, 2, 777
-    say(f"attn_bwd whole D{D} causal={causal}")
-    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=700 + D, dtype="bf16")
-    do = randn_np((B, Hq, S, D), 710 + D, "bf16")
+    D, Dv = dims
+    say(f"attn_bwd whole D{D}/{Dv} causal={causal}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, Dv, seed=700 + D, dtype="bf16")
+    do = randn_np((B, Hq, S, Dv), 710 + D, "bf16")
     dq_, dk_, dv_ = to_dev(q), to_dev(k), to_dev(v)
     o, lse = ra.ring_attn_fwd(dq_, dk_, dv_, P=1, causal=causal)
     gq, gk, gv = ra.attn_bwd(dq_, dk_, dv_, o, lse, to_dev(do), causal=causal)
@@ -120,15 +125,17 @@ def test_whole_backward_after_gpu_forward(ra, D, causal):
     grad_close(gv, rv, "dv")
 
 
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ring_backward_protocol_equals_whole(ra, causal):
+def test_ring_backward_protocol_equals_whole(ra, dims, causal):
     """Ring backward on one GPU: for every query partition i and ring step s, the
     step over (partition i, block (i - s) mod P) accumulates into dq_i and into the
     block's travelling dk_j / dv_j. The sums equal the whole-sequence backward."""
-    B, Hq, Hkv, Sp, P, D = 1, 4, 2, 160, 4, 128
+    B, Hq, Hkv, Sp, P = 1, 4, 2, 160, 4
+    D, Dv = dims
     S = Sp * P
-    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=801, dtype="bf16")
-    do = randn_np((B, Hq, S, D), 802, "bf16")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, Dv, seed=801, dtype="bf16")
+    do = randn_np((B, Hq, S, Dv), 802, "bf16")
     dq_, dk_, dv_, ddo = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
     o, lse = ra.ring_attn_fwd(dq_, dk_, dv_, P=P, causal=causal)
     gq, gk, gv = ra.attn_bwd(dq_, dk_, dv_, o, lse, ddo, causal=causal)
@@ -136,7 +143,7 @@ def test_ring_backward_protocol_equals_whole(ra, causal):
     part = lambda t, i: t[:, :, i * Sp:(i + 1) * Sp].contiguous()
     dq_parts = [torch.zeros((B, Hq, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
     dk_blk = [torch.zeros((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
-    dv_blk = [torch.zeros((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    dv_blk = [torch.zeros((B, Hkv, Sp, Dv), dtype=torch.float32, device=DEV) for _ in range(P)]
     for i in range(P):
         for j, kind in ra.ring_schedule(P, i, causal):
             if kind == "skip":
