@@ -2,24 +2,33 @@
 """One-GPU benchmark of the ring-ordered blockwise exact attention hot path (MI355X).
 
 Headline (``value``): causal ring prefill throughput in algorithmic TFLOP/s (only
-visible query/key pairs count, 2 (D_qk + D_v) FLOP each) on the 70B-class GQA
-workload: B 1, 64 query heads over 8 KV heads, S = 131072 cut into 8 ring
-partitions of 16384, d 128, bf16 -- every partition's queries visiting the KV
-blocks in ring order, in one launch. A step is one such launch over the whole
-sequence; inputs are resident in HBM before the timed region.
+visible query/key pairs count, 2 (D_qk + D_v) FLOP each) on the largest workload
+that fits one GPU, one GPU's share of an MLA-shaped prefill at a ring of 8: the
+last query partition (65536 tokens, index 7 of 8) of S = 524288, 128 heads,
+D_qk 192, D_v 128, bf16, attending to all 8 KV blocks of 65536 tokens in ring
+order with causal masking. A step is one ring launch over that share; inputs are
+resident in HBM before the timed region.
 
 The same JSON line carries:
+  prefill_other the 70B-class GQA ring (B 1, 64/8 heads, S 131072 in 8 partitions,
+                d 128, bf16), the small bf16 MHA ring (H 8, S 8192 in 4, d 128) and
+                the fp32 non-causal ring (H 1, S 1024 in 4, d 64), each timed with
+                its own roofline;
+  striped, ring_step, backward   on the 70B-class GQA workload;
   decode        split-KV decode (B 16, 64/8 heads, KV length 131072 in 8 splits,
-                bf16) in HBM GB/s of algorithmic bytes;
+                bf16) in HBM GB/s of algorithmic bytes, and the same over an fp8
+                cache;
   roofline      for each dominant kernel: algorithmic work per launch over its
                 average launch time, taken with HIP events on the launch stream
                 during the timed region, against the MI355X peak (bf16 dense MFMA
                 2.5 PFLOP/s; HBM 8 TB/s), and the HBM traffic from rocprofv3
                 counters when they were taken on the current kernel source;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload,
-                timed on this host's cores.
+                timed on this host's cores, with the full workload's oracle time
+                extrapolated at that rate; the other workloads likewise (the two
+                small ones run in full).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3|C2|C4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4|C3|C2]
 """
 from __future__ import annotations
 
@@ -177,22 +186,23 @@ def backward_flops(cfg) -> int:
 
 
 def run_backward(args, ra, torch, stream, cfg, q, k, v):
-    """Whole-sequence backward of the prefill workload: delta preprocess plus one
-    step over all (query partition, KV block) pairs, fp32 gradients."""
-    if cfg.q_part0 != 0 or cfg.n_qparts != cfg.P:
-        return None
-    out, lse = ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale)
+    """Backward of the prefill workload's computed query partitions: delta
+    preprocess plus one step over those queries against all P KV blocks (every
+    visible (query partition, KV block) pair), fp32 gradients. For the whole
+    sequence that is the full backward; for one partition it is one rank's share."""
+    out, lse = ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale, q_part0=cfg.q_part0)
     dout = torch.empty_like(out).normal_(0.0, 1.0, generator=torch.Generator(device=q.device).manual_seed(cfg.seed + 7))
     delta = ra.attn_bwd_preprocess(out, dout)
     dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
     steps, warm = max(2, min(args.steps, 3)), 1
-    log(f"[bench] backward: {warm} warmup + {steps} timed steps")
+    log(f"[bench] {cfg.name} backward: {warm} warmup + {steps} timed steps")
+    q_pos0 = cfg.q_part0 * cfg.Sp
 
     def step():
         ra.attn_bwd_preprocess(out, dout, delta)
-        ra.block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=0, k_pos0=0, causal=cfg.causal,
+        ra.block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=q_pos0, k_pos0=0, causal=cfg.causal,
                                scale=cfg.scale)
 
     wall, ev = timed(step, steps, warm, stream, torch)
@@ -200,8 +210,11 @@ def run_backward(args, ra, torch, stream, cfg, q, k, v):
     log(f"[bench] backward {wall:.3f} ms/step, {flops / (wall * 1e-3) / 1e12:.1f} TFLOP/s (algorithmic)")
     del out, lse, dout, delta, dq, dk, dv
     torch.cuda.empty_cache()
+    whole = cfg.q_part0 == 0 and cfg.n_qparts == cfg.P
     return {
-        "workload": f"{cfg.name} backward (delta + dK/dV + dQ over all pairs, fp32 gradients)",
+        "workload": (f"{cfg.name} backward (delta + dK/dV + dQ over all pairs, fp32 gradients)" if whole else
+                     f"{cfg.name} backward of query partitions {cfg.q_part0}..{cfg.q_part0 + cfg.n_qparts - 1} "
+                     f"against all {cfg.P} KV blocks (delta + dK/dV + dQ, fp32 gradients)"),
         "ms_per_step": round(wall, 4),
         "launch_ms": round(ev, 4),
         "algorithmic_flops": flops,
@@ -259,35 +272,59 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, q, k, v, budget_s: float):
-    """The fp64 oracle, as it stands, on a bounded sample of the prefill workload:
-    query rows of KV group 0 (batch 0) at seeded uniform positions, each against its
-    full causal key range. Rate = algorithmic FLOPs of those rows / oracle time."""
+def oracle_sample_inputs(cfg, q, k, v, n_batches: int = 4096):
+    """Host copies of what the bounded oracle sample reads: K and V of KV head 0
+    (batch 0) and seeded uniform query rows of that head's group, 16 per batch. Taken
+    while the device inputs are resident, so that the GPU memory can be released
+    before the oracle runs."""
     import numpy as np
     import torch
 
-    import oracle
-
     rng = np.random.default_rng(cfg.seed + 99)
     group = cfg.Hq // cfg.Hkv
-    k_np = k[0, 0].float().cpu().numpy()
-    v_np = v[0, 0].float().cpu().numpy()
+    heads = rng.integers(0, group, size=(n_batches, 16))
+    rows = rng.integers(0, cfg.Sq, size=(n_batches, 16))
+    # the first batches only: the oracle stops at its time budget long before 4096
+    nb = min(n_batches, 256)
+    qr = q[0, torch.as_tensor(heads[:nb].ravel()), torch.as_tensor(rows[:nb].ravel())].float().cpu().numpy()
+    # fp64 host copies (bf16 and fp32 values convert exactly), made once
+    return {
+        "k": k[0, 0].float().cpu().numpy().astype(np.float64),
+        "v": v[0, 0].float().cpu().numpy().astype(np.float64),
+        "q_rows": qr.reshape(nb, 16, cfg.Dqk),
+        "rows": rows[:nb],
+        "group": group,
+    }
+
+
+def cpu_baseline(cfg, sample, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample of a prefill workload:
+    query rows of KV group 0 (batch 0) at seeded uniform positions, each against its
+    full causal key range. Rate = algorithmic FLOPs of those rows / oracle time; the
+    full workload's oracle time is extrapolated at that rate."""
+    import numpy as np
+
+    import oracle
+
     q0 = cfg.q_part0 * cfg.Sp
-    rows_done, flops, elapsed, batches = 0, 0, 0.0, 0
-    while elapsed < budget_s and batches < 4096:
-        heads = rng.integers(0, group, size=16)
-        rows = rng.integers(0, cfg.Sq, size=16)
-        qr = q[0, torch.as_tensor(heads), torch.as_tensor(rows)].float().cpu().numpy()
+    rows_done, flops, elapsed = 0, 0, 0.0
+    for b in range(sample["q_rows"].shape[0]):
+        if elapsed >= budget_s:
+            break
+        rows = sample["rows"][b]
         pos = q0 + rows
         t0 = time.perf_counter()
-        oracle.attention_rows(qr, pos, k_np, v_np, scale=cfg.scale, causal=cfg.causal, k_pos0=0)
+        oracle.attention_rows(sample["q_rows"][b], pos, sample["k"], sample["v"], scale=cfg.scale,
+                              causal=cfg.causal, k_pos0=0)
         elapsed += time.perf_counter() - t0
         vis = (pos + 1) if cfg.causal else np.full_like(pos, cfg.S)
         flops += int(2 * (cfg.Dqk + cfg.Dv) * int(vis.sum()))
-        rows_done += 16
-        batches += 1
+        rows_done += len(rows)
+    rate = flops / elapsed
+    total = prefill_flops(cfg)
+    group = sample["group"]
     return {
-        "value": round(flops / elapsed / 1e12, 6),
+        "value": round(rate / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": blas_threads(),
         "kind": "oracle",
@@ -295,6 +332,30 @@ def cpu_baseline(cfg, q, k, v, budget_s: float):
                    f"uniform positions, each against its full causal key range; numpy float64 with the "
                    f"score rows materialised; {elapsed:.1f} s of oracle time"),
         "seconds": round(elapsed, 2),
+        "flops": flops,
+        "extrapolated_full_config_s": round(total / rate, 1),
+        "extrapolated_note": (f"extrapolated, not measured: the workload's {total:.4e} algorithmic FLOP at the "
+                              f"sample's measured rate"),
+    }
+
+
+def cpu_full_run(cfg, q, k, v):
+    """The fp64 oracle over every row of a small prefill workload (its full run):
+    oracle.attention on the whole query block against all keys."""
+    import oracle
+
+    qn, kn, vn = (x.float().cpu().numpy() for x in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, vn, scale=cfg.scale, causal=cfg.causal, q_pos0=cfg.q_part0 * cfg.Sp, k_pos0=0)
+    elapsed = time.perf_counter() - t0
+    flops = prefill_flops(cfg)
+    return {
+        "value": round(flops / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{cfg.name}: the full workload, every query row; numpy float64, score matrix materialised",
+        "seconds": round(elapsed, 3),
         "flops": flops,
     }
 
@@ -363,17 +424,64 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
     }
 
 
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (published, packed)
+
+
+def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
+    """Times `steps` ring prefill launches of a workload (after `warmup` untimed
+    ones) and returns its measurement: wall ms per step, per-launch ms from HIP
+    events on the launch stream, algorithmic rate and its roofline fraction."""
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out = torch.empty((cfg.B, cfg.Hq, cfg.Sq, cfg.Dv), dtype=dt, device=q.device)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Sq), dtype=torch.float32, device=q.device)
+    torch.cuda.synchronize()
+
+    def step():
+        ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale, q_part0=cfg.q_part0,
+                         out=out, lse=lse)
+
+    log(f"[bench] {cfg.name} prefill: {warmup} warmup + {steps} timed steps")
+    wall_ms, ev_ms = timed(step, steps, warmup, stream, torch)
+    flops = prefill_flops(cfg)
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    log(f"[bench] {cfg.name} prefill {wall_ms:.4f} ms/step wall, {ev_ms:.4f} ms/launch events, "
+        f"{value:.1f} TFLOP/s")
+    del out, lse
+    if cfg.dtype == "bf16":
+        roof = {"kernel": f"prefill_bf16_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "mfma",
+                "peak": PEAK_BF16_TFLOPS, "traffic": recorded_traffic("prefill", cfg.name)}
+    else:
+        # fp32 inputs run on the vector ALUs (fp32 FMAs, not packed)
+        roof = {"kernel": f"prefill_f32_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "alu",
+                "peak": PEAK_FP32_TFLOPS, "traffic": None}
+    roof.update({"achieved": round(achieved, 3), "unit": "TFLOP/s", "frac": round(achieved / roof["peak"], 4),
+                 "algorithmic_flops_per_launch": flops, "launch_ms": round(ev_ms, 5)})
+    return {
+        "workload": f"{cfg.name}: {cfg.description}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "steps": steps,
+        "ms_per_step": round(wall_ms, 5),
+        "roofline": roof,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="C3", choices=["C2", "C3", "C4"])
+    ap.add_argument("--workload", default="C4", choices=["C2", "C3", "C4"],
+                    help="headline prefill workload (default: C4, the largest that fits one GPU)")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--small-steps", type=int, default=50, help="timed steps of the small workloads C1 and C2")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (for kernel profiling)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="headline prefill only: no C3/C2/C1 lines, no striped, ring-step or backward runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on the headline")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-striped", action="store_true", help="skip the striped-layout measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode measurement")
@@ -398,9 +506,7 @@ def main():
     dev = torch.device("cuda:0")
     ra.load_library()
     stream = torch.cuda.current_stream(dev)
-    cfg = CONFIGS[args.workload]
 
-    line = {}
     if args.no_prefill:
         args.no_cpu_baseline = True
         dcfg = CONFIGS[args.decode_workload]
@@ -409,31 +515,22 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    cfg = CONFIGS[args.workload]
+    samples = {}      # host copies for the oracle, taken while the inputs are resident
+    small_inputs = {}
+
+    # ---- headline: the ring prefill of the chosen workload ------------------------
     log(f"[bench] generating {cfg.name} inputs ({cfg.description})")
     q, k, v = prefill_inputs_torch(cfg, dev)
-    out = torch.empty((cfg.B, cfg.Hq, cfg.Sq, cfg.Dv), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((cfg.B, cfg.Hq, cfg.Sq), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def step():
-        ra.ring_attn_fwd(q, k, v, P=cfg.P, causal=cfg.causal, scale=cfg.scale, q_part0=cfg.q_part0,
-                         out=out, lse=lse)
-
-    log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
-    wall_ms, ev_ms = timed(step, args.steps, args.warmup, stream, torch)
-    flops = prefill_flops(cfg)
-    value = flops / (wall_ms * 1e-3) / 1e12
-    achieved = flops / (ev_ms * 1e-3) / 1e12
-    log(f"[bench] prefill {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/launch events, {value:.1f} TFLOP/s")
-    traffic = recorded_traffic("prefill", cfg.name)
+    head = prefill_line(args, ra, torch, stream, cfg, q, k, v, args.steps, args.warmup)
     line = {
         "metric": "causal prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM) on 1 MI355X",
-        "value": round(value, 3),
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -447,21 +544,70 @@ def main():
             "heads_q_kv": [cfg.Hq, cfg.Hkv],
             "head_dims_qk_v": [cfg.Dqk, cfg.Dv],
             "causal": cfg.causal,
-            "parallelism": "single GPU; the P ring partitions are query partitions of one launch",
+            "parallelism": "single GPU; the ring's KV blocks are visited in ring order inside one launch",
         },
-        "roofline": {
-            "kernel": f"prefill_bf16_kernel<{cfg.Dqk},{cfg.Dv},ring>",
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": flops,
-            "launch_ms": round(ev_ms, 4),
-        },
+        "roofline": head["roofline"],
     }
-    del out, lse
+    if not args.no_cpu_baseline:
+        samples[cfg.name] = oracle_sample_inputs(cfg, q, k, v)
+    if cfg.name == "C3" and not args.no_secondary:
+        run_c3_extras(args, ra, torch, stream, cfg, q, k, v, line)
+    elif not args.no_backward:
+        line["backward_" + cfg.name] = run_backward(args, ra, torch, stream, cfg, q, k, v)
+    del q, k, v
+    torch.cuda.empty_cache()
+
+    # ---- the other prefill workloads, each with a line of its own -----------------
+    if not args.no_secondary:
+        line["prefill_other"] = {}
+        for name in ("C3", "C2", "C1"):
+            if name == cfg.name:
+                continue
+            c = CONFIGS[name]
+            log(f"[bench] generating {c.name} inputs ({c.description})")
+            q, k, v = prefill_inputs_torch(c, dev)
+            small = name in ("C1", "C2")
+            steps = max(args.small_steps, args.steps) if small else args.steps
+            line["prefill_other"][name] = prefill_line(args, ra, torch, stream, c, q, k, v, steps,
+                                                       max(args.warmup, 2))
+            if not args.no_cpu_baseline:
+                if small:
+                    small_inputs[name] = tuple(x.cpu() for x in (q, k, v))
+                else:
+                    samples[name] = oracle_sample_inputs(c, q, k, v)
+            if name == "C3":
+                run_c3_extras(args, ra, torch, stream, c, q, k, v, line)
+            del q, k, v
+            torch.cuda.empty_cache()
+
+    # ---- decode ----------------------------------------------------------------------
+    if not args.no_decode:
+        line["decode"] = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        if not args.no_fp8:
+            fp8 = run_decode(args, ra, torch, dev, stream, CONFIGS["C5F"], decode_inputs_fp8_torch)
+            fp8["speedup_vs_bf16_cache"] = round(line["decode"]["ms_per_step"] / fp8["ms_per_step"], 3)
+            line["decode_fp8"] = fp8
+
+    # ---- the fp64 oracle on the host, after every GPU measurement -------------------
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget:.0f} s on {cfg.name}")
+        line["cpu_baseline"] = cpu_baseline(cfg, samples.pop(cfg.name), args.cpu_budget)
+        others = {}
+        for name, smp in samples.items():
+            log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget / 2:.0f} s on {name}")
+            others[name] = cpu_baseline(CONFIGS[name], smp, args.cpu_budget / 2)
+        for name, (q, k, v) in small_inputs.items():
+            log(f"[bench] cpu baseline: fp64 oracle over all of {name}")
+            others[name] = cpu_full_run(CONFIGS[name], q, k, v)
+        if others:
+            line["cpu_baseline"]["other_workloads"] = others
+
+    print(json.dumps(line), flush=True)
+
+
+def run_c3_extras(args, ra, torch, stream, cfg, q, k, v, line):
+    """The striped layout, one ring step through the step API and the backward pass,
+    on the 70B-class GQA workload."""
     if not args.no_striped and cfg.causal:
         line["striped"] = run_striped(args, ra, torch, stream, cfg, q, k, v)
     step = run_ring_step(args, ra, torch, stream, cfg, q, k, v)
@@ -471,24 +617,6 @@ def main():
         bwd = run_backward(args, ra, torch, stream, cfg, q, k, v)
         if bwd is not None:
             line["backward"] = bwd
-
-    if not args.no_decode:
-        # the prefill inputs are dropped to make room and regenerated (same seeds) below
-        del q, k, v
-        torch.cuda.empty_cache()
-        line["decode"] = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
-        if not args.no_fp8:
-            fp8 = run_decode(args, ra, torch, dev, stream, CONFIGS["C5F"], decode_inputs_fp8_torch)
-            fp8["speedup_vs_bf16_cache"] = round(line["decode"]["ms_per_step"] / fp8["ms_per_step"], 3)
-            line["decode_fp8"] = fp8
-        if not args.no_cpu_baseline:
-            q, k, v = prefill_inputs_torch(cfg, dev)
-
-    if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_budget)
-
-    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
