@@ -16,6 +16,8 @@ Entry points (same names as the C ABI without the ``ra_`` prefix):
   splitkv_partial  split-KV partial attention per chunk (no reduction)
   splitkv_decode   split-KV (pass-Q) decode: partials per chunk + reduction
   splitkv_partial_fp8 / splitkv_decode_fp8   the same over an fp8 e4m3 KV cache
+  splitkv_decode_noalloc  splitkv_decode with its partials in library-held device
+                   scratch, for callers that cannot allocate
   attn_bwd_preprocess  delta = rowsum(dO o O) for the backward pass
   block_attn_bwd_step  one (query block, KV block) pair's dQ, dK, dV contributions
   attn_bwd         whole-sequence backward (preprocess + one step over all pairs)
@@ -32,13 +34,13 @@ import torch
 __all__ = [
     "RingAttnError", "library_path", "load_library", "abi_version", "ring_schedule",
     "ring_attn_fwd", "block_attn_step", "init_state", "lse_merge", "lse_merge_n",
-    "splitkv_partial", "splitkv_decode", "splitkv_partial_fp8", "splitkv_decode_fp8",
+    "splitkv_partial", "splitkv_decode", "splitkv_partial_fp8", "splitkv_decode_fp8", "splitkv_decode_noalloc",
     "attn_bwd_preprocess", "block_attn_bwd_step", "attn_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libringattn.so"
-_ABI_VERSION = 4
+_ABI_VERSION = 5
 RA_F32, RA_BF16 = 0, 1
 _STATUS = {0: "RA_OK", 1: "RA_EINVAL", 2: "RA_EUNSUPPORTED", 3: "RA_EHIP"}
 _KIND = {0: "skip", 1: "diag", 2: "full"}
@@ -92,6 +94,7 @@ def load_library() -> ctypes.CDLL:
         "ra_splitkv_partial": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp], i),
         "ra_splitkv_decode_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp, vp, vp], i),
         "ra_splitkv_partial_fp8": ([vp, vp, vp, f, f, i, i, i, i, i, i, i, f, vp, vp, vp], i),
+        "ra_splitkv_decode_noalloc": ([i, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp], i),
         "ra_attn_bwd_preprocess": ([i, vp, vp, ll, i, vp, vp], i),
         "ra_block_attn_bwd_step": ([i, vp, vp, vp, vp, ll, i, vp, vp, ll, i, i, i, i, i, i, f, i, vp, vp, vp, vp], i),
     }
@@ -348,6 +351,32 @@ def splitkv_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                                  _dev(o_part, "o_part"), _dev(lse_part, "lse_part"), _dev(o, "o"),
                                  _dev(lse, "lse"), _stream(q)))
     return o_part, lse_part, o, lse
+
+
+def splitkv_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_splits: int,
+                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None):
+    """splitkv_decode whose partials live in the library's per-device scratch (no
+    device allocation inside the call; pass `out` [B,Hq,D] and `lse` [B,Hq] to
+    allocate nothing at all). Calls overlapping on one GPU race on that scratch.
+    Returns (o, lse)."""
+    lib = load_library()
+    B, Hq, Dqk, Hkv, L, Dv = _decode_shapes(q, k_cache, v_cache, n_splits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _expect(out, (B, Hq, Dv), "out", q.dtype)
+    _expect(lse, (B, Hq), "lse", torch.float32)
+    _same_device(q, (out, "out"), (lse, "lse"))
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise RingAttnError(1, "q and the caches must share one dtype")
+    _check(lib.ra_splitkv_decode_noalloc(_dtype_code(q), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                         _dev(v_cache, "v_cache"), B, Hq, Hkv, L, Dqk, Dv, int(n_splits),
+                                         float(scale), _dev(out, "out"), _dev(lse, "lse"), _stream(q)))
+    return out, lse
 
 
 def splitkv_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, n_splits: int,

@@ -22,6 +22,8 @@ hipError_t lse_merge_n(int out_bf16, long long rows, int n, int Dv, const float*
 hipError_t decode_partial_bf16(const DecodeArgs& a, int d, int kv8, hipStream_t st);
 hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long long rows, int Dv, hipStream_t st);
 hipError_t bwd_bf16(const BwdArgs& a, int dqk, int dv, hipStream_t st);
+size_t scratch_bytes();
+hipError_t device_scratch(void** ptr);
 }  // namespace ra
 
 namespace {
@@ -317,6 +319,36 @@ int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cach
   const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
                                        (hipStream_t)stream);
   return hip_status(e, "ra_splitkv_decode_fp8 merge launch");
+}
+
+int ra_splitkv_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache, int B, int Hq,
+                              int Hkv, int L, int Dqk, int Dv, int n_splits, float scale, void* o, float* lse,
+                              void* stream) {
+  const char* who = "ra_splitkv_decode_noalloc";
+  if (!o || !lse) return fail(RA_EINVAL, "%s: null pointer", who);
+  if (!aligned16(o) || !aligned16(lse)) return fail(RA_EINVAL, "%s: pointers must be 16-byte aligned", who);
+  if (B <= 0 || Hq <= 0 || n_splits <= 0 || Dv <= 0) return fail(RA_EINVAL, "%s: sizes must be positive", who);
+  // the partials [B, Hq, n_splits, Dv] fp32, then their LSEs [B, Hq, n_splits] fp32 at
+  // the next 256-byte boundary, must fit the library's per-device scratch
+  const unsigned long long parts = (unsigned long long)B * Hq * n_splits;
+  const unsigned long long o_bytes = (parts * Dv * 4 + 255) / 256 * 256;
+  const unsigned long long need = o_bytes + parts * 4;
+  if (need > ra::scratch_bytes())
+    return fail(RA_EINVAL, "%s: the partials need %llu bytes of scratch, more than its %zu bytes "
+                "(B * Hq * n_splits * (Dv + 1) * 4 must stay within it)", who, need, ra::scratch_bytes());
+  // every other argument is validated by splitkv_launch before anything is enqueued;
+  // check them here first too, so that a bad call never looks the scratch up
+  if (!q || !k_cache || !v_cache) return fail(RA_EINVAL, "%s: null pointer", who);
+  void* base = nullptr;
+  if (const hipError_t e = ra::device_scratch(&base); e != hipSuccess) return hip_status(e, who);
+  float* o_part = (float*)base;
+  float* lse_part = (float*)((char*)base + o_bytes);
+  if (int r = splitkv_launch(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, Dqk, Dv, n_splits, scale, o_part,
+                             lse_part, (hipStream_t)stream, who))
+    return r;
+  const hipError_t e = ra::lse_merge_n(1, (long long)B * Hq, n_splits, Dv, o_part, lse_part, o, lse,
+                                       (hipStream_t)stream);
+  return hip_status(e, "ra_splitkv_decode_noalloc merge launch");
 }
 
 int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,

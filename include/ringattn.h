@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 4
+#define RA_ABI_VERSION 5
 
 typedef enum {
   RA_OK = 0,
@@ -201,6 +201,26 @@ int ra_splitkv_decode_fp8(const void* q, const void* k_cache, const void* v_cach
 int ra_splitkv_partial_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
                            int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
                            float* o_part, float* lse_part, void* stream);
+
+/* ra_splitkv_decode for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc):
+ * the same partials and reduction, with the partials kept in a scratch array that
+ * the library holds on each GPU (16 MiB per device, held until the process ends)
+ * instead of caller buffers. Allocates nothing; the caller passes inputs and
+ * outputs only.
+ *   q, k_cache, v_cache, o, lse: as ra_splitkv_decode; supported shapes as there.
+ * The partials [B, Hq, n_splits, Dv] fp32 and their LSEs must fit the scratch:
+ * B * Hq * n_splits * (Dv + 1) * 4 bytes (plus alignment) <= 16 MiB, else RA_EINVAL
+ * with the sizes in the message. The first call on a device looks the scratch up
+ * with that device current: call it with the stream's device current. Every call
+ * on one GPU shares that GPU's scratch, so calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results; calls ordered on one
+ * stream are safe. Each call overwrites the partials completely, so nothing of an
+ * earlier call leaks into a later one. Errors as ra_splitkv_decode, and RA_EHIP if
+ * the scratch lookup fails. */
+int ra_splitkv_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                              int B, int Hq, int Hkv, int L, int Dqk, int Dv, int n_splits, float scale,
+                              void* o, float* lse, void* stream);
 
 /* Backward pass. The pages run ring attention on training samples and name the
  * backward pass's data dependencies among what a ring must get right ([RING]

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(ra):
 
 
 def test_abi_version(ra):
-    assert ra.abi_version() == 4
+    assert ra.abi_version() == 5
 
 
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 13])
@@ -245,3 +245,18 @@ def test_binding_checks_shapes_before_the_abi(ra):
         ra.block_attn_bwd_step(q, do, lse, dl, k, v, dq, dk, dv, **kw)
     _raises_shape(ra, ra.attn_bwd_preprocess, do, do, _cpu(1, 4, 63, dtype=f32))
 
+
+def test_noalloc_decode_validation(ra):
+    """The no-allocation decode rejects partials beyond its 16 MiB scratch, and bad
+    arguments, before it looks the scratch up or launches anything."""
+    lib = ra.load_library()
+    call = lambda **kw: lib.ra_splitkv_decode_noalloc(*dict(
+        dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, B=16, Hq=64, Hkv=8, L=131072, Dqk=128, Dv=128, n=8, scale=0.1,
+             o=FAKE, l=FAKE, st=None), **kw).values())
+    assert call(B=64, n=64) == 1                  # 64*64*64*129*4 bytes of partials > 16 MiB
+    assert b"scratch" in lib.ra_last_error()
+    assert call(B=16, Hq=64, n=64) == 1           # 33.8 MB
+    assert call(o=None) == 1
+    assert call(l=FAKE + 4) == 1
+    assert call(q=None) == 1
+    assert call(B=0) == 1
