@@ -84,14 +84,22 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 // 16 bytes per lane from a raw buffer straight into LDS (buffer_load ... lds): lane
 // i's bytes land at lds_base + 16 * i, whatever its global offset; lds_base is
-// wave-uniform and goes through M0, which the asm declares clobbered so that the
-// compiler keeps none of its own values there across it. It is issued from asm so
-// that the compiler does not hold its own LDS reads of other buffers behind it. The
-// data is visible only after wait_vmem() on the issuing wave and a barrier.
+// wave-uniform and goes through M0, which the asm declares clobbered. It is issued
+// from asm so that the compiler does not hold its own LDS reads of other buffers
+// behind it. The data is visible only after wait_vmem() on the issuing wave and a
+// barrier.
+// M0 is a reserved register for the compiler, which warns that it does not save
+// such a register around an asm statement. It need not: what the clobber does is
+// make the compiler write M0 again before its own next use of it (with the clobber
+// it reloads M0 after the asm; without it, it would reuse the value it set
+// earlier), so no value of the compiler's lives in M0 across this asm.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(unsigned lds_base, unsigned byte_off, u32x4 desc) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(byte_off), "s"(desc) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 // Direct HBM -> LDS loads of a tile of ROWS consecutive global rows of ROW_BYTES bytes
 // into LDS rows of LDS_STRIDE bytes (the row plus padding). The LDS tile is cut into
 // 1 KB pieces, and piece j is written by one wave-wide lds_load16, whose lane i fills
