@@ -8,31 +8,54 @@
 // this path exists for fp32 inputs, whose tolerance no bf16 matrix-core product
 // could meet.
 //
-// Workgroup: 256 threads, 32 query rows, key tiles of 32 staged in LDS.
-//   score phase: thread t owns query t/8 and keys (t%8) + 8u, u = 0..3
-//   PV phase:    thread t owns query t/8 and output columns (t%8) + 8e
-// The eight threads of a query exchange the row max / sum with xor-shuffles.
+// Workgroup: 256 threads (4 waves), 16 query rows, key tiles of 64. Small fp32
+// problems have few query rows, so a workgroup takes few of them (more
+// workgroups) and walks the keys in tiles of 64. Thread t works for query row
+// t / 16 (the 16 threads of a row sit in one wave):
+//   score phase: keys (t % 16) + 16 u, u = 0..3; each step reads four
+//                consecutive d of the row's query (one broadcast 16-byte LDS read)
+//                and of each of its keys (16-byte reads of padded K rows,
+//                conflict-free), then 16 FMAs;
+//   PV phase:    output columns 4 (t % 16) .. + 3 (and + 64 when D_v = 128); each
+//                step reads four probabilities of the row (broadcast) and, per
+//                key, four consecutive V values (16-byte reads), then 16 (32)
+//                FMAs.
+// The row's 16 threads exchange the tile's max and sum with xor-shuffles inside
+// their group of 16 lanes. The next K/V tile is fetched into registers while the
+// current one is computed, and written to the other LDS buffer after it.
 #include "common.hpp"
 
 namespace ra {
 
 enum { F32_RING = 0, F32_STEP = 1 };
 
+template <int DQK, int DV>
+struct F32Cfg {
+  // 64-key tiles (128-key tiles at D = 64 measured 25 % slower on the small
+  // workloads this path serves: more registers, no shorter critical path)
+  static constexpr int BQ = 16, BK = 64, THREADS = 256;
+  static constexpr int KPT = BK / 16;  // keys per thread in the score phase
+  static constexpr int KS = DQK + 4;   // padded K rows: 16 consecutive rows start on 16 distinct 4-bank groups
+  static constexpr int PS = BK + 4;
+  static constexpr int NV = DV / 64;   // float4 output groups per thread
+  static constexpr int KCH = BK * DQK / 4 / THREADS;   // float4 K loads per thread per tile
+  static constexpr int VCH = BK * DV / 4 / THREADS;    // float4 V loads per thread per tile
+  static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
+};
+
 template <int DQK, int DV, int MODE>
 __global__ void __launch_bounds__(256)
 prefill_f32_kernel(PrefillArgs a) {
-  constexpr int BQ = 32, BK = 32;
-  constexpr int QS = DQK + 1;  // padded rows: conflict-free column walks
-  constexpr int KS = DQK + 1;
-  constexpr int PS = BK + 1;
-  __shared__ float qs[BQ * QS];
-  __shared__ float ksm[BK * KS];
-  __shared__ float vsm[BK * DV];
-  __shared__ float ps[BQ * PS];
+  using C = F32Cfg<DQK, DV>;
+  constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV;
+  __shared__ __attribute__((aligned(16))) float qsm[BQ * DQK];
+  __shared__ __attribute__((aligned(16))) float ksm[2][BK * KS];
+  __shared__ __attribute__((aligned(16))) float vsm[2][BK * DV];
+  __shared__ __attribute__((aligned(16))) float psm[BQ * PS];
 
   const int tid = threadIdx.x;
-  const int qi = tid >> 3;   // query row inside the tile
-  const int sub = tid & 7;
+  const int qi = tid >> 4;   // query row inside the tile
+  const int j = tid & 15;
 
   const int tiles_per_head = (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   const int bh = blockIdx.x / tiles_per_head;
@@ -77,35 +100,7 @@ prefill_f32_kernel(PrefillArgs a) {
     if (kmax <= 0) return;
     ntiles = (int)((kmax + BK - 1) / BK);
   }
-
-  // queries of the tile into LDS (zero past the end)
-  for (int e = tid; e < BQ * DQK; e += 256) {
-    const int r = e / DQK, d = e % DQK;
-    const int row = row_base + r;
-    qs[r * QS + d] = row < row_end ? q_head[(size_t)row * DQK + d] : 0.f;
-  }
-
-  const int my_row = row_base + qi;
-  const long long my_pos = pos_base + qi;
-  constexpr int NE = DV / 8;
-  float acc[NE];
-  float m = kNegInf, l = 0.f;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = 0.f;
-  if (MODE == F32_STEP && my_row < row_end) {
-    const size_t r = (size_t)bh * a.q_rows + my_row;
-    const float lin = a.lse_acc[r];
-    if (lin != kNegInf) {
-      m = lin * kLog2e;
-      l = 1.f;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] = a.o_acc[r * DV + sub + 8 * e];
-    }
-  }
-
-  for (int n = 0; n < ntiles; ++n) {
-    int krow0, nvalid;
-    long long kpos0;
+  auto tile_at = [&](int n, int& krow0, long long& kpos0, int& nvalid) {
     if (MODE == F32_RING) {
       ring.tile(n, krow0, kpos0, nvalid);
     } else {
@@ -113,59 +108,146 @@ prefill_f32_kernel(PrefillArgs a) {
       kpos0 = a.k_pos0 + (long long)n * BK;
       nvalid = min(BK, a.Sk - n * BK);
     }
-    __syncthreads();  // previous tile fully consumed (and Q staged on entry)
-    for (int e = tid; e < BK * DQK; e += 256) {
-      const int r = e / DQK, d = e % DQK;
-      ksm[r * KS + d] = r < nvalid ? k_head[(size_t)(krow0 + r) * DQK + d] : 0.f;
-    }
-    for (int e = tid; e < BK * DV; e += 256) {
-      const int r = e / DV, d = e % DV;
-      vsm[r * DV + d] = r < nvalid ? v_head[(size_t)(krow0 + r) * DV + d] : 0.f;
-    }
-    __syncthreads();
+  };
 
-    float s[4];
+  // queries of the tile into LDS (zero past the end)
+  for (int e = tid; e < BQ * DQK / 4; e += C::THREADS) {
+    const int r = e / (DQK / 4), c4 = e % (DQK / 4);
+    const int row = row_base + r;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < row_end) x = *(const float4*)(q_head + (size_t)row * DQK + 4 * c4);
+    *(float4*)&qsm[r * DQK + 4 * c4] = x;
+  }
+
+  // K / V tiles: global -> registers (rows past the tile's valid keys read as zero),
+  // registers -> LDS
+  float4 kr[C::KCH], vr[C::VCH];
+  auto load_tile = [&](int krow0, int nvalid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s[u] = 0.f;
-    for (int d = 0; d < DQK; ++d) {
-      const float qv = qs[qi * QS + d];
+    for (int it = 0; it < C::KCH; ++it) {
+      const int e = it * C::THREADS + tid, r = e / (DQK / 4), c4 = e % (DQK / 4);
+      kr[it] = r < nvalid ? *(const float4*)(k_head + (size_t)(krow0 + r) * DQK + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s[u] = fmaf(qv, ksm[(sub + 8 * u) * KS + d], s[u]);
+    for (int it = 0; it < C::VCH; ++it) {
+      const int e = it * C::THREADS + tid, r = e / (DV / 4), c4 = e % (DV / 4);
+      vr[it] = r < nvalid ? *(const float4*)(v_head + (size_t)(krow0 + r) * DV + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int e = it * C::THREADS + tid, r = e / (DQK / 4), c4 = e % (DQK / 4);
+      *(float4*)&ksm[buf][r * KS + 4 * c4] = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VCH; ++it) {
+      const int e = it * C::THREADS + tid, r = e / (DV / 4), c4 = e % (DV / 4);
+      *(float4*)&vsm[buf][r * DV + 4 * c4] = vr[it];
+    }
+  };
+
+  const int my_row = row_base + qi;
+  const long long my_pos = pos_base + qi;
+  float4 acc[NV];
+  float m = kNegInf, l = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (MODE == F32_STEP && my_row < row_end) {
+    const size_t r = (size_t)bh * a.q_rows + my_row;
+    const float lin = a.lse_acc[r];
+    if (lin != kNegInf) {
+      m = lin * kLog2e;
+      l = 1.f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) acc[e] = *(const float4*)(a.o_acc + r * DV + 64 * e + 4 * j);
+    }
+  }
+
+  int krow0, nvalid;
+  long long kpos0;
+  tile_at(0, krow0, kpos0, nvalid);
+  load_tile(krow0, nvalid);
+  store_tile(0);
+  __syncthreads();   // Q and the first K/V tile are in LDS
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    const long long kpos_cur = kpos0;
+    const int nvalid_cur = nvalid;
+    if (n + 1 < ntiles) {
+      tile_at(n + 1, krow0, kpos0, nvalid);
+      load_tile(krow0, nvalid);   // lands while this tile is computed
+    }
+
+    // scores of keys j + 16 u
+    constexpr int KPT = C::KPT;
+    float s[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) s[u] = 0.f;
+#pragma unroll 8
+    for (int d4 = 0; d4 < DQK / 4; ++d4) {
+      const float4 qv = *(const float4*)&qsm[qi * DQK + 4 * d4];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const float4 kv = *(const float4*)&ksm[buf][(j + 16 * u) * KS + 4 * d4];
+        s[u] = fmaf(qv.x, kv.x, s[u]);
+        s[u] = fmaf(qv.y, kv.y, s[u]);
+        s[u] = fmaf(qv.z, kv.z, s[u]);
+        s[u] = fmaf(qv.w, kv.w, s[u]);
+      }
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = sub + 8 * u;
-      const bool ok = key < nvalid && (!a.causal || kpos0 + key <= my_pos);
+    for (int u = 0; u < KPT; ++u) {
+      const int key = j + 16 * u;
+      const bool ok = key < nvalid_cur && (!a.causal || kpos_cur + key <= my_pos);
       s[u] = ok ? s[u] : kNegInf;
       mx = fmaxf(mx, s[u]);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 1));
-    mx = fmaxf(mx, shfl_xor_f(mx, 2));
-    mx = fmaxf(mx, shfl_xor_f(mx, 4));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
     const float mnew = fmaxf(m, mx * a.scale_log2);
     const float muse = mnew == kNegInf ? 0.f : mnew;
     const float alpha = exp2_hw(m - muse);
     m = mnew;
     float rs = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KPT; ++u) {
       const float p = exp2_hw(fmaf(s[u], a.scale_log2, -muse));
-      ps[qi * PS + sub + 8 * u] = p;
+      psm[qi * PS + j + 16 * u] = p;
       rs += p;
     }
-    rs += shfl_xor_f(rs, 1);
-    rs += shfl_xor_f(rs, 2);
-    rs += shfl_xor_f(rs, 4);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) rs += shfl_xor_f(rs, o);
     l = l * alpha + rs;
-    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] *= alpha;
-    for (int k = 0; k < BK; ++k) {
-      const float p = ps[qi * PS + k];
-#pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] = fmaf(p, vsm[k * DV + sub + 8 * e], acc[e]);
+    for (int e = 0; e < NV; ++e) {
+      acc[e].x *= alpha;
+      acc[e].y *= alpha;
+      acc[e].z *= alpha;
+      acc[e].w *= alpha;
     }
+    __syncthreads();   // the row's probabilities are in LDS
+
+    // O += P V over the tile's keys, four keys per step
+#pragma unroll 4
+    for (int c4 = 0; c4 < BK / 4; ++c4) {
+      const float4 pv = *(const float4*)&psm[qi * PS + 4 * c4];
+      const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const float4 vv = *(const float4*)&vsm[buf][(4 * c4 + e4) * DV + 64 * e + 4 * j];
+          acc[e].x = fmaf(pk[e4], vv.x, acc[e].x);
+          acc[e].y = fmaf(pk[e4], vv.y, acc[e].y);
+          acc[e].z = fmaf(pk[e4], vv.z, acc[e].z);
+          acc[e].w = fmaf(pk[e4], vv.w, acc[e].w);
+        }
+      }
+    }
+    if (n + 1 < ntiles) store_tile(buf ^ 1);   // its last readers passed the previous barrier
+    __syncthreads();   // this tile fully consumed, the next one in LDS
   }
 
   if (my_row < row_end) {
@@ -174,8 +256,9 @@ prefill_f32_kernel(PrefillArgs a) {
     const float lse = l > 0.f ? (m + log2_hw(l)) * kLn2 : kNegInf;
     float* out = MODE == F32_RING ? (float*)a.o : a.o_acc;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) out[r * DV + sub + 8 * e] = acc[e] * inv;
-    if (sub == 0) {
+    for (int e = 0; e < NV; ++e)
+      *(float4*)(out + r * DV + 64 * e + 4 * j) = make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
+    if (j == 0) {
       if (MODE == F32_RING)
         a.lse[r] = lse;
       else
@@ -186,12 +269,13 @@ prefill_f32_kernel(PrefillArgs a) {
 
 template <int DQK, int DV, int MODE>
 static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
+  using C = F32Cfg<DQK, DV>;
   const int rows_per_part = MODE == F32_RING ? a.Sp : a.q_rows;
-  a.n_qtiles = (rows_per_part + 31) / 32;
+  a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;
   const long long tiles = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 

@@ -290,3 +290,102 @@ def test_c3_backward_zero_query_closed_form(ra):
         del x, ref, err
     say(f"C3 backward Q=0: dV worst relative max error {worst_max:.3e}, mean {worst_mean:.3e}")
     assert worst_max <= 2e-2 and worst_mean <= 5e-3, (worst_max, worst_mean)
+
+
+@pytest.mark.timeout(1200)
+def test_c4_backward_sampled_rows_keys_and_closed_form(ra):
+    """Backward of the MLA-shaped share (query partition 7 of 8 of S 524288, 128
+    heads, D_qk 192, D_v 128) in the launch configuration bench.py times: one step
+    of the partition's queries against all 8 KV blocks. References come from the
+    inputs alone:
+      * dQ of sampled rows: exact, with the oracle's row statistics over each row's
+        whole causal key range;
+      * dK / dV of keys in the last 256 positions of two heads: every query row that
+        sees them (MHA: one query head per KV head), with its LSE and delta from the
+        oracle's forward;
+      * Q = 0 at every key of every head: each visible probability is 1/(r+1) for the
+        query at position r, so dV at key c is sum over the partition's queries
+        r >= c of dO_r/(r+1) (fp64 on the device with torch), and dK is exactly 0."""
+    cfg = CONFIGS["C4"]
+    q0pos = cfg.q_part0 * cfg.Sp
+    S = cfg.S
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    o, lse = run_prefill(ra, cfg, q, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 7)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    say(f"attn_bwd step {cfg.name}: partition 7 against all KV blocks")
+    delta = ra.attn_bwd_preprocess(o, dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+    ra.block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=q0pos, k_pos0=0, causal=True,
+                           scale=cfg.scale)
+    torch.cuda.synchronize()
+    del o, lse, delta
+    rng = np.random.default_rng(cfg.seed + 11)
+    worst = 0.0
+    for h in (0, cfg.Hq - 1):
+        k_np, v_np = k[0, h].double().cpu().numpy(), v[0, h].double().cpu().numpy()
+        # dQ of sampled rows (local indices), exact
+        rows = np.unique(np.concatenate([rng.integers(0, cfg.Sq, 4), [0, cfg.Sq - 1]]))
+        rt = torch.as_tensor(rows, device=DEV)
+        qr = q[0, h, rt].double().cpu().numpy()
+        dr = dout[0, h, rt].double().cpu().numpy()
+        o_r, l_r = oracle.attention_rows(qr, q0pos + rows, k_np, v_np, scale=cfg.scale, causal=True)
+        ref, _, _ = oracle.block_bwd(qr[None, None], k_np[None, None], v_np[None, None], dr[None, None],
+                                     l_r[None, None], ((dr * o_r).sum(-1))[None, None], scale=cfg.scale,
+                                     causal=True, q_pos=q0pos + rows, k_pos0=0)
+        err = np.abs(dq[0, h, rt].double().cpu().numpy() - ref[0, 0]).max() / np.abs(ref[0, 0]).max()
+        worst = max(worst, err)
+        assert err <= 2e-2, ("dq", h, err)
+        # dK, dV of keys in the last 256 positions: every query row at or after them
+        keys = np.unique(np.concatenate([S - 1 - rng.integers(0, 256, 3), [S - 1, S - 2, S - 128, S - 129, S - 256]]))
+        r0 = int(keys.min()) - q0pos
+        lrows = np.arange(r0, cfg.Sq)
+        qh = q[0, h, r0:].double().cpu().numpy()
+        dh = dout[0, h, r0:].double().cpu().numpy()
+        o_ref, l_ref = oracle.attention_rows(qh, q0pos + lrows, k_np, v_np, scale=cfg.scale, causal=True)
+        _, gk, gv = oracle.block_bwd(qh[None, None], k_np[keys][None, None], v_np[keys][None, None], dh[None, None],
+                                     l_ref[None, None], ((dh * o_ref).sum(-1))[None, None], scale=cfg.scale,
+                                     causal=True, q_pos=q0pos + lrows, k_pos=keys)
+        kt = torch.as_tensor(keys, device=DEV)
+        for got, refg, name in ((dk[0, h, kt], gk[0, 0], "dk"), (dv[0, h, kt], gv[0, 0], "dv")):
+            err = np.abs(got.double().cpu().numpy() - refg).max() / np.abs(refg).max()
+            worst = max(worst, err)
+            assert err <= 2e-2, (name, h, err)
+        del k_np, v_np
+    say(f"C4 backward: worst relative max error {worst:.3e}")
+    del dq, dk, dv, dout
+    torch.cuda.empty_cache()
+
+    # Q = 0 closed form at every key
+    qz = torch.zeros_like(q)
+    del q
+    o, lse = run_prefill(ra, cfg, qz, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 8)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    delta = ra.attn_bwd_preprocess(o, dout)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+    dq = torch.zeros(qz.shape, dtype=torch.float32, device=DEV)
+    say(f"attn_bwd step {cfg.name} with Q = 0")
+    ra.block_attn_bwd_step(qz, dout, lse, delta, k, v, dq, dk, dv, q_pos0=q0pos, k_pos0=0, causal=True,
+                           scale=cfg.scale)
+    torch.cuda.synchronize()
+    del o, lse, delta, dq
+    assert torch.count_nonzero(dk).item() == 0, "dK must be exactly zero when Q = 0"
+    del dk
+    inv = 1.0 / torch.arange(q0pos + 1, S + 1, device=DEV, dtype=torch.float64)
+    worst_max = worst_mean = 0.0
+    for h in range(cfg.Hq):
+        x = dout[0, h].double() * inv[:, None]                       # [Sq, Dv], query r at q0pos + r
+        tail = torch.flip(torch.cumsum(torch.flip(x, (0,)), 0), (0,))  # keys at q0pos + c, c < Sq
+        err_tail = (dv[0, h, q0pos:].double() - tail).abs()
+        err_head = (dv[0, h, :q0pos].double() - tail[0]).abs()        # keys before the partition see every query
+        rmax = max(float(err_tail.max()), float(err_head.max())) / float(tail.abs().max())
+        rmean = (float(err_tail.sum()) + float(err_head.sum())) / (S * cfg.Dv) / \
+            ((float(tail.abs().sum()) + q0pos * float(tail[0].abs().sum())) / (S * cfg.Dv))
+        worst_max, worst_mean = max(worst_max, rmax), max(worst_mean, rmean)
+        del x, tail, err_tail, err_head
+    say(f"C4 backward Q=0: dV worst relative max error {worst_max:.3e}, mean {worst_mean:.3e}")
+    assert worst_max <= 2e-2 and worst_mean <= 5e-3, (worst_max, worst_mean)
