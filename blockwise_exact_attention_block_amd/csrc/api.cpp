@@ -73,8 +73,10 @@ int check_common(int dtype, int B, int Hq, int Hkv, int Dqk, int Dv, float scale
   return RA_OK;
 }
 
+// rows * d * esize <= 2^31 - 1, compared without forming the product (rows can be a
+// product of two ints itself)
 int check_slab(long long rows, int d, int esize, const char* name) {
-  if (rows * (long long)d * esize > kMaxSlabBytes)
+  if (rows > kMaxSlabBytes / ((long long)d * esize))
     return fail(RA_EUNSUPPORTED, "%s: a per-head slab of %lld rows x %d exceeds 2^31 bytes", name, rows, d);
   return RA_OK;
 }
@@ -329,13 +331,18 @@ int ra_splitkv_decode_noalloc(int dtype, const void* q, const void* k_cache, con
   if (!aligned16(o) || !aligned16(lse)) return fail(RA_EINVAL, "%s: pointers must be 16-byte aligned", who);
   if (B <= 0 || Hq <= 0 || n_splits <= 0 || Dv <= 0) return fail(RA_EINVAL, "%s: sizes must be positive", who);
   // the partials [B, Hq, n_splits, Dv] fp32, then their LSEs [B, Hq, n_splits] fp32 at
-  // the next 256-byte boundary, must fit the library's per-device scratch
-  const unsigned long long parts = (unsigned long long)B * Hq * n_splits;
-  const unsigned long long o_bytes = (parts * Dv * 4 + 255) / 256 * 256;
-  const unsigned long long need = o_bytes + parts * 4;
-  if (need > ra::scratch_bytes())
-    return fail(RA_EINVAL, "%s: the partials need %llu bytes of scratch, more than its %zu bytes "
-                "(B * Hq * n_splits * (Dv + 1) * 4 must stay within it)", who, need, ra::scratch_bytes());
+  // the next 256-byte boundary, must fit the library's per-device scratch; each
+  // product is bounded before the next factor joins it, so nothing wraps
+  const unsigned long long cap = ra::scratch_bytes();
+  unsigned long long parts = (unsigned long long)B * (unsigned long long)Hq;   // < 2^62
+  if (parts <= cap) parts *= (unsigned long long)n_splits;                      // < 2^24 * 2^31
+  const unsigned long long need =
+      parts <= cap ? (parts * 4ULL * (unsigned long long)Dv + 255) / 256 * 256 + parts * 4 : ~0ULL;
+  if (need > cap)
+    return fail(RA_EINVAL, "%s: the partials of B %d x Hq %d x n_splits %d (Dv %d) do not fit the %zu bytes "
+                "of scratch (B * Hq * n_splits * (Dv + 1) * 4 plus alignment must stay within it)", who, B, Hq,
+                n_splits, Dv, ra::scratch_bytes());
+  const unsigned long long o_bytes = (parts * 4ULL * (unsigned long long)Dv + 255) / 256 * 256;
   // every other argument is validated by splitkv_launch before anything is enqueued;
   // check them here first too, so that a bad call never looks the scratch up
   if (!q || !k_cache || !v_cache) return fail(RA_EINVAL, "%s: null pointer", who);

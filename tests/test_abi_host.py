@@ -103,6 +103,7 @@ def check_ring_validation(lib, call):
     assert call(Dqk=96, Dv=96) == 2             # no kernel for that head dim
     assert call(dtype=0, Dqk=192, Dv=128) == 2  # fp32 path has no 192
     assert call(Sp=1 << 24, P=8) == 2           # per-head slab past 2^31 bytes
+    assert call(Sp=1 << 30, P=1 << 30, nq=1) == 2   # rows * d * 2 would wrap 64 bits
     assert b"" != lib.ra_last_error()
 
 
@@ -256,6 +257,9 @@ def test_noalloc_decode_validation(ra):
     assert call(B=64, n=64) == 1                  # 64*64*64*129*4 bytes of partials > 16 MiB
     assert b"scratch" in lib.ra_last_error()
     assert call(B=16, Hq=64, n=64) == 1           # 33.8 MB
+    # products of the sizes that wrap 64 bits must not slip under the limit
+    assert call(B=1 << 30, Hq=1 << 30, Hkv=1 << 30, n=1 << 30, L=1 << 30) == 1
+    assert call(B=1 << 21, Hq=1 << 21, Hkv=1 << 21, n=1 << 21, L=1 << 21) == 1
     assert call(o=None) == 1
     assert call(l=FAKE + 4) == 1
     assert call(q=None) == 1
