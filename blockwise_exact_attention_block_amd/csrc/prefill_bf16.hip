@@ -49,14 +49,16 @@ enum { MODE_RING = 0, MODE_STEP = 1 };
 // shift is moved: P stays below 2^8 between moves.
 constexpr float kLazyShift = 8.0f;
 
-template <int DQK, int DV, int NQ, int NW>
+template <int DQK, int DV, int NQ, int NW, int SPLIT>
 struct PCfg {
-  // 128 keys per tile, all through one online-softmax update. Two double-buffered
-  // tiles take 128 KB of LDS at D = 128, exactly 160 KB at D_qk = 192 / D_v = 128
-  // (unpadded rows) and 84 KB at D = 64 (padded rows).
-  static constexpr int BK = 128;
+  // SPLIT = 1: 128 keys per tile, all through one online-softmax update. Two
+  // double-buffered tiles take 128 KB of LDS at D = 128, exactly 160 KB at
+  // D_qk = 192 / D_v = 128 (unpadded rows) and 84 KB at D = 64 (padded rows).
+  // SPLIT = 2: two key streams of 64-key tiles, each double-buffered (the same LDS).
+  static constexpr int BK = SPLIT == 1 ? 128 : 64;
   static constexpr int THREADS = NW * 64;
-  static constexpr int BQ = NW * NQ * 32;             // query rows per workgroup
+  static constexpr int NWS = NW / SPLIT;              // waves per key stream
+  static constexpr int BQ = NWS * NQ * 32;            // query rows per workgroup
   // D = 128 (DMA) and D_qk = 192 (DMAW): unpadded rows with an XOR swizzle of
   // 16-byte chunks. D = 64: rows padded so that consecutive K rows (16-byte reads)
   // and V rows (transposed 8-byte reads) start on different banks. Either way each
@@ -67,7 +69,7 @@ struct PCfg {
   static constexpr int VS = (DMA || DMAW) ? DV : DV + 32;
   static constexpr int K_TILE = padded_tile_bytes(BK, KS * 2) / 2;   // elements, whole KB
   static constexpr int V_TILE = padded_tile_bytes(BK, VS * 2) / 2;
-  static_assert(2 * (K_TILE + V_TILE) * 2 <= 160 * 1024, "two tiles of K and V must fit in LDS");
+  static_assert(2 * SPLIT * (K_TILE + V_TILE) * 2 <= 160 * 1024, "two tiles of K and V per stream must fit in LDS");
   static constexpr int DS = DQK / 16;                 // MFMA k-steps along D_qk
   static constexpr int MT = DV / 32;                  // 32-row output tiles along D_v
 };
@@ -78,17 +80,20 @@ struct TileRef {
   int nvalid;      // keys of the tile that exist (<= BK)
 };
 
-template <int DQK, int DV, int NQ, int NW, int MODE>
+template <int DQK, int DV, int NQ, int NW, int MODE, int SPLIT>
 __global__ void __launch_bounds__(NW * 64)
 prefill_bf16_kernel(PrefillArgs a) {
-  using C = PCfg<DQK, DV, NQ, NW>;
-  constexpr int BK = C::BK;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][C::K_TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[2][C::V_TILE];
+  using C = PCfg<DQK, DV, NQ, NW, SPLIT>;
+  constexpr int BK = C::BK, NWS = C::NWS;
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2 * SPLIT][C::K_TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2 * SPLIT][C::V_TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // SPLIT = 2: waves 0 .. NWS-1 are key stream 0, the rest stream 1; both streams
+  // cover the same query rows (row group = wave index within the stream)
+  const int stream = SPLIT == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / NWS;   // wave-uniform
+  const int wave = (tid >> 6) - stream * NWS;
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
@@ -183,8 +188,8 @@ prefill_bf16_kernel(PrefillArgs a) {
   };
   constexpr int ROWB = DQK * 2, ROWBV = DV * 2;
   constexpr bool SWZ = C::DMA || C::DMAW;
-  constexpr int NI = SWZ ? BK * ROWBV / 1024 / NW : 1;    // 1 KB V loads per wave per tile
-  constexpr int NIK = C::DMAW ? BK * ROWB / 1024 / NW : 1; // 1 KB K loads per wave per tile (384-byte rows)
+  constexpr int NI = SWZ ? BK * ROWBV / 1024 / NWS : 1;    // 1 KB V loads per wave per tile
+  constexpr int NIK = C::DMAW ? BK * ROWB / 1024 / NWS : 1; // 1 KB K loads per wave per tile (384-byte rows)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // 384-byte K rows (D_qk = 192): the low three bits of chunk c of row r are XORed
   // with (r >> 1) & 7, which keeps c within its group of 8 chunks. Consecutive rows
@@ -196,7 +201,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   if constexpr (SWZ) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int row = wave * (BK / NW) + 4 * j + (lane >> 4);
+      const int row = wave * (BK / NWS) + 4 * j + (lane >> 4);
       dgo[j] = (unsigned)(row * ROWBV + 16 * ((lane & 15) ^ swz(row)));
     }
   }
@@ -212,10 +217,11 @@ prefill_bf16_kernel(PrefillArgs a) {
   const unsigned k_bytes_last = (unsigned)((size_t)a.kv_rows * ROWB - 16);
   const u32x4 kdesc = raw_desc((const __bf16*)a.k + kvh * DQK, (unsigned)((size_t)a.kv_rows * DQK * 2));
   const u32x4 vdesc = raw_desc((const __bf16*)a.v + kvh * DV, (unsigned)((size_t)a.kv_rows * DV * 2));
-  const unsigned k_lds = lds_addr(&ks[0][0]), v_lds = lds_addr(&vs[0][0]);
+  // this stream's two buffers
+  const unsigned k_lds = lds_addr(&ks[2 * stream][0]), v_lds = lds_addr(&vs[2 * stream][0]);
   // other head dims: the same direct loads into the padded rows, 1 KB piece by piece
-  PaddedTileDma<BK, DQK * 2, C::KS * 2, NW> kpad;
-  PaddedTileDma<BK, DV * 2, C::VS * 2, NW> vpad;
+  PaddedTileDma<BK, DQK * 2, C::KS * 2, NWS> kpad;
+  PaddedTileDma<BK, DV * 2, C::VS * 2, NWS> vpad;
   if constexpr (!SWZ) {
     kpad.init(wave_u, lane);
     vpad.init(wave_u, lane);
@@ -229,7 +235,7 @@ prefill_bf16_kernel(PrefillArgs a) {
                    kdesc);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        lds_load16(v_lds + (unsigned)(buf * C::V_TILE * 2 + (wave_u * (BK / NW) + 4 * j) * ROWBV),
+        lds_load16(v_lds + (unsigned)(buf * C::V_TILE * 2 + (wave_u * (BK / NWS) + 4 * j) * ROWBV),
                    min(vbase + dgo[j], kv_bytes_last), vdesc);
     } else if constexpr (!C::DMA) {
       kpad.issue(wave_u, k_lds + (unsigned)(buf * C::K_TILE * 2), (unsigned)t.row0 * (DQK * 2),
@@ -243,7 +249,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         // rows past the slab re-read its last chunk: finite values under the mask
         const unsigned off = min(base + dgo[j], kv_bytes_last);
         // K and V rows are both 256 bytes here, so one row offset serves both tiles
-        const unsigned row_off = (unsigned)((wave_u * (BK / NW) + 4 * j) * ROWB);
+        const unsigned row_off = (unsigned)((wave_u * (BK / NWS) + 4 * j) * ROWB);
         lds_load16(k_lds + (unsigned)(buf * C::K_TILE * 2) + row_off, off, kdesc);
         lds_load16(v_lds + (unsigned)(buf * C::V_TILE * 2) + row_off, off, vdesc);
       }
@@ -269,7 +275,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     fresh[nq] = true;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) oacc[nq][mt] = f32x16{};
-    if (MODE == MODE_STEP && valid) {
+    if (MODE == MODE_STEP && valid && stream == 0) {
       // running state (O normalised, LSE) is the online state with m = LSE, l = 1
       const size_t r = (size_t)bh * a.q_rows + row;
       const float lin = a.lse_acc[r];
@@ -329,7 +335,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     else if constexpr (C::DMAW)
       return *(RA_LDS const bf16x8*)(uintptr_t)(kra[4 * buf + (s & 3)] + (unsigned)(128 * (s >> 2) + krow0 * ROWB));
     else
-      return *(const bf16x8*)&ks[buf][(krow0 + l32) * C::KS + 16 * s + 8 * h];
+      return *(const bf16x8*)&ks[2 * stream + buf][(krow0 + l32) * C::KS + 16 * s + 8 * h];
   };
   auto compute_tile = [&](int buf, const TileRef& t, bool need_mask) __attribute__((always_inline)) {
     static_assert(NQ == 1, "one 32-row query block per wave");
@@ -440,7 +446,7 @@ prefill_bf16_kernel(PrefillArgs a) {
           } else {
             const int dcol = 32 * mt + 16 * (gg & 1) + 4 * (L & 3);
             const int key = kt * 32 + 16 * t2 + 8 * x + 4 * (gg >> 1) + (L >> 2);
-            f[t2][x] = lds_read_tr16(&vs[buf][key * C::VS + dcol]);
+            f[t2][x] = lds_read_tr16(&vs[2 * stream + buf][key * C::VS + dcol]);
           }
         }
     };
@@ -469,31 +475,87 @@ prefill_bf16_kernel(PrefillArgs a) {
     skip = a.causal && t.pos0 > wave_pos1;
     need_mask = (t.nvalid < BK) || (a.causal && t.pos0 + BK - 1 > wave_pos0);
   };
-  // tile n+1 streams into the other buffer (last read before the previous
-  // barrier) while tile n is computed; the loop is unrolled by two so that every
-  // LDS address is a lane base plus an immediate
+  // Stream s takes tiles s, s + SPLIT, s + 2 SPLIT, ... of the schedule (SPLIT = 1:
+  // every tile). Each stream's next tile streams into its other buffer (last read
+  // before the previous barrier) while its current tile is computed; every step
+  // ends with one barrier of the whole workgroup, so both streams run the same
+  // number of steps (the second may have no tile in the last one). The loop is
+  // unrolled by two so that every LDS address is a lane base plus an immediate.
+  const int nsteps = (ntiles + SPLIT - 1) / SPLIT;
   TileRef t = walk_ref();
-  dma_tile(t, 0);
+  if (SPLIT == 2 && stream == 1 && ntiles > 1) {
+    walk_next();
+    t = walk_ref();
+  }
+  if (SPLIT == 1 || stream < ntiles) dma_tile(t, 0);
   wait_vmem();
   __syncthreads();
-  auto step = [&](int n, auto bufc) __attribute__((always_inline)) {
+  auto step = [&](int k, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    const int n = k * SPLIT + stream;   // this stream's tile
     bool skip, need_mask;
     tile_flags(t, skip, need_mask);
     TileRef tn = t;
-    if (n + 1 < ntiles) {
-      walk_next();
+    if (n + SPLIT < ntiles) {
+#pragma unroll
+      for (int sx = 0; sx < SPLIT; ++sx) walk_next();
       tn = walk_ref();
       dma_tile(tn, buf ^ 1);
     }
-    if (!skip) compute_tile(buf, t, need_mask);
+    if ((SPLIT == 1 || n < ntiles) && !skip) compute_tile(buf, t, need_mask);
     t = tn;
-    wait_vmem();   // this wave's loads of tile n+1 have landed
+    wait_vmem();   // this wave's loads of its next tile have landed
     __syncthreads();
   };
-  for (int n = 0; n < ntiles; n += 2) {
-    step(n, std::integral_constant<int, 0>{});
-    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
+  for (int k = 0; k < nsteps; k += 2) {
+    step(k, std::integral_constant<int, 0>{});
+    if (k + 1 < nsteps) step(k + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- merge of the two key streams (SPLIT = 2) ------------------------------------
+  // Each stream holds the online state of the same rows over half of the keys.
+  // Stream 1 hands its shift, exp-sum and accumulator to stream 0 through LDS (the
+  // tiles are no longer read after the last barrier), which combines them: with
+  // M the larger of the two shifts, both sides are scaled by 2^(shift - M) before
+  // they are added (a side that saw no key contributes nothing).
+  if constexpr (SPLIT == 2) {
+    static_assert(NWS * C::MT * 4 * 64 * 16 <= sizeof(ks) && NWS * 64 * 2 * 4 <= sizeof(vs), "merge buffers");
+    f32x4* xo = (f32x4*)&ks[0][0];     // [row group][4 MT][64 lanes] f32x4, conflict-free
+    float* xm = (float*)&vs[0][0];     // [row group][64 lanes] shift, then exp-sum
+    float* xl = xm + NWS * 64;
+    if (stream == 1) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = oacc[0][mt][4 * g4 + e];
+          xo[((wave * C::MT + mt) * 4 + g4) * 64 + lane] = x;
+        }
+      xm[wave * 64 + lane] = fresh[0] ? kNegInf : m[0];
+      xl[wave * 64 + lane] = l[0];
+    }
+    __syncthreads();
+    if (stream == 1) return;   // no barrier follows
+    const float mine = fresh[0] ? kNegInf : m[0];
+    const float other = xm[wave * 64 + lane];
+    const float mm = fmaxf(mine, other);
+    if (mm != kNegInf) {
+      const float fa = mine == kNegInf ? 0.f : exp2_hw(mine - mm);
+      const float fb = other == kNegInf ? 0.f : exp2_hw(other - mm);
+      m[0] = mm;
+      fresh[0] = false;
+      l[0] = fa * l[0] + fb * xl[wave * 64 + lane];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 x = xo[((wave * C::MT + mt) * 4 + g4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[0][mt][4 * g4 + e] = fa * oacc[0][mt][4 * g4 + e] + fb * x[e];
+        }
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------------
@@ -528,21 +590,40 @@ prefill_bf16_kernel(PrefillArgs a) {
   }
 }
 
-template <int DQK, int DV, int MODE>
-static hipError_t launch_one(PrefillArgs a, hipStream_t st) {
+// Workgroups of the launch for a given rows-per-workgroup.
+static long long prefill_items(const PrefillArgs& a, int mode, int bq, int& n_qtiles) {
+  const int rows_per_part = mode == MODE_RING ? a.Sp : a.q_rows;
+  n_qtiles = (rows_per_part + bq - 1) / bq;
+  return (long long)a.B * a.Hq * (mode == MODE_RING ? a.nq : 1) * n_qtiles;
+}
+
+template <int DQK, int DV, int MODE, int SPLIT>
+static hipError_t launch_cfg(PrefillArgs a, hipStream_t st) {
   // 8 waves of 32 query rows: two waves per SIMD, so one wave's softmax (VALU)
   // overlaps the other's MFMAs, and each wave's working set fits in VGPRs.
   constexpr int NQ = 1, NW = 8;
-  using C = PCfg<DQK, DV, NQ, NW>;
-  int rows_per_part = MODE == MODE_RING ? a.Sp : a.q_rows;
-  a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;
-  const long long tiles = (long long)a.B * a.Hq * (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
+  using C = PCfg<DQK, DV, NQ, NW, SPLIT>;
+  const long long tiles = prefill_items(a, MODE, C::BQ, a.n_qtiles);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
   const long long grid = 8 * ((tiles + 7) / 8);   // whole rounds of the 8 XCDs
-  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE, SPLIT>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
+}
+
+// One workgroup runs per CU (its LDS tiles fill most of the CU's 160 KB). A launch
+// of fewer 256-row workgroups than two rounds of the chip's 256 CUs is short and
+// bound by its heaviest workgroup, which under a causal mask walks up to twice the
+// average key range; those launches split every workgroup's key range over two
+// streams of waves (128 rows per workgroup), which halves that critical path.
+constexpr long long kSplitBelow = 2 * 256;
+
+template <int DQK, int DV, int MODE>
+static hipError_t launch_one(PrefillArgs a, hipStream_t st) {
+  int nqt;
+  if (prefill_items(a, MODE, PCfg<DQK, DV, 1, 8, 1>::BQ, nqt) < kSplitBelow) return launch_cfg<DQK, DV, MODE, 2>(a, st);
+  return launch_cfg<DQK, DV, MODE, 1>(a, st);
 }
 
 // Returns hipErrorInvalidValue when no kernel instance covers (dqk, dv).
