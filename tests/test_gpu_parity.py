@@ -127,6 +127,57 @@ def test_one_partition_ring_equals_plain_and_split(ra):
     assert float((o1.float() - o4.float()).abs().max()) <= 2e-2
 
 
+# ------------------------------------------------------------------------------ one-stream launches
+# A launch of fewer 256-row workgroups than two rounds of the 256 CUs splits every
+# workgroup's key range over two wave streams (128 rows each); larger launches run
+# one stream per 256-row workgroup. The cases above are small, so they take the
+# two-stream path; these have enough heads and rows for one stream, with ragged
+# query and key tiles.
+
+ONE_STREAM_ITEMS = 2 * 256
+
+
+def one_stream_items(B, Hq, rows, nparts=1):
+    return B * Hq * nparts * ((rows + 255) // 256)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_bf16_ring_one_stream_ragged(ra, dims, causal, layout):
+    B, Hq, Hkv, Sp, P = 1, 128, 16, 300, 2
+    assert one_stream_items(B, Hq, Sp, P) >= ONE_STREAM_ITEMS
+    case = ring_case if layout == "contiguous" else striped_case
+    case(ra, dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+         seed=131 + dims[0])
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_step_chain_one_stream(ra, dims, causal):
+    """Block steps over partitions of 769 rows (three full tiles and one row), from
+    the empty state and then carrying it."""
+    B, Hq, Hkv, Sp, P = 1, 128, 16, 769, 2
+    assert one_stream_items(B, Hq, Sp) >= ONE_STREAM_ITEMS
+    Dqk, Dv = dims
+    S = Sp * P
+    say(f"block_attn_step chain, one stream, D{Dqk}/{Dv} causal={causal}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, Dqk, Dv, seed=141 + Dqk, dtype="bf16")
+    dq, dk, dv = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    o_ref, l_ref = oracle.attention(q, k, v, scale=1 / math.sqrt(Dqk), causal=causal)
+    for i in range(P):
+        qi = dq[:, :, i * Sp:(i + 1) * Sp].contiguous()
+        o_acc, l_acc = ra.init_state(qi, Dv)
+        for j, kind in ra.ring_schedule(P, i, causal):
+            if kind == "skip":
+                continue
+            ra.block_attn_step(qi, dk[:, :, j * Sp:(j + 1) * Sp].contiguous(), dv[:, :, j * Sp:(j + 1) * Sp].contiguous(),
+                               o_acc, l_acc, q_pos0=i * Sp, k_pos0=j * Sp, causal=causal)
+        torch.cuda.synchronize()
+        sl = slice(i * Sp, (i + 1) * Sp)
+        assert_close(np64(o_acc), np64(l_acc), o_ref[:, :, sl], l_ref[:, :, sl], "bf16", f"one-stream chain part {i}")
+
+
 # ------------------------------------------------------------------------------ striped layout
 
 def striped(x, P):

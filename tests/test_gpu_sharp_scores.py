@@ -224,6 +224,32 @@ def test_step_chain_from_empty_negative(ra, kind, dims, causal, layout):
                     f"step chain from empty, part {i}")
 
 
+@pytest.mark.parametrize("kind", ["neg", "negmix"])
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+def test_one_stream_negative(ra, kind, dims):
+    """The same strongly negative scores in launches large enough to run one key
+    stream per 256-row workgroup (128 heads, 2 partitions of 385 rows): the causal
+    ring, and one block step over the whole sequence from the empty state."""
+    B, Hq, Hkv, Sp, P = 1, 128, 16, 385, 2
+    assert B * Hq * P * ((Sp + 255) // 256) >= 2 * 256
+    assert B * Hq * ((Sp * P + 255) // 256) >= 2 * 256
+    Dqk, Dv = dims
+    S = Sp * P
+    say(f"one-stream launches, {kind} D{Dqk}/{Dv}")
+    q, k, v = sharp_inputs(B, Hq, Hkv, S, Dqk, Dv, seed=1200 + Dqk, kind=kind)
+    scale = 1 / math.sqrt(Dqk)
+    o_ref, l_ref = oracle.attention(q, k, v, scale=scale, causal=True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = ra.ring_attn_fwd(qd, kd, vd, P=P, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    sharp_close(np64(o), np64(lse), o_ref, l_ref, f"one-stream ring {kind}")
+    # the whole sequence as one block step: 128 heads x 4 query tiles in one launch
+    o_acc, l_acc = ra.init_state(qd, Dv)
+    ra.block_attn_step(qd, kd, vd, o_acc, l_acc, q_pos0=0, k_pos0=0, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    sharp_close(np64(o_acc), np64(l_acc), o_ref, l_ref, f"one-stream step from empty {kind}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_decode_negative(ra, D):
     """Split-KV decode where every score of the token is strongly negative."""
