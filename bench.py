@@ -22,7 +22,10 @@ The same JSON line carries:
                 average launch time, taken with HIP events on the launch stream
                 during the timed region, against the MI355X peak (bf16 dense MFMA
                 2.5 PFLOP/s; HBM 8 TB/s), and the HBM traffic from rocprofv3
-                counters when they were taken on the current kernel source;
+                counters when they were taken on the current kernel source; for
+                the bf16 prefill also the shader clock rocprofv3 measured over
+                that kernel (GRBM_GUI_ACTIVE per XCD over the launch) and the
+                fraction of the MFMA peak recomputed at that clock;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload,
                 timed on this host's cores, with the full workload's oracle time
                 extrapolated at that rate; the other workloads likewise (the two
@@ -48,6 +51,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 CSRC = os.path.join(ROOT, "blockwise_exact_attention_block_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+SCLK_FILE = os.path.join(ROOT, "profiles", "sclk.txt")
+# dense bf16 MFMA work per clock: 256 CUs x 4 SIMDs x one 32x32x16 product (32768 FLOP)
+# per 32 cycles; 2.4 GHz gives the 2.5 PFLOP/s peak
+MFMA_BF16_FLOP_PER_CLK = 256 * 4 * 1024
 KERNEL_SOURCES = {
     "prefill": ["prefill_bf16.hip", "common.hpp"],
     "decode": ["decode_bf16.hip", "common.hpp"],
@@ -66,18 +73,25 @@ def source_sha(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
+def recorded(path: str, kind: str, workload: str, nvalues: int):
+    """The values recorded in a profiles/ table for (kernel kind, workload) on this
+    exact kernel source, or None."""
+    if not os.path.exists(path):
+        return None
+    sha = source_sha(kind)
+    with open(path) as f:
+        for line in f:
+            parts = line.split("#", 1)[0].split()
+            if len(parts) == 3 + nvalues and parts[:3] == [kind, workload, sha]:
+                return [float(x) for x in parts[3:]]
+    return None
+
+
 def recorded_traffic(kind: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
     scaled by the copy-kernel calibration), if recorded for this exact source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    sha = source_sha(kind)
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            parts = line.split("#", 1)[0].split()
-            if len(parts) == 5 and parts[0] == kind and parts[1] == workload and parts[2] == sha:
-                return float(parts[3]) + float(parts[4])
-    return None
+    r = recorded(TRAFFIC_FILE, kind, workload, 2)
+    return None if r is None else r[0] + r[1]
 
 
 def prefill_flops(cfg) -> int:
@@ -457,6 +471,13 @@ def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
                 "peak": PEAK_FP32_TFLOPS, "traffic": None}
     roof.update({"achieved": round(achieved, 3), "unit": "TFLOP/s", "frac": round(achieved / roof["peak"], 4),
                  "algorithmic_flops_per_launch": flops, "launch_ms": round(ev_ms, 5)})
+    sclk = recorded(SCLK_FILE, "prefill", cfg.name, 1) if cfg.dtype == "bf16" else None
+    if sclk is not None:
+        # the clock is a property of the box and its load: recorded on one box, it
+        # rescales this run's peak only approximately
+        peak_at = MFMA_BF16_FLOP_PER_CLK * sclk[0] * 1e9 / 1e12
+        roof.update({"sclk_ghz_recorded": sclk[0], "peak_at_sclk": round(peak_at, 1),
+                     "frac_at_sclk": round(achieved / peak_at, 4)})
     return {
         "workload": f"{cfg.name}: {cfg.description}",
         "value": round(value, 3),
