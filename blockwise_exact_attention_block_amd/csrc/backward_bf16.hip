@@ -19,10 +19,11 @@
 //     - LSE * log2(e)). The dP products start from -delta (their C operand), so they
 //     come out as dP - delta.
 //   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
-//     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column);
-//     K and V tiles are staged in LDS (double buffered). Per 32 keys: S^T = K Q^T and
+//     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column;
+//     at D_qk = 192 the dO rows wait in a lane-private LDS area instead); K and V
+//     tiles are staged in LDS (double buffered). Per 32 keys: S^T = K Q^T and
 //     dP^T = V dO^T (lane-local LSE and delta), dS^T, then dQ^T += K^T dS^T with
-//     K^T read through ds_read_b64_tr_b16. K / V tiles are 128 keys.
+//     K^T read through ds_read_b64_tr_b16. K / V tiles are 128 keys (64 at D_qk = 192).
 //   * bwd_dkdv_kernel: one workgroup per 256 keys of one (batch, KV head), 8 waves
 //     of 32 keys, looping over the group's query heads and the visible query tiles
 //     (64 rows, loaded straight from HBM into LDS, with their LSE and delta). K and V
@@ -65,9 +66,11 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
 //
 // NW waves of 32 rows (dQ) or keys (dK, dV) per workgroup. At D_qk = 192, D_v = 128
 // a wave's accumulators alone (dK^T and dV^T of its 32 keys: 160 registers) and its
-// K and V rows (80) leave no room at two waves per SIMD, and the dQ kernel's Q and
-// dO rows (80) and dQ^T accumulators (96) do not fit either, so both kernels run
-// four waves there, one per SIMD, each with the whole register file.
+// K and V rows (80) leave no room at two waves per SIMD, so the dK/dV kernel runs
+// four waves there, one per SIMD, each with the whole register file. The dQ
+// kernel's Q and dO rows (80) and dQ^T accumulators (96) do not fit either; there
+// its dO rows move to a lane-private LDS area (64 KB beside two 64-key K and V
+// tiles), which leaves 239 VGPRs and keeps eight waves.
 template <int DQK, int DV, int NW>
 struct BCfg {
   static constexpr int THREADS = NW * 64;
@@ -82,7 +85,11 @@ struct BCfg {
 template <int DQK, int DV>
 constexpr int dkdv_waves() { return DQK > 128 ? 4 : 8; }
 template <int DQK, int DV>
-constexpr int dq_waves() { return DQK > 128 ? 4 : 8; }
+constexpr int dq_waves() { return 8; }
+// D_qk = 192: the dO rows of each wave sit in a lane-private LDS area instead of VGPRs
+// (each lane reads back only the 16-byte chunks it wrote, so no barrier is needed)
+template <int DQK, int DV>
+constexpr bool dq_o_in_lds() { return DQK > 128; }
 
 // Row order inside each 16-row block of a tile read both as rows and transposed: the
 // MFMA row (accumulator row) 4a + b reads LDS row 4b + a (an involution). A half
@@ -100,8 +107,11 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int BK = C::BK;
   constexpr int KCH = BK * DQK / 8 / C::THREADS, VCH = BK * DV / 8 / C::THREADS;
   static_assert(KCH * C::THREADS * 8 == BK * DQK && VCH * C::THREADS * 8 == BK * DV, "tile split");
+  constexpr bool OLDS = dq_o_in_lds<DQK, DV>();
   __shared__ __attribute__((aligned(16))) __bf16 ks[2][BK * C::KS];
   __shared__ __attribute__((aligned(16))) __bf16 vs[2][BK * C::VS];
+  // lane-private dO rows (OLDS): lane (wave, l32, h) holds chunk 16 s + 8 h of row l32
+  __shared__ __attribute__((aligned(16))) bf16x8 osm[OLDS ? NW * C::DSV * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, gg = lane >> 4, L = lane & 15;
@@ -133,13 +143,21 @@ bwd_dq_kernel(BwdArgs a) {
   const int wave_row0 = row_base + wave * 32;
   const long long wave_pos0 = a.q_pos0 + wave_row0;
   const int my_row = wave_row0 + l32;
-  bf16x8 qf[C::DS], of[C::DSV];
+  bf16x8 qf[C::DS], of[OLDS ? 1 : C::DSV];
 #pragma unroll
   for (int s = 0; s < C::DS; ++s)
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (unsigned)(my_row * DQK + 16 * s + 8 * h) * 2u));
+  // conflict-free: consecutive lanes take consecutive 16-byte slots
+  auto oslot = [&](int s) -> bf16x8& { return osm[(wave * C::DSV + s) * 64 + lane]; };
+  if constexpr (OLDS) {
 #pragma unroll
-  for (int s = 0; s < C::DSV; ++s)
-    of[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
+    for (int s = 0; s < C::DSV; ++s)
+      oslot(s) = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::DSV; ++s)
+      of[s] = __builtin_bit_cast(bf16x8, buf_load16(ors, (unsigned)(my_row * DV + 16 * s + 8 * h) * 2u));
+  }
   // a row past the block, or with no visible key at all, gets P = 0
   float lse2 = kPosInf, dlt = 0.f;
   if (my_row < a.Sq) {
@@ -214,7 +232,12 @@ bwd_dq_kernel(BwdArgs a) {
         if (s + 1 < C::DSV) vn = *(const bf16x8*)&vs[buf][krow * C::VS + 16 * (s + 1) + 8 * h];
         __builtin_amdgcn_sched_barrier(0);
         if (s < C::DS) st = mfma32(kc, qf[s], st);
-        if (s < C::DSV) dpt = mfma32(vc, of[s], dpt);
+        if (s < C::DSV) {
+          if constexpr (OLDS)
+            dpt = mfma32(vc, oslot(s), dpt);
+          else
+            dpt = mfma32(vc, of[s], dpt);
+        }
         __builtin_amdgcn_sched_barrier(0);
         kc = kn;
         vc = vn;
