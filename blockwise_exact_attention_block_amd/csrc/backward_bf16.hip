@@ -26,11 +26,12 @@
 //     K^T read through ds_read_b64_tr_b16. K / V tiles are 128 keys (64 at D_qk = 192).
 //   * bwd_dkdv_kernel: one workgroup per 256 keys of one (batch, KV head), 8 waves
 //     of 32 keys, looping over the group's query heads and the visible query tiles
-//     (64 rows, loaded straight from HBM into LDS, with their LSE and delta). K and V
-//     rows stay in VGPRs as the B operands of S = Q K^T and dP = dO V^T (lane = key
-//     column). dV^T += dO^T P and dK^T += Q^T dS take dO^T and Q^T through
-//     ds_read_b64_tr_b16. Rows past the query block carry LSE = +inf, so their P
-//     and dS are exactly 0 with no row mask.
+//     (64 rows, 32 at D_qk = 192, loaded straight from HBM into LDS, with their LSE
+//     and delta). K and V rows stay in VGPRs as the B operands of S = Q K^T and
+//     dP = dO V^T (lane = key column; at D_qk = 192 the K rows wait in a
+//     lane-private LDS area instead). dV^T += dO^T P and dK^T += Q^T dS take dO^T
+//     and Q^T through ds_read_b64_tr_b16. Rows past the query block carry
+//     LSE = +inf, so their P and dS are exactly 0 with no row mask.
 #include "common.hpp"
 
 namespace ra {
@@ -64,26 +65,31 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
 // (D + 8)-element rows start 4 (D = 64, 128) or 36 (D = 192) banks apart, which
 // serves both reads below alike.
 //
-// NW waves of 32 rows (dQ) or keys (dK, dV) per workgroup. At D_qk = 192, D_v = 128
-// a wave's accumulators alone (dK^T and dV^T of its 32 keys: 160 registers) and its
-// K and V rows (80) leave no room at two waves per SIMD, so the dK/dV kernel runs
-// four waves there, one per SIMD, each with the whole register file. The dQ
-// kernel's Q and dO rows (80) and dQ^T accumulators (96) do not fit either; there
-// its dO rows move to a lane-private LDS area (64 KB beside two 64-key K and V
-// tiles), which leaves 239 VGPRs and keeps eight waves.
+// NW = 8 waves of 32 rows (dQ) or keys (dK, dV) per workgroup, two per SIMD. At
+// D_qk = 192, D_v = 128 a wave's working set does not fit the 256 registers of
+// two waves per SIMD as it does at D = 128: the dK/dV kernel's dK^T and dV^T
+// accumulators of 32 keys take 160 registers beside 80 of K and V rows, the dQ
+// kernel's dQ^T 96 beside 80 of Q and dO rows. There one stationary operand moves
+// to a lane-private LDS area: each lane stores its own 16-byte chunks once and
+// reads back only those, so no barrier is involved. The dK/dV kernel parks its K
+// rows (96 KB beside 32-row Q and dO tiles: 139 KB) and runs at 254 VGPRs; the dQ
+// kernel parks its dO rows (64 KB beside 64-key K and V tiles: 148 KB), 239 VGPRs.
 template <int DQK, int DV, int NW>
 struct BCfg {
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * 32;              // query rows (dQ) / keys (dK, dV) per workgroup
   static constexpr int BK = DQK > 128 ? 64 : 128;   // keys per LDS tile (dQ kernel): two K + V tiles fit
-  static constexpr int BQ = 64;                     // query rows per LDS tile (dK/dV kernel)
+  static constexpr int BQ = DQK > 128 ? 32 : 64;    // query rows per LDS tile (dK/dV kernel; 32 leaves room for the K rows)
   static constexpr int KS = DQK + 8, VS = DV + 8, OS = DV + 8;
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
   static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
 };
 // Waves per workgroup of the two kernels.
 template <int DQK, int DV>
-constexpr int dkdv_waves() { return DQK > 128 ? 4 : 8; }
+constexpr int dkdv_waves() { return 8; }
+// D_qk = 192: the K rows of each wave sit in a lane-private LDS area instead of VGPRs
+template <int DQK, int DV>
+constexpr bool dkdv_k_in_lds() { return DQK > 128; }
 template <int DQK, int DV>
 constexpr int dq_waves() { return 8; }
 // D_qk = 192: the dO rows of each wave sit in a lane-private LDS area instead of VGPRs
@@ -108,8 +114,9 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int KCH = BK * DQK / 8 / C::THREADS, VCH = BK * DV / 8 / C::THREADS;
   static_assert(KCH * C::THREADS * 8 == BK * DQK && VCH * C::THREADS * 8 == BK * DV, "tile split");
   constexpr bool OLDS = dq_o_in_lds<DQK, DV>();
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][BK * C::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[2][BK * C::VS];
+  // the direct loads fill whole 1 KB pieces, so each tile is allocated in whole KB
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][padded_tile_bytes(BK, C::KS * 2) / 2];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[2][padded_tile_bytes(BK, C::VS * 2) / 2];
   // lane-private dO rows (OLDS): lane (wave, l32, h) holds chunk 16 s + 8 h of row l32
   __shared__ __attribute__((aligned(16))) bf16x8 osm[OLDS ? NW * C::DSV * 64 : 1];
 
@@ -174,6 +181,8 @@ bwd_dq_kernel(BwdArgs a) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   PaddedTileDma<BK, DQK * 2, C::KS * 2, NW> kdma;
   PaddedTileDma<BK, DV * 2, C::VS * 2, NW> vdma;
+  static_assert(sizeof(ks[0]) == decltype(kdma)::PIECES * 1024 && sizeof(vs[0]) == decltype(vdma)::PIECES * 1024,
+                "every 1 KB piece of a tile's direct loads lands inside that tile");
   if constexpr (DMA) {
     kdma.init(wave_u, lane);
     vdma.init(wave_u, lane);
@@ -349,10 +358,15 @@ bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<DQK, DV, NW>;
   constexpr int BQ = C::BQ;
   constexpr int QS = C::KS, OS = C::OS;   // Q rows like K rows
-  __shared__ __attribute__((aligned(16))) __bf16 qsm[2][BQ * QS];
-  __shared__ __attribute__((aligned(16))) __bf16 osm[2][BQ * OS];
+  // the direct loads fill whole 1 KB pieces, so each tile is allocated in whole KB
+  // (32 rows of 400 or 272 bytes are not)
+  __shared__ __attribute__((aligned(16))) __bf16 qsm[2][padded_tile_bytes(BQ, QS * 2) / 2];
+  __shared__ __attribute__((aligned(16))) __bf16 osm[2][padded_tile_bytes(BQ, OS * 2) / 2];
   __shared__ __attribute__((aligned(16))) float lsm[2][BQ];
   __shared__ __attribute__((aligned(16))) float dsm[2][BQ];
+  constexpr bool KLDS = dkdv_k_in_lds<DQK, DV>();
+  // lane-private K row chunks (KLDS): lane (wave, l32, h) holds chunk 16 s + 8 h of its key
+  __shared__ __attribute__((aligned(16))) bf16x8 kpriv[KLDS ? NW * C::DS * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: derived positions stay scalar
@@ -388,10 +402,16 @@ bwd_dkdv_kernel(BwdArgs a) {
   const int my_key = wave_key0 + l32;
 
   // K row of the lane's key as the B operand of S = Q K^T (keys past the block read 0)
-  bf16x8 kf[C::DS];
+  bf16x8 kf[KLDS ? 1 : C::DS];
+  auto kslot = [&](int s) -> bf16x8& { return kpriv[(wave * C::DS + s) * 64 + lane]; };
 #pragma unroll
-  for (int s = 0; s < C::DS; ++s)
-    kf[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
+  for (int s = 0; s < C::DS; ++s) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, buf_load16(krs, (unsigned)(my_key * DQK + 16 * s + 8 * h) * 2u));
+    if constexpr (KLDS)
+      kslot(s) = x;
+    else
+      kf[s] = x;
+  }
   // V row of the lane's key as the B operand of dP = dO V^T
   bf16x8 vf[C::DSV];
 #pragma unroll
@@ -410,6 +430,8 @@ bwd_dkdv_kernel(BwdArgs a) {
   static_assert(C::THREADS >= 2 * BQ, "threads 0 .. 2 BQ - 1 carry the rows' LSE and delta");
   PaddedTileDma<BQ, DQK * 2, QS * 2, NW> qdma;
   PaddedTileDma<BQ, DV * 2, OS * 2, NW> odma;
+  static_assert(sizeof(qsm[0]) == decltype(qdma)::PIECES * 1024 && sizeof(osm[0]) == decltype(odma)::PIECES * 1024,
+                "every 1 KB piece of a tile's direct loads lands inside that tile");
   qdma.init(wave, lane);
   odma.init(wave, lane);
   auto tile_head = [&](int n) { return g * a.group + n / nqt; };
@@ -464,7 +486,12 @@ bwd_dkdv_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kf[s], st);
+      for (int s = 0; s < C::DS; ++s) {
+        if constexpr (KLDS)
+          st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kslot(s), st);
+        else
+          st = mfma32(*(const bf16x8*)&qsm[buf][qrow * QS + 16 * s + 8 * h], kf[s], st);
+      }
 #pragma unroll
       for (int s = 0; s < C::DSV; ++s) {
         dpt = mfma32(*(const bf16x8*)&osm[buf][qrow * OS + 16 * s + 8 * h], vf[s], dpt);
