@@ -72,7 +72,7 @@ bwd_delta_kernel(const __bf16* o, const __bf16* dout, float* delta, long long ro
 // kernel's dQ^T 96 beside 80 of Q and dO rows. There one stationary operand moves
 // to a lane-private LDS area: each lane stores its own 16-byte chunks once and
 // reads back only those, so no barrier is involved. The dK/dV kernel parks its K
-// rows (96 KB beside 32-row Q and dO tiles: 139 KB) and runs at 254 VGPRs; the dQ
+// rows (96 KB beside 32-row Q and dO tiles: 141 KB) and runs at 254 VGPRs; the dQ
 // kernel parks its dO rows (64 KB beside 64-key K and V tiles: 148 KB), 239 VGPRs.
 template <int DQK, int DV, int NW>
 struct BCfg {
@@ -84,16 +84,13 @@ struct BCfg {
   static constexpr int DS = DQK / 16, DSV = DV / 16;  // MFMA k-steps
   static constexpr int MT = DQK / 32, MTV = DV / 32;  // 32-row output tiles
 };
-// Waves per workgroup of the two kernels.
-template <int DQK, int DV>
-constexpr int dkdv_waves() { return 8; }
-// D_qk = 192: the K rows of each wave sit in a lane-private LDS area instead of VGPRs
+// Waves per workgroup of both kernels.
+constexpr int kBwdWaves = 8;
+// D_qk = 192: the K rows (dK/dV kernel) and the dO rows (dQ kernel) of each wave sit
+// in a lane-private LDS area instead of VGPRs (each lane reads back only the 16-byte
+// chunks it wrote, so no barrier is needed)
 template <int DQK, int DV>
 constexpr bool dkdv_k_in_lds() { return DQK > 128; }
-template <int DQK, int DV>
-constexpr int dq_waves() { return 8; }
-// D_qk = 192: the dO rows of each wave sit in a lane-private LDS area instead of VGPRs
-// (each lane reads back only the 16-byte chunks it wrote, so no barrier is needed)
 template <int DQK, int DV>
 constexpr bool dq_o_in_lds() { return DQK > 128; }
 
@@ -612,15 +609,15 @@ hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long lon
 
 template <int DQK, int DV>
 static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
-  using CK = BCfg<DQK, DV, dkdv_waves<DQK, DV>()>;
-  using CQ = BCfg<DQK, DV, dq_waves<DQK, DV>()>;
+  using CK = BCfg<DQK, DV, kBwdWaves>;
+  using CQ = BCfg<DQK, DV, kBwdWaves>;
   // dK, dV first: one workgroup per CK::ROWS keys of a (batch, KV head)
   BwdArgs b = a;
   b.n_tiles = (a.Sk + CK::ROWS - 1) / CK::ROWS;
   long long grid = 8 * (((long long)a.B * a.Hkv * b.n_tiles + 7) / 8);   // whole rounds of the 8 XCDs
   if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
   if (grid > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, dkdv_waves<DQK, DV>()>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, kBwdWaves>), dim3((unsigned)grid),
                        dim3(CK::THREADS), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -629,7 +626,7 @@ static hipError_t bwd_launch(BwdArgs a, hipStream_t st) {
   grid = 8 * (((long long)a.B * a.Hq * b.n_tiles + 7) / 8);
   if (grid > 0x7ffffff0LL) return hipErrorInvalidValue;
   if (grid > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, dq_waves<DQK, DV>()>), dim3((unsigned)grid), dim3(CQ::THREADS),
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, kBwdWaves>), dim3((unsigned)grid), dim3(CQ::THREADS),
                        0, st, b);
   return hipGetLastError();
 }
