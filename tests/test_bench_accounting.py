@@ -46,3 +46,51 @@ def test_decode_bytes():
     assert kv == 8_589_934_592
     assert bench.decode_partial_bytes(c) > kv
     assert bench.decode_partial_bytes(c) - kv < 5e6
+
+
+def test_recorded_profiles_parse():
+    """profiles/traffic.txt and profiles/sclk.txt hold a row per (kernel, workload)
+    that the bench line reports on; bench.py uses a row only while its source hash
+    matches the kernel source, so every row carries a 16-digit hash and sane values."""
+    rows = {}
+    for path, nvals in ((bench.TRAFFIC_FILE, 2), (bench.SCLK_FILE, 1)):
+        with open(path) as f:
+            for line in f:
+                parts = line.split("#", 1)[0].split()
+                if not parts:
+                    continue
+                assert len(parts) == 3 + nvals, line
+                kind, wl, sha = parts[:3]
+                assert len(sha) == 16 and int(sha, 16) >= 0, line
+                vals = [float(x) for x in parts[3:]]
+                rows[(path, kind, wl)] = vals
+    for wl in ("C4", "C3"):
+        fetch, write = rows[(bench.TRAFFIC_FILE, "prefill", wl)]
+        assert fetch > write > 0
+        (ghz,) = rows[(bench.SCLK_FILE, "prefill", wl)]
+        assert 1.0 < ghz < 2.5
+    for wl in ("C5", "C5F"):
+        assert (bench.TRAFFIC_FILE, "decode", wl) in rows
+
+
+def test_recorded_ignores_other_sources(tmp_path):
+    sha = bench.source_sha("prefill")
+    f = tmp_path / "t.txt"
+    f.write_text("# comment\nprefill C4 0000000000000000 1.0 2.0\n"
+                 f"prefill C4 {sha} 3.0 4.0   # trailing comment\nprefill C3 {sha} 5.0\n")
+    assert bench.recorded(str(f), "prefill", "C4", 2) == [3.0, 4.0]
+    assert bench.recorded(str(f), "prefill", "C3", 2) is None      # wrong field count
+    assert bench.recorded(str(f), "decode", "C4", 2) is None
+
+
+def test_mfma_peak_per_clock():
+    # 256 CUs x 4 SIMDs x 32768 FLOP per 32-cycle 32x32x16 product, at 2.4 GHz
+    assert abs(bench.MFMA_BF16_FLOP_PER_CLK * 2.4e9 / 1e12 - 2516.58) < 0.01
+    assert bench.PEAK_BF16_TFLOPS == 2500.0
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
