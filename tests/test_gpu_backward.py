@@ -125,6 +125,26 @@ def test_whole_backward_after_gpu_forward(ra, dims, causal):
     grad_close(gv, rv, "dv")
 
 
+@pytest.mark.parametrize("dims", DIMS)
+def test_whole_backward_group3_batch2(ra, dims):
+    """The same after a GPU forward with a group of three query heads per KV head
+    (not a power of two) and two sequences: the kernels' (batch, KV head, query
+    head) decompositions and the dK/dV sum over a group."""
+    B, Hq, Hkv, S = 2, 6, 2, 401
+    D, Dv = dims
+    say(f"attn_bwd whole, group 3, batch 2, D{D}/{Dv}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, S, S, D, Dv, seed=720 + D, dtype="bf16")
+    do = randn_np((B, Hq, S, Dv), 730 + D, "bf16")
+    dq_, dk_, dv_ = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = ra.ring_attn_fwd(dq_, dk_, dv_, P=1, causal=True)
+    gq, gk, gv = ra.attn_bwd(dq_, dk_, dv_, o, lse, to_dev(do), causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv, _, _ = oracle.attention_bwd(q, k, v, do, scale=1 / math.sqrt(D), causal=True)
+    grad_close(gq, rq, "dq")
+    grad_close(gk, rk, "dk")
+    grad_close(gv, rv, "dv")
+
+
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ring_backward_protocol_equals_whole(ra, dims, causal):

@@ -83,6 +83,18 @@ def test_bf16_gqa_group8(ra):
     ring_case(ra, dtype="bf16", B=1, Hq=16, Hkv=2, Sp=384, P=4, Dqk=128, Dv=128, causal=True, seed=8)
 
 
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_bf16_gqa_group3(ra, dims, layout):
+    """Three query heads per KV head (not a power of two), two sequences."""
+    case = ring_case if layout == "contiguous" else striped_case
+    case(ra, dtype="bf16", B=2, Hq=6, Hkv=2, Sp=200, P=3, Dqk=dims[0], Dv=dims[1], causal=True, seed=61 + dims[0])
+
+
+def test_fp32_gqa_group3(ra):
+    ring_case(ra, dtype="f32", B=2, Hq=6, Hkv=2, Sp=70, P=3, Dqk=64, Dv=64, causal=True, seed=66)
+
+
 def test_single_token_partitions(ra):
     ring_case(ra, dtype="bf16", B=1, Hq=2, Hkv=1, Sp=1, P=5, Dqk=128, Dv=128, causal=True, seed=9)
     ring_case(ra, dtype="f32", B=1, Hq=2, Hkv=1, Sp=1, P=5, Dqk=64, Dv=64, causal=True, seed=9)
@@ -150,6 +162,15 @@ def test_bf16_ring_one_stream_ragged(ra, dims, causal, layout):
     case = ring_case if layout == "contiguous" else striped_case
     case(ra, dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
          seed=131 + dims[0])
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
+def test_bf16_ring_one_stream_batch2(ra, dims):
+    """Two sequences, GQA 8:1, in a launch that runs one key stream per workgroup."""
+    B, Hq, Hkv, Sp, P = 2, 64, 8, 300, 2
+    assert one_stream_items(B, Hq, Sp, P) >= ONE_STREAM_ITEMS
+    ring_case(ra, dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=True,
+              seed=151 + dims[0])
 
 
 @pytest.mark.parametrize("dims", [(128, 128), (192, 128)])
