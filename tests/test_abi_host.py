@@ -264,3 +264,21 @@ def test_noalloc_decode_validation(ra):
     assert call(l=FAKE + 4) == 1
     assert call(q=None) == 1
     assert call(B=0) == 1
+
+
+def test_largest_slab_boundary(ra):
+    """One row past the largest per-head slab (2^31 - 1 bytes) is refused with
+    RA_EUNSUPPORTED before any launch; tests/test_gpu_limits.py runs the largest
+    accepted sizes on the GPU."""
+    lib = ra.load_library()
+    D = 128
+    max_bf16, max_fp8 = (2**31 - 1) // (2 * D), (2**31 - 1) // D
+    # block step: K / V slab of Sk rows
+    assert lib.ra_block_attn_step(1, FAKE, 0, 64, FAKE, FAKE, 0, max_bf16 + 1, 1, 16, 1, D, D, 0.1, 1, FAKE, FAKE,
+                                  None) == 2
+    # decode: cache slab of L rows (bf16, then one-byte fp8 values)
+    L = (max_bf16 // 8 + 1) * 8
+    assert lib.ra_splitkv_partial(1, FAKE, FAKE, FAKE, 1, 8, 1, L, D, D, 8, 0.1, FAKE, FAKE, None) == 2
+    L8 = (max_fp8 // 8 + 1) * 8
+    assert lib.ra_splitkv_partial_fp8(FAKE, FAKE, FAKE, 1.0, 1.0, 1, 8, 1, L8, D, D, 8, 0.1, FAKE, FAKE, None) == 2
+    assert b"exceeds 2^31 bytes" in lib.ra_last_error()
