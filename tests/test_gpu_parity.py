@@ -470,3 +470,36 @@ def test_splitkv_decode_fp8_equals_bf16_path_on_the_widened_cache(ra):
     op, lp, o, l = ra.splitkv_decode(q, kc.to(torch.bfloat16), vc.to(torch.bfloat16), n_splits=n)
     torch.cuda.synchronize()
     assert float((op8 - op).abs().max()) <= 1e-5 and float((lp8 - lp).abs().max()) <= 1e-5
+
+
+# ------------------------------------------------------------------------------ streams
+
+def test_calls_on_two_streams_match_the_default_stream(ra):
+    """Every call runs on torch's current stream and keeps no state between calls:
+    a ring prefill, a block step and a decode issued on two side streams at once
+    (default priority) give bit-identical results to the same calls on the default
+    stream."""
+    q, k, v = (to_dev(x, torch.bfloat16) for x in prefill_inputs_np(1, 8, 2, 2048, 2048, 128, 128, seed=171,
+                                                                       dtype="bf16"))
+    dq_ = to_dev(randn_np((4, 16, 128), 172, "bf16"), torch.bfloat16)
+    dk_ = to_dev(randn_np((4, 2, 3000, 128), 173, "bf16"), torch.bfloat16)
+    dv_ = to_dev(randn_np((4, 2, 3000, 128), 174, "bf16"), torch.bfloat16)
+
+    def work():
+        o, lse = ra.ring_attn_fwd(q, k, v, P=4, causal=True)
+        oa, la = ra.init_state(q[:, :, :512].contiguous(), 128)
+        ra.block_attn_step(q[:, :, :512].contiguous(), k[:, :, 512:1024].contiguous(), v[:, :, 512:1024].contiguous(),
+                           oa, la, q_pos0=1024, k_pos0=512, causal=True)
+        _, _, od, ld = ra.splitkv_decode(dq_, dk_, dv_, n_splits=3)
+        return o, lse, oa, la, od, ld
+
+    ref = work()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        r1 = work()
+    with torch.cuda.stream(s2):
+        r2 = work()
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, r1, r2):
+        assert torch.equal(a, b) and torch.equal(a, c)
