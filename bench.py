@@ -255,6 +255,16 @@ def decode_total_bytes(cfg) -> int:
     return decode_partial_bytes(cfg) + parts + out
 
 
+def guarded(name, fn, *args):
+    """A secondary measurement: an exception in it is recorded in its place on the
+    line ({"error": ...}) instead of losing the headline measured before it."""
+    try:
+        return fn(*args)
+    except Exception as e:   # noqa: BLE001 -- reported on the line, not hidden
+        log(f"[bench] {name} failed: {e!r}")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def timed(fn, steps, warmup, stream, torch):
     """Run warmup untimed steps, then exactly `steps` timed ones bracketed by full
     synchronisation; returns (wall ms per step, mean per-launch ms from events)."""
@@ -574,7 +584,7 @@ def main():
     if cfg.name == "C3" and not args.no_secondary:
         run_c3_extras(args, ra, torch, stream, cfg, q, k, v, line)
     elif not args.no_backward:
-        line["backward_" + cfg.name] = run_backward(args, ra, torch, stream, cfg, q, k, v)
+        line["backward_" + cfg.name] = guarded("backward", run_backward, args, ra, torch, stream, cfg, q, k, v)
     del q, k, v
     torch.cuda.empty_cache()
 
@@ -589,8 +599,8 @@ def main():
             q, k, v = prefill_inputs_torch(c, dev)
             small = name in ("C1", "C2")
             steps = max(args.small_steps, args.steps) if small else args.steps
-            line["prefill_other"][name] = prefill_line(args, ra, torch, stream, c, q, k, v, steps,
-                                                       max(args.warmup, 2))
+            line["prefill_other"][name] = guarded(name, prefill_line, args, ra, torch, stream, c, q, k, v, steps,
+                                                  max(args.warmup, 2))
             if not args.no_cpu_baseline:
                 if small:
                     small_inputs[name] = tuple(x.cpu() for x in (q, k, v))
@@ -603,23 +613,26 @@ def main():
 
     # ---- decode ----------------------------------------------------------------------
     if not args.no_decode:
-        line["decode"] = run_decode(args, ra, torch, dev, stream, CONFIGS["C5"], decode_inputs_torch)
+        line["decode"] = guarded("decode", run_decode, args, ra, torch, dev, stream, CONFIGS["C5"],
+                                 decode_inputs_torch)
         if not args.no_fp8:
-            fp8 = run_decode(args, ra, torch, dev, stream, CONFIGS["C5F"], decode_inputs_fp8_torch)
-            fp8["speedup_vs_bf16_cache"] = round(line["decode"]["ms_per_step"] / fp8["ms_per_step"], 3)
+            fp8 = guarded("fp8 decode", run_decode, args, ra, torch, dev, stream, CONFIGS["C5F"],
+                          decode_inputs_fp8_torch)
+            if "error" not in fp8 and "error" not in line["decode"]:
+                fp8["speedup_vs_bf16_cache"] = round(line["decode"]["ms_per_step"] / fp8["ms_per_step"], 3)
             line["decode_fp8"] = fp8
 
     # ---- the fp64 oracle on the host, after every GPU measurement -------------------
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget:.0f} s on {cfg.name}")
-        line["cpu_baseline"] = cpu_baseline(cfg, samples.pop(cfg.name), args.cpu_budget)
+        line["cpu_baseline"] = guarded("cpu baseline", cpu_baseline, cfg, samples.pop(cfg.name), args.cpu_budget)
         others = {}
         for name, smp in samples.items():
             log(f"[bench] cpu baseline: fp64 oracle for ~{args.cpu_budget / 2:.0f} s on {name}")
-            others[name] = cpu_baseline(CONFIGS[name], smp, args.cpu_budget / 2)
+            others[name] = guarded(f"cpu baseline {name}", cpu_baseline, CONFIGS[name], smp, args.cpu_budget / 2)
         for name, (q, k, v) in small_inputs.items():
             log(f"[bench] cpu baseline: fp64 oracle over all of {name}")
-            others[name] = cpu_full_run(CONFIGS[name], q, k, v)
+            others[name] = guarded(f"cpu baseline {name}", cpu_full_run, CONFIGS[name], q, k, v)
         if others:
             line["cpu_baseline"]["other_workloads"] = others
 
@@ -630,12 +643,12 @@ def run_c3_extras(args, ra, torch, stream, cfg, q, k, v, line):
     """The striped layout, one ring step through the step API and the backward pass,
     on the 70B-class GQA workload."""
     if not args.no_striped and cfg.causal:
-        line["striped"] = run_striped(args, ra, torch, stream, cfg, q, k, v)
-    step = run_ring_step(args, ra, torch, stream, cfg, q, k, v)
+        line["striped"] = guarded("striped", run_striped, args, ra, torch, stream, cfg, q, k, v)
+    step = guarded("ring step", run_ring_step, args, ra, torch, stream, cfg, q, k, v)
     if step is not None:
         line["ring_step"] = step
     if not args.no_backward:
-        bwd = run_backward(args, ra, torch, stream, cfg, q, k, v)
+        bwd = guarded("backward", run_backward, args, ra, torch, stream, cfg, q, k, v)
         if bwd is not None:
             line["backward"] = bwd
 

@@ -94,3 +94,9 @@ def test_more_than_one_gpu_is_refused():
     import sys
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_guarded_records_a_failure_in_place():
+    assert bench.guarded("ok", lambda a, b: a + b, 2, 3) == 5
+    r = bench.guarded("fails", lambda: {}["missing"])
+    assert r == {"error": "KeyError: 'missing'"}
