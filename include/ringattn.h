@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   RA_OK = 0,
   RA_EINVAL = 1,        /* null pointer, bad size, inconsistent shapes, misalignment */
-  RA_EUNSUPPORTED = 2,  /* valid request this build has no kernel for (dtype/head dims) */
+  RA_EUNSUPPORTED = 2,  /* valid request with no kernel instance for it (dtype, head dims, slab size) */
   RA_EHIP = 3           /* the HIP runtime reported an error at launch */
 } ra_status;
 
