@@ -233,7 +233,9 @@ def run_backward(args, ra, torch, stream, cfg, q, k, v):
         "launch_ms": round(ev, 4),
         "algorithmic_flops": flops,
         "tflops": round(flops / (wall * 1e-3) / 1e12, 2),
-        "frac_of_bf16_peak": round(flops / (wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        # bf16 runs on the matrix cores, fp32 on the vector ALUs
+        ("frac_of_bf16_peak" if cfg.dtype == "bf16" else "frac_of_fp32_vector_peak"):
+            round(flops / (wall * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS), 4),
     }
 
 
@@ -451,6 +453,15 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (published, packed)
 
 
+def _f32_backward_workload():
+    from workloads import PrefillConfig
+    return PrefillConfig(name="F32B", dtype="f32", causal=True, B=1, Hq=8, Hkv=2, Sp=2048, P=4, Dqk=128, Dv=128,
+                         seed=1300, description="fp32, causal, GQA 8:2, S 8192 = 4 x 2048, d 128")
+
+
+F32_BWD = _f32_backward_workload()
+
+
 def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
     """Times `steps` ring prefill launches of a workload (after `warmup` untimed
     ones) and returns its measurement: wall ms per step, per-launch ms from HIP
@@ -608,8 +619,19 @@ def main():
                     samples[name] = oracle_sample_inputs(c, q, k, v)
             if name == "C3":
                 run_c3_extras(args, ra, torch, stream, c, q, k, v, line)
+            elif name == "C1" and not args.no_backward:
+                line["backward_C1"] = guarded("backward C1", run_backward, args, ra, torch, stream, c, q, k, v)
             del q, k, v
             torch.cuda.empty_cache()
+            if name == "C1" and not args.no_backward:
+                # C1 (one head, 1024 rows) is far too small to load the chip, so the
+                # fp32 backward is also timed on a GQA sequence of 8192 tokens
+                log(f"[bench] generating {F32_BWD.name} inputs ({F32_BWD.description})")
+                q, k, v = prefill_inputs_torch(F32_BWD, dev)
+                line["backward_f32"] = guarded("backward f32", run_backward, args, ra, torch, stream, F32_BWD, q,
+                                               k, v)
+                del q, k, v
+                torch.cuda.empty_cache()
 
     # ---- decode ----------------------------------------------------------------------
     if not args.no_decode:

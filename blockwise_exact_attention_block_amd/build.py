@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libringattn.so")
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "merge.hip", "decode_bf16.hip", "backward_bf16.hip",
+SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "merge.hip", "decode_bf16.hip", "backward_bf16.hip", "backward_f32.hip",
            "scratch.hip"]
 
 ARCH = "gfx950"

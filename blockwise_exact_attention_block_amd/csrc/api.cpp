@@ -22,6 +22,8 @@ hipError_t lse_merge_n(int out_bf16, long long rows, int n, int Dv, const float*
 hipError_t decode_partial_bf16(const DecodeArgs& a, int d, int kv8, hipStream_t st);
 hipError_t bwd_delta(const __bf16* o, const __bf16* dout, float* delta, long long rows, int Dv, hipStream_t st);
 hipError_t bwd_bf16(const BwdArgs& a, int dqk, int dv, hipStream_t st);
+hipError_t bwd_delta_f32(const float* o, const float* dout, float* delta, long long rows, int Dv, hipStream_t st);
+hipError_t bwd_f32(const BwdArgs& a, int dqk, int dv, hipStream_t st);
 size_t scratch_bytes();
 hipError_t device_scratch(void** ptr);
 }  // namespace ra
@@ -361,12 +363,14 @@ int ra_splitkv_decode_noalloc(int dtype, const void* q, const void* k_cache, con
 int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,
                            void* stream) {
   if (!o || !dout || !delta) return fail(RA_EINVAL, "ra_attn_bwd_preprocess: null pointer");
-  if (dtype != RA_BF16) return fail(RA_EUNSUPPORTED, "ra_attn_bwd_preprocess: bf16 only");
+  if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_EINVAL, "dtype must be RA_F32 or RA_BF16");
   if (rows < 0 || Dv <= 0 || Dv % 8 != 0) return fail(RA_EINVAL, "need rows >= 0 and Dv a positive multiple of 8");
   if (!aligned16(o) || !aligned16(dout) || !aligned16(delta))
     return fail(RA_EINVAL, "ra_attn_bwd_preprocess: pointers must be 16-byte aligned");
-  return hip_status(ra::bwd_delta((const __bf16*)o, (const __bf16*)dout, delta, rows, Dv, (hipStream_t)stream),
-                    "ra_attn_bwd_preprocess launch");
+  const hipError_t e =
+      dtype == RA_BF16 ? ra::bwd_delta((const __bf16*)o, (const __bf16*)dout, delta, rows, Dv, (hipStream_t)stream)
+                       : ra::bwd_delta_f32((const float*)o, (const float*)dout, delta, rows, Dv, (hipStream_t)stream);
+  return hip_status(e, "ra_attn_bwd_preprocess launch");
 }
 
 int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
@@ -376,15 +380,14 @@ int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const flo
   if (!q || !dout || !lse || !delta || !k_blk || !v_blk || !dq_acc || !dk_acc || !dv_acc)
     return fail(RA_EINVAL, "ra_block_attn_bwd_step: null pointer");
   if (int r = check_common(dtype, B, Hq, Hkv, Dqk, Dv, scale)) return r;
-  if (dtype != RA_BF16 || !bf16_dims_ok(Dqk, Dv))
-    return fail(RA_EUNSUPPORTED, "the backward step supports bf16 with (Dqk, Dv) in {(64,64), (128,128), (192,128)}");
   if (Sq <= 0 || Sk <= 0) return fail(RA_EINVAL, "Sq and Sk must be positive");
   if (q_pos0 < 0 || k_pos0 < 0) return fail(RA_EINVAL, "positions must be >= 0");
   if (!aligned16(q) || !aligned16(dout) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(dq_acc) ||
       !aligned16(dk_acc) || !aligned16(dv_acc) || !aligned16(lse) || !aligned16(delta))
     return fail(RA_EINVAL, "pointers must be 16-byte aligned");
-  if (int r = check_slab(Sq, Dqk > Dv ? Dqk : Dv, 2, "q/dout")) return r;
-  if (int r = check_slab(Sk, Dqk > Dv ? Dqk : Dv, 2, "k/v")) return r;
+  const int es = dtype == RA_BF16 ? 2 : 4;
+  if (int r = check_slab(Sq, Dqk > Dv ? Dqk : Dv, es, "q/dout")) return r;
+  if (int r = check_slab(Sk, Dqk > Dv ? Dqk : Dv, es, "k/v")) return r;
   ra::BwdArgs a{};
   a.q = q;
   a.k = k_blk;
@@ -406,7 +409,9 @@ int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const flo
   a.scale = scale;
   a.scale_log2 = scale * ra::kLog2e;
   a.causal = causal ? 1 : 0;
-  return hip_status(ra::bwd_bf16(a, Dqk, Dv, (hipStream_t)stream), "ra_block_attn_bwd_step launch");
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = dtype == RA_BF16 ? ra::bwd_bf16(a, Dqk, Dv, st) : ra::bwd_f32(a, Dqk, Dv, st);
+  return hip_status(e, "ra_block_attn_bwd_step launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,468 @@
+// Backward pass of blockwise exact attention for fp32 inputs on gfx950, on the
+// vector ALUs.
+//
+// The same gradients as the bf16 backward (the exact gradients of O = softmax(scale *
+// Q K^T) V over the visible keys, page "长上下文的第一性挑战", §挑战 1, eq.
+// lc-ch-attention; computed one (query block, KV block) pair at a time from the
+// queries' saved row LSE and delta = rowsum(dO o O), so a ring backward sums such
+// pairs; page "AI 推理系列（十一）：Ring Attention 如何让多张 GPU 共同计算一条超长序列",
+// §什么时候值得引入 Context Parallelism). With P = exp(scale q k - LSE):
+//     dV += P^T dO,  dS = P o (dO V^T - delta),  dQ += scale dS K,  dK += scale dS^T Q.
+// Everything stays in fp32: no product rounds P or dS, so this path meets the fp32
+// tolerance that the bf16 kernels cannot.
+//
+// Three kernels:
+//   * bwd_delta_f32_kernel: delta per query row, 16 lanes per row.
+//   * bwd_dq_f32_kernel (256 threads): 16 query rows of one (batch, head) per
+//     workgroup, key tiles of 64 (32 when D_qk + D_v = 256) in LDS, the next tile
+//     prefetched into registers. Thread t serves row t / 16: first the scores and dP
+//     of keys (t % 16) + 16 u, each Q and dO chunk read once for all of them, whose
+//     dS go to LDS; then dQ columns 64 e + 4 (t % 16) .. + 3 summed over the keys.
+//   * bwd_dkdv_f32_kernel (512 threads): key tiles of 32 of one (batch, KV head), the
+//     tile's K and V rows in LDS; it walks the group's query heads and the visible
+//     query tiles of 16 rows, the two halves of the workgroup taking alternate ones.
+//     Thread t of a half first computes P and dS for key t % 32 and rows t / 32 and
+//     t / 32 + 8, then dV and dK columns 4 (t % 8) + 32 m of key t / 8, summed over the
+//     tile's rows; the halves' sums meet in LDS at the end. A workgroup takes key
+//     tiles kt and n - 1 - kt, which balances causal work.
+// LDS rows are padded by 4 floats; every sum runs in a fixed order, so results are
+// reproducible run to run.
+#include "common.hpp"
+
+namespace ra {
+
+// ---- delta = rowsum(dO o O) -----------------------------------------------------------
+__global__ void __launch_bounds__(256)
+bwd_delta_f32_kernel(const float* o, const float* dout, float* delta, long long rows, int Dv) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int L = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    for (int c = L; c < Dv / 4; c += 16) {
+      const float4 x = *(const float4*)(o + row * Dv + 4 * c);
+      const float4 y = *(const float4*)(dout + row * Dv + 4 * c);
+      acc = fmaf(x.x, y.x, acc);
+      acc = fmaf(x.y, y.y, acc);
+      acc = fmaf(x.z, y.z, acc);
+      acc = fmaf(x.w, y.w, acc);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += shfl_xor_f(acc, m);
+  if (row < rows && L == 0) delta[row] = acc;
+}
+
+template <int DQK, int DV>
+struct F32BCfg {
+  static constexpr int THREADS = 256;
+  static constexpr int BQ = 16;                 // query rows per workgroup (dQ) / per tile (dK/dV)
+  // keys per tile (dQ): 32 when the head dims sum to 256, so that two workgroups
+  // fit a CU's LDS
+  static constexpr int BK = DQK + DV >= 256 ? 32 : 64;
+  static constexpr int NU = BK / 16;            // keys per thread in the dQ kernel's score pass
+  static constexpr int BKEY = 32;               // keys per tile (dK/dV)
+  // every LDS row padded by 4 floats: 16-byte reads of up to 16 rows at one column
+  // start on distinct 4-bank groups
+  static constexpr int QS = DQK + 4, OS = DV + 4, KS = DQK + 4, VS = DV + 4;
+  static constexpr int PS = BK + 4, PS2 = BKEY + 4;
+  static constexpr int KCH = BK * DQK / 4 / THREADS, VCH = BK * DV / 4 / THREADS;
+  static constexpr int QCH = BQ * DQK / 4 / THREADS, OCH = BQ * DV / 4 / THREADS;
+  static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
+  static_assert(QCH * THREADS * 4 == BQ * DQK && OCH * THREADS * 4 == BQ * DV, "tile split");
+  static_assert(DQK % 64 == 0 && DV % 64 == 0, "64-column groups");
+};
+
+__device__ __forceinline__ float dot4(float4 x, float4 y, float acc) {
+  acc = fmaf(x.x, y.x, acc);
+  acc = fmaf(x.y, y.y, acc);
+  acc = fmaf(x.z, y.z, acc);
+  return fmaf(x.w, y.w, acc);
+}
+__device__ __forceinline__ void axpy4(float s, float4 x, float4& acc) {
+  acc.x = fmaf(s, x.x, acc.x);
+  acc.y = fmaf(s, x.y, acc.y);
+  acc.z = fmaf(s, x.z, acc.z);
+  acc.w = fmaf(s, x.w, acc.w);
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *(const float4*)p; }
+
+// Rows [row0, row0 + rows) of a [n, D] fp32 matrix, 16-byte chunks dealt round-robin
+// over the workgroup's threads (chunk e = it * THREADS + tid); rows at or past
+// `limit` read as zero.
+template <int D, int CH, int THREADS>
+__device__ __forceinline__ void load_rows(float4 (&r)[CH], const float* base, int row0, int limit, int tid) {
+#pragma unroll
+  for (int it = 0; it < CH; ++it) {
+    const int e = it * THREADS + tid, rr = e / (D / 4), c4 = e % (D / 4);
+    r[it] = row0 + rr < limit ? *(const float4*)(base + (size_t)(row0 + rr) * D + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+template <int D, int CH, int THREADS, int STRIDE>
+__device__ __forceinline__ void store_rows(const float4 (&r)[CH], float* lds, int tid) {
+#pragma unroll
+  for (int it = 0; it < CH; ++it) {
+    const int e = it * THREADS + tid, rr = e / (D / 4), c4 = e % (D / 4);
+    *(float4*)&lds[rr * STRIDE + 4 * c4] = r[it];
+  }
+}
+
+// ---- dQ -------------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ void __launch_bounds__(256)
+bwd_dq_f32_kernel(BwdArgs a) {
+  using C = F32BCfg<DQK, DV>;
+  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS = C::PS;
+  constexpr int T = C::THREADS;
+  __shared__ __attribute__((aligned(16))) float qsm[BQ * QS];
+  __shared__ __attribute__((aligned(16))) float osm[BQ * OS];
+  __shared__ __attribute__((aligned(16))) float ksm[BK * KS];
+  __shared__ __attribute__((aligned(16))) float vsm[BK * VS];
+  __shared__ __attribute__((aligned(16))) float dssm[BQ * PS];
+
+  const int tid = threadIdx.x, r = tid >> 4, j = tid & 15;
+  // workgroup -> (batch, head, query tile), the heaviest causal tiles first
+  const int qt = a.n_tiles - 1 - (int)(blockIdx.x % a.n_tiles);
+  const int bh = blockIdx.x / a.n_tiles;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / a.group;
+  const int row_base = qt * BQ;
+  const int last_row = min(row_base + BQ, a.Sq) - 1;
+  long long kmax = a.Sk;
+  if (a.causal) kmax = min(kmax, a.q_pos0 + last_row - a.k_pos0 + 1);
+  if (kmax <= 0) return;   // no key of the block is visible to this tile
+  const int ntiles = (int)((kmax + BK - 1) / BK);
+
+  const float* q_head = (const float*)a.q + (size_t)bh * a.Sq * DQK;
+  const float* o_head = (const float*)a.dout + (size_t)bh * a.Sq * DV;
+  const size_t kvh = (size_t)(b * a.Hkv + g) * a.Sk;
+  const float* k_head = (const float*)a.k + kvh * DQK;
+  const float* v_head = (const float*)a.v + kvh * DV;
+
+  {
+    float4 qr[C::QCH], orr[C::OCH];
+    load_rows<DQK, C::QCH, T>(qr, q_head, row_base, a.Sq, tid);
+    load_rows<DV, C::OCH, T>(orr, o_head, row_base, a.Sq, tid);
+    store_rows<DQK, C::QCH, T, QS>(qr, qsm, tid);
+    store_rows<DV, C::OCH, T, OS>(orr, osm, tid);
+  }
+  // the row's statistics: a row past the block, or with no visible key, gets P = 0
+  const int my_row = row_base + r;
+  const long long my_pos = a.q_pos0 + my_row;
+  float lse2 = __builtin_huge_valf(), dlt = 0.f;   // +inf: exp2(s - lse2) = 0
+  if (my_row < a.Sq) {
+    const float l = a.lse[(size_t)bh * a.Sq + my_row];
+    if (l != kNegInf) lse2 = l * kLog2e;
+    dlt = a.delta[(size_t)bh * a.Sq + my_row];
+  }
+
+  // K / V tiles: global -> registers (one tile ahead) -> LDS
+  float4 kr[C::KCH], vr[C::VCH];
+  constexpr int NE = DQK / 64;
+  float4 acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  load_rows<DQK, C::KCH, T>(kr, k_head, 0, a.Sk, tid);
+  load_rows<DV, C::VCH, T>(vr, v_head, 0, a.Sk, tid);
+  store_rows<DQK, C::KCH, T, KS>(kr, ksm, tid);
+  store_rows<DV, C::VCH, T, VS>(vr, vsm, tid);
+  __syncthreads();   // Q, dO and the first K / V tile are in LDS
+  for (int n = 0; n < ntiles; ++n) {
+    const long long kpos0 = a.k_pos0 + (long long)n * BK;
+    const int nvalid = min(BK, a.Sk - n * BK);
+    if (n + 1 < ntiles) {   // lands while this tile is computed
+      load_rows<DQK, C::KCH, T>(kr, k_head, (n + 1) * BK, a.Sk, tid);
+      load_rows<DV, C::VCH, T>(vr, v_head, (n + 1) * BK, a.Sk, tid);
+    }
+    // scores and dP of keys j + 16 u against this thread's row: each Q (dO) chunk
+    // read once for all of them
+    constexpr int NU = C::NU;
+    float s[NU], dp[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) s[u] = dp[u] = 0.f;
+#pragma unroll 4
+    for (int d4 = 0; d4 < DQK / 4; ++d4) {
+      const float4 x = lds4(&qsm[r * QS + 4 * d4]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) s[u] = dot4(x, lds4(&ksm[(j + 16 * u) * KS + 4 * d4]), s[u]);
+    }
+#pragma unroll 4
+    for (int d4 = 0; d4 < DV / 4; ++d4) {
+      const float4 x = lds4(&osm[r * OS + 4 * d4]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) dp[u] = dot4(x, lds4(&vsm[(j + 16 * u) * VS + 4 * d4]), dp[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int key = j + 16 * u;
+      const bool vis = key < nvalid && (!a.causal || kpos0 + key <= my_pos);
+      const float p = vis ? exp2_hw(fmaf(s[u], a.scale_log2, -lse2)) : 0.f;
+      dssm[r * PS + key] = p * (dp[u] - dlt);
+    }
+    __syncthreads();   // the tile's dS is in LDS
+    // dQ columns 64 e + 4 j .. + 3 over the tile's keys
+#pragma unroll 4
+    for (int kk = 0; kk < BK; ++kk) {
+      const float ds = dssm[r * PS + kk];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) axpy4(ds, lds4(&ksm[kk * KS + 64 * e + 4 * j]), acc[e]);
+    }
+    __syncthreads();   // K, V and dS of this tile consumed
+    if (n + 1 < ntiles) {
+      store_rows<DQK, C::KCH, T, KS>(kr, ksm, tid);
+      store_rows<DV, C::VCH, T, VS>(vr, vsm, tid);
+      __syncthreads();
+    }
+  }
+
+  if (my_row < a.Sq) {
+    float* dqp = a.dq + ((size_t)bh * a.Sq + my_row) * DQK;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float4 cur = *(const float4*)(dqp + 64 * e + 4 * j);
+      axpy4(a.scale, acc[e], cur);
+      *(float4*)(dqp + 64 * e + 4 * j) = cur;
+    }
+  }
+}
+
+// ---- dK, dV ---------------------------------------------------------------------------
+// One 32-key tile of one (batch, KV head): dK, dV of its keys summed over the group's
+// query heads and the query tiles that see them, added into the accumulators. The
+// workgroup's two halves of 256 threads walk alternate (head, query tile) pairs, each
+// with its own Q / dO / P / dS tiles, and add their sums through LDS at the end.
+template <int DQK, int DV>
+struct F32KvSmem {
+  using C = F32BCfg<DQK, DV>;
+  // K and V rows; at the end, the second half's partial sums
+  float kv[C::BKEY * (C::KS + C::VS)];
+  float q[2][C::BQ * C::QS];
+  float o[2][C::BQ * C::OS];
+  float p[2][C::BQ * C::PS2];
+  float ds[2][C::BQ * C::PS2];
+  float l2[2][C::BQ];
+  float dl[2][C::BQ];
+};
+
+template <int DQK, int DV>
+__device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, int kt, F32KvSmem<DQK, DV>& sm) {
+  using C = F32BCfg<DQK, DV>;
+  constexpr int BQ = C::BQ, BKEY = C::BKEY, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS2 = C::PS2;
+  constexpr int T = C::THREADS;   // threads per half
+  constexpr int MK = DQK / 32, MV = DV / 32;
+  static_assert(T * (MK + MV) * 16 <= BKEY * (KS + VS) * 4, "partial sums fit the K / V area");
+  const int tid = threadIdx.x, half = tid / T, lt = tid % T;
+  const int key_base = kt * BKEY;
+  int q_first = 0;   // the first query that can see the tile's first key
+  if (a.causal) {
+    const long long f = a.k_pos0 + key_base - a.q_pos0;
+    q_first = (int)max(0LL, min(f, (long long)a.Sq));
+  }
+  if (q_first >= a.Sq) return;   // no query of the block sees these keys
+  const int qt0 = q_first / BQ;
+  const int nqt = (a.Sq + BQ - 1) / BQ - qt0;
+  const int ntiles = a.group * nqt;   // (query head of the group, query tile) pairs
+  const int niter = (ntiles + 1) / 2; // half h takes pairs 2 i + h
+
+  float* ksm = sm.kv;
+  float* vsm = sm.kv + BKEY * KS;
+  float* qsm = sm.q[half];
+  float* osm = sm.o[half];
+  float* psm = sm.p[half];
+  float* dssm = sm.ds[half];
+  const size_t kvh = (size_t)(b * a.Hkv + g) * a.Sk;
+  __syncthreads();   // the previous tile's K, V and partial sums are consumed
+  for (int e = tid; e < BKEY * DQK / 4; e += 2 * T) {
+    const int rr = e / (DQK / 4), c4 = e % (DQK / 4), key = key_base + rr;
+    *(float4*)&ksm[rr * KS + 4 * c4] = key < a.Sk ? *(const float4*)((const float*)a.k + (kvh + key) * DQK + 4 * c4)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int e = tid; e < BKEY * DV / 4; e += 2 * T) {
+    const int rr = e / (DV / 4), c4 = e % (DV / 4), key = key_base + rr;
+    *(float4*)&vsm[rr * VS + 4 * c4] = key < a.Sk ? *(const float4*)((const float*)a.v + (kvh + key) * DV + 4 * c4)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  // phase 1: key kk1 = t % 32 against rows r1 and r1 + 8; phase 2: key kk2 = t / 8,
+  // columns 4 c2 + 32 m (t: the thread's index in its half)
+  const int kk1 = lt & 31, r1 = lt >> 5;
+  const int kk2 = lt >> 3, c2 = lt & 7;
+  const long long kpos1 = a.k_pos0 + key_base + kk1;
+  const bool key1_ok = key_base + kk1 < a.Sk;
+  float4 acck[MK], accv[MV];
+#pragma unroll
+  for (int m = 0; m < MK; ++m) acck[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int m = 0; m < MV; ++m) accv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // the half's next (head, query tile): rows and statistics fetched one step ahead
+  float4 qr[C::QCH], orr[C::OCH];
+  float l2n = kNegInf, dln = 0.f;
+  auto fetch = [&](int n) {
+    const int hq = g * a.group + n / nqt, row0 = (qt0 + n % nqt) * BQ;
+    const size_t bh = (size_t)b * a.Hq + hq;
+    load_rows<DQK, C::QCH, T>(qr, (const float*)a.q + bh * a.Sq * DQK, row0, a.Sq, lt);
+    load_rows<DV, C::OCH, T>(orr, (const float*)a.dout + bh * a.Sq * DV, row0, a.Sq, lt);
+    if (lt < BQ) {
+      // -LSE * log2(e) of each row (-inf past the block or with no visible key: P = 0)
+      const int row = row0 + lt;
+      l2n = kNegInf;
+      dln = 0.f;
+      if (row < a.Sq) {
+        const float l = a.lse[bh * a.Sq + row];
+        if (l != kNegInf) l2n = -l * kLog2e;
+        dln = a.delta[bh * a.Sq + row];
+      }
+    }
+  };
+  if (half < ntiles) fetch(half);
+  for (int it = 0; it < niter; ++it) {
+    const int n = 2 * it + half;
+    const bool active = n < ntiles;   // the second half idles on an odd count's last step
+    const int row0 = (qt0 + n % nqt) * BQ;
+    __syncthreads();   // the previous pair's rows, P and dS are consumed
+    if (active) {
+      store_rows<DQK, C::QCH, T, QS>(qr, qsm, lt);
+      store_rows<DV, C::OCH, T, OS>(orr, osm, lt);
+      if (lt < BQ) {
+        sm.l2[half][lt] = l2n;
+        sm.dl[half][lt] = dln;
+      }
+    }
+    __syncthreads();   // the pair's rows and statistics (and the K, V rows) are in LDS
+    if (n + 2 < ntiles) fetch(n + 2);   // lands while this pair is computed
+    if (active) {
+      float s0 = 0.f, s1 = 0.f, p0 = 0.f, p1 = 0.f;
+#pragma unroll 4
+      for (int d4 = 0; d4 < DQK / 4; ++d4) {
+        const float4 kx = lds4(&ksm[kk1 * KS + 4 * d4]);
+        s0 = dot4(lds4(&qsm[r1 * QS + 4 * d4]), kx, s0);
+        s1 = dot4(lds4(&qsm[(r1 + 8) * QS + 4 * d4]), kx, s1);
+      }
+#pragma unroll 4
+      for (int d4 = 0; d4 < DV / 4; ++d4) {
+        const float4 vx = lds4(&vsm[kk1 * VS + 4 * d4]);
+        p0 = dot4(lds4(&osm[r1 * OS + 4 * d4]), vx, p0);
+        p1 = dot4(lds4(&osm[(r1 + 8) * OS + 4 * d4]), vx, p1);
+      }
+      const long long qpos = a.q_pos0 + row0 + r1;
+      const bool vis0 = key1_ok && (!a.causal || kpos1 <= qpos);
+      const bool vis1 = key1_ok && (!a.causal || kpos1 <= qpos + 8);
+      const float pa = vis0 ? exp2_hw(fmaf(s0, a.scale_log2, sm.l2[half][r1])) : 0.f;
+      const float pb = vis1 ? exp2_hw(fmaf(s1, a.scale_log2, sm.l2[half][r1 + 8])) : 0.f;
+      psm[r1 * PS2 + kk1] = pa;
+      psm[(r1 + 8) * PS2 + kk1] = pb;
+      dssm[r1 * PS2 + kk1] = pa * (p0 - sm.dl[half][r1]);
+      dssm[(r1 + 8) * PS2 + kk1] = pb * (p1 - sm.dl[half][r1 + 8]);
+    }
+    __syncthreads();   // P and dS of the pair are in LDS
+    if (active) {
+#pragma unroll 2
+      for (int rr = 0; rr < BQ; ++rr) {
+        const float p = psm[rr * PS2 + kk2], ds = dssm[rr * PS2 + kk2];
+#pragma unroll
+        for (int m = 0; m < MV; ++m) axpy4(p, lds4(&osm[rr * OS + 32 * m + 4 * c2]), accv[m]);
+#pragma unroll
+        for (int m = 0; m < MK; ++m) axpy4(ds, lds4(&qsm[rr * QS + 32 * m + 4 * c2]), acck[m]);
+      }
+    }
+  }
+
+  // the second half's sums join the first half's through the K / V area
+  float4* red = (float4*)sm.kv;
+  __syncthreads();   // every read of K and V is done
+  if (half == 1) {
+#pragma unroll
+    for (int m = 0; m < MK; ++m) red[m * T + lt] = acck[m];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) red[(MK + m) * T + lt] = accv[m];
+  }
+  __syncthreads();
+  const int key = key_base + kk2;
+  if (half == 0 && key < a.Sk) {
+    float* dkp = a.dk + (kvh + key) * DQK;
+    float* dvp = a.dv + (kvh + key) * DV;
+#pragma unroll
+    for (int m = 0; m < MK; ++m) {
+      const float4 o2 = red[m * T + lt];
+      float4 sum = acck[m];
+      sum.x += o2.x;
+      sum.y += o2.y;
+      sum.z += o2.z;
+      sum.w += o2.w;
+      float4 cur = *(const float4*)(dkp + 32 * m + 4 * c2);
+      axpy4(a.scale, sum, cur);
+      *(float4*)(dkp + 32 * m + 4 * c2) = cur;
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const float4 o2 = red[(MK + m) * T + lt];
+      float4 cur = *(const float4*)(dvp + 32 * m + 4 * c2);
+      cur.x += accv[m].x + o2.x;
+      cur.y += accv[m].y + o2.y;
+      cur.z += accv[m].z + o2.z;
+      cur.w += accv[m].w + o2.w;
+      *(float4*)(dvp + 32 * m + 4 * c2) = cur;
+    }
+  }
+}
+
+// A workgroup takes key tiles kt and n - 1 - kt of one (batch, KV head), one after
+// the other. Under a causal mask the first sees about as many query tiles as the
+// second misses, so every workgroup has about the same work; with fewer workgroups
+// than the chip holds at once, an unpaired grid would last as long as its first
+// (heaviest) tile.
+template <int DQK, int DV>
+// Two waves per SIMD: one workgroup per CU, with the registers to keep more LDS
+// reads in flight (at D = 128 the compiler otherwise holds the kernel to the 128
+// registers of two workgroups per CU and serialises the reads).
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dkdv_f32_kernel(BwdArgs a) {
+  using C = F32BCfg<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) F32KvSmem<DQK, DV> sm;
+  const int nkt = (a.Sk + C::BKEY - 1) / C::BKEY;
+  const int pair = (int)(blockIdx.x % a.n_tiles);   // a.n_tiles = ceil(nkt / 2)
+  const int bg = blockIdx.x / a.n_tiles;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  dkdv_f32_tile<DQK, DV>(a, b, g, pair, sm);
+  if (nkt - 1 - pair != pair) dkdv_f32_tile<DQK, DV>(a, b, g, nkt - 1 - pair, sm);
+}
+
+// ---- launchers ------------------------------------------------------------------------
+hipError_t bwd_delta_f32(const float* o, const float* dout, float* delta, long long rows, int Dv, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long long grid = (rows + 15) / 16;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_delta_f32_kernel, dim3((unsigned)grid), dim3(256), 0, st, o, dout, delta, rows, Dv);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
+  using C = F32BCfg<DQK, DV>;
+  BwdArgs b = a;
+  b.n_tiles = ((a.Sk + C::BKEY - 1) / C::BKEY + 1) / 2;   // pairs of key tiles
+  long long grid = (long long)a.B * a.Hkv * b.n_tiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(2 * C::THREADS), 0, st, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  b.n_tiles = (a.Sq + C::BQ - 1) / C::BQ;
+  grid = (long long)a.B * a.Hq * b.n_tiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0)
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  return hipGetLastError();
+}
+
+// Returns hipErrorInvalidValue when no kernel instance covers (dqk, dv).
+hipError_t bwd_f32(const BwdArgs& a, int dqk, int dv, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return bwd_f32_launch<64, 64>(a, st);
+  if (dqk == 64 && dv == 128) return bwd_f32_launch<64, 128>(a, st);
+  if (dqk == 128 && dv == 64) return bwd_f32_launch<128, 64>(a, st);
+  if (dqk == 128 && dv == 128) return bwd_f32_launch<128, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

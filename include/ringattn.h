@@ -229,10 +229,11 @@ int ra_splitkv_decode_noalloc(int dtype, const void* q, const void* k_cache, con
  * the forward's saved row LSE.
  *
  * delta[r] = sum_d dout[r, d] * o[r, d] in fp32, for `rows` rows of Dv values
- * (o: the forward output, dout: its incoming gradient; bf16, device, [rows, Dv]).
+ * (o: the forward output, dout: its incoming gradient; device, [rows, Dv], both
+ * RA_BF16 or both RA_F32 as `dtype` says).
  * Errors: RA_EINVAL for null pointers or pointers (delta included) not 16-byte
- * aligned, rows < 0, Dv not a positive multiple of 8; RA_EUNSUPPORTED for a dtype
- * other than RA_BF16. */
+ * aligned, rows < 0, Dv not a positive multiple of 8, a dtype other than RA_F32
+ * or RA_BF16. */
 int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long rows, int Dv, float* delta,
                            void* stream);
 
@@ -241,16 +242,17 @@ int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long
  *   dv_acc += P^T dout,  dS = P o (dout V^T - delta),
  *   dq_acc += scale dS K, dk_acc += scale dS^T Q   (dk/dv summed over each KV
  *   head's query heads),  P = exp(scale Q K^T - lse) on the visible keys.
- *   q, dout  device [B, Hq,  Sq, Dqk / Dv] bf16, queries at global positions q_pos0 ..
+ *   q, dout  device [B, Hq,  Sq, Dqk / Dv] in dtype, queries at global positions q_pos0 ..
  *   lse, delta device [B, Hq, Sq] fp32: the queries' full-row LSE (forward output)
  *            and delta (ra_attn_bwd_preprocess); a row with LSE = -inf adds nothing
- *   k_blk, v_blk device [B, Hkv, Sk, Dqk / Dv] bf16, keys at global positions k_pos0 ..
+ *   k_blk, v_blk device [B, Hkv, Sk, Dqk / Dv] in dtype, keys at global positions k_pos0 ..
  *   dq_acc [B, Hq, Sq, Dqk], dk_acc [B, Hkv, Sk, Dqk], dv_acc [B, Hkv, Sk, Dv] fp32 (in/out)
  * A ring backward is this step for every (query block, KV block) pair, in any
  * order, with dk_acc / dv_acc travelling with their block. Two launches (dK/dV,
  * then dQ) on the stream. Supported: RA_BF16 with (Dqk, Dv) in {(64,64),
- * (128,128), (192,128)}. Errors as ra_block_attn_step. The accumulators must not overlap the
- * inputs or each other. */
+ * (128,128), (192,128)} (matrix cores; P and dS rounded to bf16 for the products)
+ * and RA_F32 with Dqk, Dv in {64, 128} (vector ALUs, fp32 throughout). Errors as
+ * ra_block_attn_step. The accumulators must not overlap the inputs or each other. */
 int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
                            long long q_pos0, int Sq, const void* k_blk, const void* v_blk, long long k_pos0, int Sk,
                            int B, int Hq, int Hkv, int Dqk, int Dv, float scale, int causal, float* dq_acc,

@@ -127,11 +127,14 @@ def test_step_merge_decode_validation(ra):
         dtype=1, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, q_pos0=0, Sq=64, k=FAKE, v=FAKE, k_pos0=0, Sk=64, B=1,
         Hq=2, Hkv=2, Dqk=128, Dv=128, scale=0.1, causal=1, dq=FAKE, dk=FAKE, dv=FAKE, stream=None), **kw).values())
     assert bw(Dqk=96, Dv=96) == 2
-    assert bw(dtype=0) == 2
+    assert bw(dtype=0, Dqk=192, Dv=128) == 2   # no fp32 kernel at D_qk 192
+    assert bw(dtype=2) == 1
+    assert bw(dtype=0, Dqk=64, Dv=96) == 2
     assert bw(Sq=0) == 1
     assert bw(q=None) == 1
     assert bw(Hkv=3) == 1
-    assert lib.ra_attn_bwd_preprocess(0, FAKE, FAKE, 10, 128, FAKE, None) == 2
+    assert lib.ra_attn_bwd_preprocess(2, FAKE, FAKE, 10, 128, FAKE, None) == 1
+    assert lib.ra_attn_bwd_preprocess(0, FAKE, FAKE, 10, 12, FAKE, None) == 1
     assert lib.ra_attn_bwd_preprocess(1, FAKE, FAKE, 10, 12, FAKE, None) == 1
     assert lib.ra_attn_bwd_preprocess(1, FAKE, FAKE, 0, 128, FAKE, None) == 0
     # merges: zero rows is a no-op; bad Dv rejected

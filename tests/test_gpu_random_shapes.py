@@ -6,7 +6,8 @@ parameters before it runs.
 
 Sizes stay small enough for the fp64 oracle (at most a few hundred rows and keys
 per block). Gates are those of the other parity tests (gpu_util.TOL for forward
-and decode, the backward gates of tests/test_gpu_backward.py)."""
+and decode, the backward gates of tests/test_gpu_backward.py and, for fp32 inputs,
+tests/test_gpu_backward_f32.py)."""
 import math
 
 import numpy as np
@@ -83,13 +84,13 @@ def decode_cases(n, seed=2026):
     return out
 
 
-def bwd_cases(n, seed=2027):
+def bwd_cases(n, seed=2027, dt="bf16"):
     g = np.random.default_rng(seed)
     out = []
     for _ in range(n):
-        dims = DIMS["bf16"][int(g.integers(3))]
+        dims = DIMS[dt][int(g.integers(len(DIMS[dt])))]
         hq, hkv = heads(g)
-        out.append(dict(dims=dims, B=int(g.integers(1, 3)), Hq=hq, Hkv=hkv, Sq=int(g.integers(1, 400)),
+        out.append(dict(dt=dt, dims=dims, B=int(g.integers(1, 3)), Hq=hq, Hkv=hkv, Sq=int(g.integers(1, 400)),
                         Sk=int(g.integers(1, 400)), q_pos0=int(g.integers(0, 600)), k_pos0=int(g.integers(0, 600)),
                         causal=bool(g.integers(2)), seed=int(g.integers(1 << 30))))
     return out
@@ -98,7 +99,7 @@ def bwd_cases(n, seed=2027):
 STEP = step_cases(40)
 RING = ring_cases(30)
 DECODE = decode_cases(20)
-BWD = bwd_cases(20)
+BWD = bwd_cases(20) + bwd_cases(12, seed=2028, dt="f32")
 
 
 @pytest.mark.parametrize("c", STEP, ids=[f"step{i}" for i in range(len(STEP))])
@@ -172,13 +173,19 @@ def test_random_decode(ra, c):
     assert_close(np64(o), np64(lse), o_r, l_r, "bf16", "merged")
 
 
-def bwd_close(got, ref, what, rmax=2e-2, rmean=5e-3):
+# (max error / max |ref|, mean error / mean |ref|, absolute floors): the bf16 gates of
+# tests/test_gpu_backward.py and the fp32 gates of tests/test_gpu_backward_f32.py
+BWD_TOL = {"bf16": (2e-2, 5e-3, 1e-6, 1e-7), "f32": (1e-4, 1e-5, 1e-5, 1e-6)}
+
+
+def bwd_close(got, ref, what, dt):
+    rmax, rmean, amax, amean = BWD_TOL[dt]
     got = np64(got)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     top = float(np.max(np.abs(ref))) if ref.size else 0.0
     err = np.abs(got - ref)
-    assert err.max(initial=0.0) <= rmax * top + 1e-6, (what, float(err.max(initial=0.0)), top)
-    assert err.mean() <= rmean * np.abs(ref).mean() + 1e-7, (what, float(err.mean()))
+    assert err.max(initial=0.0) <= rmax * top + amax, (what, float(err.max(initial=0.0)), top)
+    assert err.mean() <= rmean * np.abs(ref).mean() + amean, (what, float(err.mean()))
 
 
 @pytest.mark.parametrize("c", BWD, ids=[f"bwd{i}" for i in range(len(BWD))])
@@ -189,8 +196,9 @@ def test_random_backward_step(ra, c):
     D, Dv = c["dims"]
     B, Hq, Hkv, Sq, Sk = c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sk"]
     scale = 1 / math.sqrt(D)
-    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=c["seed"], dtype="bf16")
-    do = randn_np((B, Hq, Sq, Dv), c["seed"] + 3, "bf16")
+    dt = c["dt"]
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=c["seed"], dtype=dt)
+    do = randn_np((B, Hq, Sq, Dv), c["seed"] + 3, dt)
     extra = np.arange(7) % Sk                     # 7 more keys after the block (repeats when Sk < 7)
     kf, vf = (np.concatenate([x, x[:, :, extra]], axis=2) for x in (k, v))
     kpos = np.concatenate([c["k_pos0"] + np.arange(Sk), c["k_pos0"] + Sk + np.arange(7)])
@@ -201,11 +209,11 @@ def test_random_backward_step(ra, c):
     dq = torch.zeros((B, Hq, Sq, D), dtype=torch.float32, device=DEV)
     dk = torch.zeros((B, Hkv, Sk, D), dtype=torch.float32, device=DEV)
     dv = torch.zeros((B, Hkv, Sk, Dv), dtype=torch.float32, device=DEV)
-    ra.block_attn_bwd_step(to_dev(q, torch.bfloat16), to_dev(do, torch.bfloat16),
+    ra.block_attn_bwd_step(to_dev(q, TD[dt]), to_dev(do, TD[dt]),
                            to_dev(np.where(np.isfinite(lse), lse, -np.inf), torch.float32),
-                           to_dev(delta, torch.float32), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16),
+                           to_dev(delta, torch.float32), to_dev(k, TD[dt]), to_dev(v, TD[dt]),
                            dq, dk, dv, q_pos0=c["q_pos0"], k_pos0=c["k_pos0"], causal=c["causal"], scale=scale)
     torch.cuda.synchronize()
-    bwd_close(dq, gq, "dq")
-    bwd_close(dk, gk, "dk")
-    bwd_close(dv, gv, "dv")
+    bwd_close(dq, gq, "dq", dt)
+    bwd_close(dk, gk, "dk", dt)
+    bwd_close(dv, gv, "dv", dt)
