@@ -267,9 +267,10 @@ def guarded(name, fn, *args):
         return {"error": f"{type(e).__name__}: {e}"}
 
 
-def timed(fn, steps, warmup, stream, torch):
+def timed(fn, steps, warmup, stream, torch, launches=None):
     """Run warmup untimed steps, then exactly `steps` timed ones bracketed by full
-    synchronisation; returns (wall ms per step, mean per-launch ms from events)."""
+    synchronisation; returns (wall ms per step, mean per-launch ms from events).
+    `launches`, if given, receives every step's event time."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -283,8 +284,18 @@ def timed(fn, steps, warmup, stream, torch):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    ev_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return wall_ms, ev_ms
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if launches is not None:
+        launches.extend(per)
+    return wall_ms, sum(per) / steps
+
+
+def launch_stats(per):
+    """min / median / max of per-step event times (ms)."""
+    v = sorted(per)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"min": round(v[0], 5), "median": round(med, 5), "max": round(v[-1], 5), "n": n}
 
 
 def blas_threads() -> int:
@@ -420,7 +431,8 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
     nsteps = max(args.decode_steps, args.steps)
     log(f"[bench] decode: {max(args.warmup, 2)} warmup + {nsteps} timed steps")
     d_wall, d_ev = timed(dec, nsteps, max(args.warmup, 2), stream, torch)
-    p_wall, p_ev = timed(part, nsteps, max(args.warmup, 2), stream, torch)
+    per = []
+    p_wall, p_ev = timed(part, nsteps, max(args.warmup, 2), stream, torch, per)
     tot_bytes = decode_total_bytes(dcfg)
     part_bytes = decode_partial_bytes(dcfg)
     d_value = tot_bytes / (d_wall * 1e-3) / 1e9
@@ -446,6 +458,7 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
             "traffic": recorded_traffic("decode", dcfg.name),
             "algorithmic_bytes_per_launch": part_bytes,
             "launch_ms": round(p_ev, 5),
+            "launch_ms_stats": launch_stats(per),
         },
     }
 
@@ -476,7 +489,8 @@ def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
                          out=out, lse=lse)
 
     log(f"[bench] {cfg.name} prefill: {warmup} warmup + {steps} timed steps")
-    wall_ms, ev_ms = timed(step, steps, warmup, stream, torch)
+    per = []
+    wall_ms, ev_ms = timed(step, steps, warmup, stream, torch, per)
     flops = prefill_flops(cfg)
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (ev_ms * 1e-3) / 1e12
@@ -491,7 +505,8 @@ def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
         roof = {"kernel": f"prefill_f32_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "alu",
                 "peak": PEAK_FP32_TFLOPS, "traffic": None}
     roof.update({"achieved": round(achieved, 3), "unit": "TFLOP/s", "frac": round(achieved / roof["peak"], 4),
-                 "algorithmic_flops_per_launch": flops, "launch_ms": round(ev_ms, 5)})
+                 "algorithmic_flops_per_launch": flops, "launch_ms": round(ev_ms, 5),
+                 "launch_ms_stats": launch_stats(per)})
     sclk = recorded(SCLK_FILE, "prefill", cfg.name, 1) if cfg.dtype == "bf16" else None
     if sclk is not None:
         # the clock is a property of the box and its load: recorded on one box, it

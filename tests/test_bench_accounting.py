@@ -100,3 +100,9 @@ def test_guarded_records_a_failure_in_place():
     assert bench.guarded("ok", lambda a, b: a + b, 2, 3) == 5
     r = bench.guarded("fails", lambda: {}["missing"])
     assert r == {"error": "KeyError: 'missing'"}
+
+
+def test_launch_stats():
+    """min / median / max of the per-launch times, odd and even counts."""
+    assert bench.launch_stats([3.0, 1.0, 2.0]) == {"min": 1.0, "median": 2.0, "max": 3.0, "n": 3}
+    assert bench.launch_stats([4.0, 1.0, 2.0, 3.0]) == {"min": 1.0, "median": 2.5, "max": 4.0, "n": 4}
