@@ -23,6 +23,9 @@
 // The row's 16 threads exchange the tile's max and sum with xor-shuffles inside
 // their group of 16 lanes. The next K/V tile is fetched into registers while the
 // current one is computed, and written to the other LDS buffer after it.
+// A launch of fewer than 512 query tiles (two per CU) runs 2 or 4 such groups of
+// 256 threads per workgroup instead, each over its own share of the key tiles,
+// and merges their states at the end (prefill_f32_streams_kernel).
 #include "common.hpp"
 
 namespace ra {
@@ -43,6 +46,66 @@ struct F32Cfg {
   static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
 };
 
+// A workgroup's query tile (rows, positions, head) and its key-tile schedule.
+template <int BQ, int BK, int MODE>
+struct F32Work {
+  int bh, b, g, row_base, row_end, ntiles;
+  long long pos_base;
+  RingTiles ring;
+  size_t kvh;
+  long long k_pos0;
+  int Sk;
+  // false: the tile sees no key (step mode), nothing to do
+  __device__ __forceinline__ bool init(const PrefillArgs& a) {
+    const int tiles_per_head = (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
+    bh = blockIdx.x / tiles_per_head;
+    const int gt = tiles_per_head - 1 - (int)(blockIdx.x % tiles_per_head);
+    b = bh / a.Hq;
+    const int hq = bh - b * a.Hq;
+    g = hq / a.group;
+    int part = 0, qt = gt;
+    if (MODE == F32_RING) {
+      part = gt / a.n_qtiles;
+      qt = gt - part * a.n_qtiles;
+    }
+    if (MODE == F32_RING) {
+      row_base = part * a.Sp + qt * BQ;
+      row_end = part * a.Sp + a.Sp;
+      // striped causal: virtual query position = local row (see RingTiles)
+      pos_base = (a.causal && a.striped ? 0LL : (long long)(a.q_part0 + part) * a.Sp) + qt * BQ;
+    } else {
+      row_base = qt * BQ;
+      row_end = a.q_rows;
+      pos_base = a.q_pos0 + row_base;
+    }
+    const int last_row = min(row_base + BQ, row_end) - 1;
+    const long long last_pos = pos_base + (last_row - row_base);
+    kvh = (size_t)(b * a.Hkv + g) * a.kv_rows;
+    k_pos0 = a.k_pos0;
+    Sk = a.Sk;
+    if (MODE == F32_RING) {
+      ring.init(a.q_part0 + part, a.P, a.Sp, BK, a.causal != 0, a.striped != 0, last_row - part * a.Sp);
+      ntiles = ring.ntiles;
+    } else {
+      long long kmax = a.Sk;
+      if (a.causal) kmax = min(kmax, last_pos - a.k_pos0 + 1);
+      if (kmax <= 0) return false;
+      ntiles = (int)((kmax + BK - 1) / BK);
+    }
+    return true;
+  }
+  // tile n -> first key row, position of that key, valid keys (random access)
+  __device__ __forceinline__ void tile_at(int n, int& krow0, long long& kpos0, int& nvalid) const {
+    if (MODE == F32_RING) {
+      ring.tile(n, krow0, kpos0, nvalid);
+    } else {
+      krow0 = n * BK;
+      kpos0 = k_pos0 + (long long)n * BK;
+      nvalid = min(BK, Sk - n * BK);
+    }
+  }
+};
+
 template <int DQK, int DV, int MODE>
 __global__ void __launch_bounds__(256)
 prefill_f32_kernel(PrefillArgs a) {
@@ -57,58 +120,14 @@ prefill_f32_kernel(PrefillArgs a) {
   const int qi = tid >> 4;   // query row inside the tile
   const int j = tid & 15;
 
-  const int tiles_per_head = (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
-  const int bh = blockIdx.x / tiles_per_head;
-  const int gt = tiles_per_head - 1 - (int)(blockIdx.x % tiles_per_head);
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
-  const int g = hq / a.group;
-  int part = 0, qt = gt;
-  if (MODE == F32_RING) {
-    part = gt / a.n_qtiles;
-    qt = gt - part * a.n_qtiles;
-  }
-  int row_base, row_end;
-  long long pos_base;
-  if (MODE == F32_RING) {
-    row_base = part * a.Sp + qt * BQ;
-    row_end = part * a.Sp + a.Sp;
-    // striped causal: virtual query position = local row (see RingTiles)
-    pos_base = (a.causal && a.striped ? 0LL : (long long)(a.q_part0 + part) * a.Sp) + qt * BQ;
-  } else {
-    row_base = qt * BQ;
-    row_end = a.q_rows;
-    pos_base = a.q_pos0 + row_base;
-  }
-  const int last_row = min(row_base + BQ, row_end) - 1;
-  const long long last_pos = pos_base + (last_row - row_base);
-
+  F32Work<BQ, BK, MODE> w;
+  if (!w.init(a)) return;
+  const int bh = w.bh, row_base = w.row_base, row_end = w.row_end, ntiles = w.ntiles;
+  const long long pos_base = w.pos_base;
   const float* q_head = (const float*)a.q + (size_t)bh * a.q_rows * DQK;
-  const size_t kvh = (size_t)(b * a.Hkv + g) * a.kv_rows;
-  const float* k_head = (const float*)a.k + kvh * DQK;
-  const float* v_head = (const float*)a.v + kvh * DV;
-
-  // tile schedule (the same RingTiles rules as the bf16 kernel)
-  RingTiles ring;
-  int ntiles;
-  if (MODE == F32_RING) {
-    ring.init(a.q_part0 + part, a.P, a.Sp, BK, a.causal != 0, a.striped != 0, last_row - part * a.Sp);
-    ntiles = ring.ntiles;
-  } else {
-    long long kmax = a.Sk;
-    if (a.causal) kmax = min(kmax, last_pos - a.k_pos0 + 1);
-    if (kmax <= 0) return;
-    ntiles = (int)((kmax + BK - 1) / BK);
-  }
-  auto tile_at = [&](int n, int& krow0, long long& kpos0, int& nvalid) {
-    if (MODE == F32_RING) {
-      ring.tile(n, krow0, kpos0, nvalid);
-    } else {
-      krow0 = n * BK;
-      kpos0 = a.k_pos0 + (long long)n * BK;
-      nvalid = min(BK, a.Sk - n * BK);
-    }
-  };
+  const float* k_head = (const float*)a.k + w.kvh * DQK;
+  const float* v_head = (const float*)a.v + w.kvh * DV;
+  auto tile_at = [&](int n, int& krow0, long long& kpos0, int& nvalid) { w.tile_at(n, krow0, kpos0, nvalid); };
 
   // queries of the tile into LDS (zero past the end)
   for (int e = tid; e < BQ * DQK / 4; e += C::THREADS) {
@@ -267,6 +286,242 @@ prefill_f32_kernel(PrefillArgs a) {
   }
 }
 
+// Key streams, for launches too small to fill the chip: NS groups of 256 threads
+// share one query tile, group s takes key tiles s, s + NS, s + 2 NS, ... with the
+// same per-tile work as above (single-buffered LDS, the next tile prefetched in
+// registers), and the groups' running states (m, l, O) meet in LDS at the end:
+// with M the largest m, l = sum l_s 2^(m_s - M) and O = sum O_s 2^(m_s - M), the
+// merge of partial softmax states over disjoint key sets.
+template <int DQK, int DV>
+struct F32StreamCfg {
+  using C = F32Cfg<DQK, DV>;
+  static constexpr int NS = DQK + DV <= 128 ? 4 : 2;   // what fits 160 KB of LDS
+  static constexpr int KV = C::BK * C::KS + C::BK * DV;  // one stream's K and V tile
+  static_assert(C::BQ * DV <= KV, "a stream's partial output fits its K / V area");
+};
+
+template <int DQK, int DV, int MODE>
+__global__ void __launch_bounds__((F32StreamCfg<DQK, DV>::NS * 256))
+prefill_f32_streams_kernel(PrefillArgs a) {
+  using C = F32Cfg<DQK, DV>;
+  using SC = F32StreamCfg<DQK, DV>;
+  constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV, NS = SC::NS;
+  constexpr int T = C::THREADS;
+  __shared__ __attribute__((aligned(16))) float qsm[BQ * DQK];
+  __shared__ __attribute__((aligned(16))) float kvsm[NS][SC::KV];
+  __shared__ __attribute__((aligned(16))) float psm[NS][BQ * PS];
+
+  const int tid = threadIdx.x, st = tid / T, lt = tid % T;
+  const int qi = lt >> 4;   // query row inside the tile
+  const int j = lt & 15;
+  float* ksm = kvsm[st];
+  float* vsm = kvsm[st] + BK * KS;
+  float* prow = psm[st];
+
+  F32Work<BQ, BK, MODE> w;
+  if (!w.init(a)) return;
+  const int bh = w.bh, row_base = w.row_base, row_end = w.row_end, ntiles = w.ntiles;
+  const float* q_head = (const float*)a.q + (size_t)bh * a.q_rows * DQK;
+  const float* k_head = (const float*)a.k + w.kvh * DQK;
+  const float* v_head = (const float*)a.v + w.kvh * DV;
+
+  for (int e = tid; e < BQ * DQK / 4; e += NS * T) {
+    const int r = e / (DQK / 4), c4 = e % (DQK / 4);
+    const int row = row_base + r;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < row_end) x = *(const float4*)(q_head + (size_t)row * DQK + 4 * c4);
+    *(float4*)&qsm[r * DQK + 4 * c4] = x;
+  }
+
+  float4 kr[C::KCH], vr[C::VCH];
+  auto load_tile = [&](int krow0, int nvalid) {
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int e = it * T + lt, r = e / (DQK / 4), c4 = e % (DQK / 4);
+      kr[it] = r < nvalid ? *(const float4*)(k_head + (size_t)(krow0 + r) * DQK + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < C::VCH; ++it) {
+      const int e = it * T + lt, r = e / (DV / 4), c4 = e % (DV / 4);
+      vr[it] = r < nvalid ? *(const float4*)(v_head + (size_t)(krow0 + r) * DV + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < C::KCH; ++it) {
+      const int e = it * T + lt, r = e / (DQK / 4), c4 = e % (DQK / 4);
+      *(float4*)&ksm[r * KS + 4 * c4] = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VCH; ++it) {
+      const int e = it * T + lt, r = e / (DV / 4), c4 = e % (DV / 4);
+      *(float4*)&vsm[r * DV + 4 * c4] = vr[it];
+    }
+  };
+
+  const int my_row = row_base + qi;
+  const long long my_pos = w.pos_base + qi;
+  float4 acc[NV];
+  float m = kNegInf, l = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (MODE == F32_STEP && st == 0 && my_row < row_end) {
+    // the running state enters through the first stream
+    const size_t r = (size_t)bh * a.q_rows + my_row;
+    const float lin = a.lse_acc[r];
+    if (lin != kNegInf) {
+      m = lin * kLog2e;
+      l = 1.f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) acc[e] = *(const float4*)(a.o_acc + r * DV + 64 * e + 4 * j);
+    }
+  }
+
+  int krow0 = 0, nvalid = 0;
+  long long kpos0 = 0;
+  if (st < ntiles) {
+    w.tile_at(st, krow0, kpos0, nvalid);
+    load_tile(krow0, nvalid);
+  }
+  const int niter = (ntiles + NS - 1) / NS;
+  for (int it = 0; it < niter; ++it) {
+    const int n = it * NS + st;
+    const bool active = n < ntiles;   // a stream past the end idles through the barriers
+    const long long kpos_cur = kpos0;
+    const int nvalid_cur = nvalid;
+    __syncthreads();   // the previous tile is consumed (and Q is in LDS)
+    if (active) store_tile();
+    __syncthreads();   // this tile is in LDS
+    if (n + NS < ntiles) {
+      w.tile_at(n + NS, krow0, kpos0, nvalid);
+      load_tile(krow0, nvalid);   // lands while this tile is computed
+    }
+    float alpha = 1.f;
+    if (active) {
+      constexpr int KPT = C::KPT;
+      float s[KPT];
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) s[u] = 0.f;
+#pragma unroll 8
+      for (int d4 = 0; d4 < DQK / 4; ++d4) {
+        const float4 qv = *(const float4*)&qsm[qi * DQK + 4 * d4];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const float4 kv = *(const float4*)&ksm[(j + 16 * u) * KS + 4 * d4];
+          s[u] = fmaf(qv.x, kv.x, s[u]);
+          s[u] = fmaf(qv.y, kv.y, s[u]);
+          s[u] = fmaf(qv.z, kv.z, s[u]);
+          s[u] = fmaf(qv.w, kv.w, s[u]);
+        }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int key = j + 16 * u;
+        const bool ok = key < nvalid_cur && (!a.causal || kpos_cur + key <= my_pos);
+        s[u] = ok ? s[u] : kNegInf;
+        mx = fmaxf(mx, s[u]);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+      const float mnew = fmaxf(m, mx * a.scale_log2);
+      const float muse = mnew == kNegInf ? 0.f : mnew;
+      alpha = exp2_hw(m - muse);
+      m = mnew;
+      float rs = 0.f;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const float p = exp2_hw(fmaf(s[u], a.scale_log2, -muse));
+        prow[qi * PS + j + 16 * u] = p;
+        rs += p;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) rs += shfl_xor_f(rs, o);
+      l = l * alpha + rs;
+    }
+    __syncthreads();   // the rows' probabilities are in LDS
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        acc[e].x *= alpha;
+        acc[e].y *= alpha;
+        acc[e].z *= alpha;
+        acc[e].w *= alpha;
+      }
+#pragma unroll 4
+      for (int c4 = 0; c4 < BK / 4; ++c4) {
+        const float4 pv = *(const float4*)&prow[qi * PS + 4 * c4];
+        const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+#pragma unroll
+          for (int e = 0; e < NV; ++e) {
+            const float4 vv = *(const float4*)&vsm[(4 * c4 + e4) * DV + 64 * e + 4 * j];
+            acc[e].x = fmaf(pk[e4], vv.x, acc[e].x);
+            acc[e].y = fmaf(pk[e4], vv.y, acc[e].y);
+            acc[e].z = fmaf(pk[e4], vv.z, acc[e].z);
+            acc[e].w = fmaf(pk[e4], vv.w, acc[e].w);
+          }
+        }
+      }
+    }
+  }
+
+  // merge: streams 1.. leave (m, l, O) in their own LDS areas, stream 0 combines
+  __syncthreads();   // every tile is consumed
+  if (st > 0) {
+    float* ob = kvsm[st];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) *(float4*)&ob[qi * DV + 64 * e + 4 * j] = acc[e];
+    if (j == 0) {
+      psm[st][2 * qi] = m;
+      psm[st][2 * qi + 1] = l;
+    }
+  }
+  __syncthreads();
+  if (st == 0 && my_row < row_end) {
+    float M = m;
+#pragma unroll
+    for (int t = 1; t < NS; ++t) M = fmaxf(M, psm[t][2 * qi]);
+    const float wown = m == kNegInf ? 0.f : exp2_hw(m - M);
+    l *= wown;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      acc[e].x *= wown;
+      acc[e].y *= wown;
+      acc[e].z *= wown;
+      acc[e].w *= wown;
+    }
+#pragma unroll
+    for (int t = 1; t < NS; ++t) {
+      const float mt = psm[t][2 * qi];
+      const float wt = mt == kNegInf ? 0.f : exp2_hw(mt - M);
+      l = fmaf(psm[t][2 * qi + 1], wt, l);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const float4 o = *(const float4*)&kvsm[t][qi * DV + 64 * e + 4 * j];
+        acc[e].x = fmaf(o.x, wt, acc[e].x);
+        acc[e].y = fmaf(o.y, wt, acc[e].y);
+        acc[e].z = fmaf(o.z, wt, acc[e].z);
+        acc[e].w = fmaf(o.w, wt, acc[e].w);
+      }
+    }
+    const size_t r = (size_t)bh * a.q_rows + my_row;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse = l > 0.f ? (M + log2_hw(l)) * kLn2 : kNegInf;
+    float* out = MODE == F32_RING ? (float*)a.o : a.o_acc;
+#pragma unroll
+    for (int e = 0; e < NV; ++e)
+      *(float4*)(out + r * DV + 64 * e + 4 * j) = make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
+    if (j == 0) {
+      if (MODE == F32_RING)
+        a.lse[r] = lse;
+      else
+        a.lse_acc[r] = lse;
+    }
+  }
+}
+
 template <int DQK, int DV, int MODE>
 static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
   using C = F32Cfg<DQK, DV>;
@@ -275,7 +530,13 @@ static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
   const long long tiles = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles), dim3(C::THREADS), 0, st, a);
+  if (tiles < 512) {
+    // fewer query tiles than two per CU: split each tile's keys over streams
+    hipLaunchKernelGGL((prefill_f32_streams_kernel<DQK, DV, MODE>), dim3((unsigned)tiles),
+                       dim3(F32StreamCfg<DQK, DV>::NS * C::THREADS), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles), dim3(C::THREADS), 0, st, a);
+  }
   return hipGetLastError();
 }
 

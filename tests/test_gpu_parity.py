@@ -61,6 +61,48 @@ def test_fp32_ring_ragged(ra, dims, causal, Sp, P):
               seed=11 + Sp + P)
 
 
+# fp32 launches of fewer than 512 query tiles (16 rows each) split every tile's keys
+# over 2 or 4 streams of one workgroup; the cases above take that path. These have
+# enough tiles for one stream per workgroup, with ragged query and key tiles.
+
+F32_ONE_STREAM_TILES = 512
+
+
+def f32_tiles(B, Hq, rows, nparts=1):
+    return B * Hq * nparts * ((rows + 15) // 16)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+def test_fp32_ring_one_stream_ragged(ra, dims, causal, layout):
+    B, Hq, Hkv, Sp, P = 2, 8, 2, 263, 2
+    assert f32_tiles(B, Hq, Sp, P) >= F32_ONE_STREAM_TILES
+    case = ring_case if layout == "contiguous" else striped_case
+    case(ra, dtype="f32", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
+         seed=171 + dims[0] + dims[1])
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("Sq", [520, 40])
+def test_fp32_step_chain_both_paths(ra, dims, Sq):
+    """Two causal block steps from the empty state, queries after both blocks: 520
+    query rows run one key stream per workgroup, 40 rows split the keys."""
+    B, Hq, Hkv, Sk = 2, 8, 2, 300
+    Dqk, Dv = dims
+    assert (f32_tiles(B, Hq, Sq) >= F32_ONE_STREAM_TILES) == (Sq == 520)
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, 2 * Sk, Dqk, Dv, seed=181 + Sq, dtype="f32")
+    q_pos0 = 2 * Sk - 20
+    tq, tk, tv = (to_dev(x, torch.float32) for x in (q, k, v))
+    o_acc, l_acc = ra.init_state(tq, Dv)
+    for j in (1, 0):
+        ra.block_attn_step(tq, tk[:, :, j * Sk:(j + 1) * Sk].contiguous(), tv[:, :, j * Sk:(j + 1) * Sk].contiguous(),
+                           o_acc, l_acc, q_pos0=q_pos0, k_pos0=j * Sk, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, scale=1 / math.sqrt(Dqk), causal=True, q_pos0=q_pos0, k_pos0=0)
+    assert_close(np64(o_acc), np64(l_acc), o_ref, l_ref, "f32", f"fp32 step chain Sq {Sq}")
+
+
 # ------------------------------------------------------------------------------ bf16
 
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)])
