@@ -23,8 +23,8 @@
 //     query tiles of 16 rows, the two halves of the workgroup taking alternate ones.
 //     Thread t of a half first computes P and dS for key t % 32 and rows t / 32 and
 //     t / 32 + 8, then dV and dK columns 4 (t % 8) + 32 m of key t / 8, summed over the
-//     tile's rows; the halves' sums meet in LDS at the end. A workgroup takes key
-//     tiles kt and n - 1 - kt, which balances causal work.
+//     tile's rows; the halves' sums meet in LDS at the end. Under a causal mask a
+//     workgroup takes key tiles kt and n - 1 - kt, which balances the work.
 // LDS rows are padded by 4 floats; every sum runs in a fixed order, so results are
 // reproducible run to run.
 #include "common.hpp"
@@ -407,11 +407,12 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
   }
 }
 
-// A workgroup takes key tiles kt and n - 1 - kt of one (batch, KV head), one after
-// the other. Under a causal mask the first sees about as many query tiles as the
+// Under a causal mask a workgroup takes key tiles kt and n - 1 - kt of one (batch,
+// KV head), one after the other: the first sees about as many query tiles as the
 // second misses, so every workgroup has about the same work; with fewer workgroups
 // than the chip holds at once, an unpaired grid would last as long as its first
-// (heaviest) tile.
+// (heaviest) tile. Without a mask every tile has the same work and a workgroup
+// takes one.
 template <int DQK, int DV>
 // Two waves per SIMD: one workgroup per CU, with the registers to keep more LDS
 // reads in flight (at D = 128 the compiler otherwise holds the kernel to the 128
@@ -421,11 +422,11 @@ bwd_dkdv_f32_kernel(BwdArgs a) {
   using C = F32BCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) F32KvSmem<DQK, DV> sm;
   const int nkt = (a.Sk + C::BKEY - 1) / C::BKEY;
-  const int pair = (int)(blockIdx.x % a.n_tiles);   // a.n_tiles = ceil(nkt / 2)
+  const int kt = (int)(blockIdx.x % a.n_tiles);   // a.n_tiles: ceil(nkt / 2) causal, nkt otherwise
   const int bg = blockIdx.x / a.n_tiles;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  dkdv_f32_tile<DQK, DV>(a, b, g, pair, sm);
-  if (nkt - 1 - pair != pair) dkdv_f32_tile<DQK, DV>(a, b, g, nkt - 1 - pair, sm);
+  dkdv_f32_tile<DQK, DV>(a, b, g, kt, sm);
+  if (a.causal && nkt - 1 - kt != kt) dkdv_f32_tile<DQK, DV>(a, b, g, nkt - 1 - kt, sm);
 }
 
 // ---- launchers ------------------------------------------------------------------------
@@ -441,7 +442,8 @@ template <int DQK, int DV>
 static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
   using C = F32BCfg<DQK, DV>;
   BwdArgs b = a;
-  b.n_tiles = ((a.Sk + C::BKEY - 1) / C::BKEY + 1) / 2;   // pairs of key tiles
+  const int nkt = (a.Sk + C::BKEY - 1) / C::BKEY;
+  b.n_tiles = a.causal ? (nkt + 1) / 2 : nkt;   // causal: pairs of key tiles
   long long grid = (long long)a.B * a.Hkv * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid > 0)
