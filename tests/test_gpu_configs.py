@@ -389,3 +389,94 @@ def test_c4_backward_sampled_rows_keys_and_closed_form(ra):
         del x, tail, err_tail, err_head
     say(f"C4 backward Q=0: dV worst relative max error {worst_max:.3e}, mean {worst_mean:.3e}")
     assert worst_max <= 2e-2 and worst_mean <= 5e-3, (worst_max, worst_mean)
+
+
+@pytest.mark.timeout(600)
+def test_fp32_backward_workload_sampled_rows_keys_and_closed_form(ra):
+    """The fp32 backward at the shape bench.py times it on (causal, GQA 8:2, S 8192 in
+    4 partitions, d 128, fp32), in the same launch configuration: the fp32 ring
+    forward, then the delta preprocess and one step over the whole sequence. The
+    references come from the inputs alone, as for C3 (dQ of sampled rows; dK / dV of
+    keys in the last 256 positions, over every query row that sees them), at the
+    fp32 gate of the backward parity tests: max error <= 1e-4 of the largest
+    reference value.
+
+    Then Q = 0: dV at key c is sum_{r >= c} dO_r / (r + 1) over the KV head's four
+    query heads (fp64 on the device with torch) and dK is exactly 0, at every key.
+    That sum runs over up to n = 32768 terms in fp32, so its rounding is about
+    sqrt(n) 2^-24 ~ 1e-5 of each value: the mean gate there is 5e-5 of the mean
+    |reference| (and max 1e-4 of the largest)."""
+    from bench import F32_BWD as cfg
+    S = cfg.S
+    q, k, v = prefill_inputs_torch(cfg, DEV)
+    o, lse = run_prefill(ra, cfg, q, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 7)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    say(f"attn_bwd {cfg.name} (whole sequence, fp32)")
+    delta = ra.attn_bwd_preprocess(o, dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+    ra.block_attn_bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_pos0=0, k_pos0=0, causal=True, scale=cfg.scale)
+    torch.cuda.synchronize()
+    del o, lse, delta
+    group = cfg.Hq // cfg.Hkv
+    rng = np.random.default_rng(cfg.seed + 11)
+    worst = 0.0
+    for g in (0, cfg.Hkv - 1):
+        k_np, v_np = k[0, g].double().cpu().numpy(), v[0, g].double().cpu().numpy()
+        for h in (g * group, g * group + group - 1):
+            rows = np.unique(np.concatenate([rng.integers(0, S, 6), [0, S - 1, cfg.Sp, cfg.Sp - 1]]))
+            rt = torch.as_tensor(rows, device=DEV)
+            qr = q[0, h, rt].double().cpu().numpy()
+            dr = dout[0, h, rt].double().cpu().numpy()
+            o_r, l_r = oracle.attention_rows(qr, rows, k_np, v_np, scale=cfg.scale, causal=True)
+            ref, _, _ = oracle.block_bwd(qr[None, None], k_np[None, None], v_np[None, None], dr[None, None],
+                                         l_r[None, None], ((dr * o_r).sum(-1))[None, None], scale=cfg.scale,
+                                         causal=True, q_pos=rows, k_pos0=0)
+            err = np.abs(dq[0, h, rt].double().cpu().numpy() - ref[0, 0]).max() / np.abs(ref[0, 0]).max()
+            worst = max(worst, err)
+            assert err <= 1e-4, ("dq", g, h, err)
+        keys = np.unique(np.concatenate([S - 1 - rng.integers(0, 256, 3),
+                                         [S - 1, S - 2, S - 32, S - 33, S - 64, S - 128, S - 256]]))
+        r0 = int(keys.min())
+        rows = np.arange(r0, S)
+        ref_k = np.zeros((len(keys), cfg.Dqk))
+        ref_v = np.zeros((len(keys), cfg.Dv))
+        for h in range(g * group, (g + 1) * group):
+            qh = q[0, h, r0:].double().cpu().numpy()
+            dh = dout[0, h, r0:].double().cpu().numpy()
+            o_ref, l_ref = oracle.attention_rows(qh, rows, k_np, v_np, scale=cfg.scale, causal=True)
+            _, gk, gv = oracle.block_bwd(qh[None, None], k_np[keys][None, None], v_np[keys][None, None],
+                                         dh[None, None], l_ref[None, None], ((dh * o_ref).sum(-1))[None, None],
+                                         scale=cfg.scale, causal=True, q_pos=rows, k_pos=keys)
+            ref_k += gk[0, 0]
+            ref_v += gv[0, 0]
+        kt = torch.as_tensor(keys, device=DEV)
+        for got, refg, name in ((dk[0, g, kt], ref_k, "dk"), (dv[0, g, kt], ref_v, "dv")):
+            err = np.abs(got.double().cpu().numpy() - refg).max() / np.abs(refg).max()
+            worst = max(worst, err)
+            assert err <= 1e-4, (name, g, err)
+    say(f"{cfg.name} backward: worst relative max error {worst:.3e}")
+    del dq, dk, dv, dout
+
+    qz = torch.zeros_like(q)
+    del q
+    o, lse = run_prefill(ra, cfg, qz, k, v)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 8)
+    dout = torch.empty_like(o).normal_(0.0, 1.0, generator=gen)
+    say(f"attn_bwd {cfg.name} with Q = 0")
+    dq, dk, dv = ra.attn_bwd(qz, k, v, o, lse, dout, causal=True, scale=cfg.scale)
+    torch.cuda.synchronize()
+    del o, lse, dq
+    assert torch.count_nonzero(dk).item() == 0, "dK must be exactly zero when Q = 0"
+    inv = 1.0 / torch.arange(1, S + 1, device=DEV, dtype=torch.float64)
+    worst_max = worst_mean = 0.0
+    for g in range(cfg.Hkv):
+        x = dout[0, g * group:(g + 1) * group].double().sum(0) * inv[:, None]
+        ref = torch.flip(torch.cumsum(torch.flip(x, (0,)), 0), (0,))
+        err = (dv[0, g].double() - ref).abs()
+        worst_max = max(worst_max, float(err.max()) / float(ref.abs().max()))
+        worst_mean = max(worst_mean, float(err.mean()) / float(ref.abs().mean()))
+    say(f"{cfg.name} backward Q=0: dV worst relative max error {worst_max:.3e}, mean {worst_mean:.3e}")
+    assert worst_max <= 1e-4 and worst_mean <= 5e-5, (worst_max, worst_mean)
