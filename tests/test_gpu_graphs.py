@@ -103,3 +103,51 @@ def test_noalloc_decode_in_a_graph(ra):
         # an eager call on a smaller problem between replays overwrites the shared partials
         ra.splitkv_decode_noalloc(q[:1].contiguous(), kc[:1].contiguous(), vc[:1].contiguous(), n_splits=2)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_ring_in_a_graph(ra, dtype):
+    """The backward ring protocol (delta, then every visible (query partition, KV
+    block) step, accumulators zeroed by fill kernels) captured and replayed: bf16
+    and fp32 kernels."""
+    B, Hq, Hkv, Sp, P, D = 1, 4, 2, 160, 3, 128
+    S = Sp * P
+    q, k, v = (to_dev(x, dtype) for x in prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=195, dtype="f32"))
+    dout = to_dev(randn_np((B, Hq, S, D), 196, "f32"), dtype)
+    o, lse = ra.ring_attn_fwd(q, k, v, P=P, causal=True)
+    delta = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    part = lambda t, i: t[:, :, i * Sp:(i + 1) * Sp]
+    qs, ks, vs, ds, ls = ([part(t, i).contiguous() for i in range(P)] for t in (q, k, v, dout, lse))
+    dqs = [torch.empty((B, Hq, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    dks = [torch.empty((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    dvs = [torch.empty((B, Hkv, Sp, D), dtype=torch.float32, device=DEV) for _ in range(P)]
+    deltas = [torch.empty((B, Hq, Sp), dtype=torch.float32, device=DEV) for _ in range(P)]
+    os_ = [part(o, i).contiguous() for i in range(P)]
+
+    def chain():
+        for t in dqs + dks + dvs:
+            t.zero_()
+        for i in range(P):
+            ra.attn_bwd_preprocess(os_[i], ds[i], deltas[i])
+        for i in range(P):
+            for j, kind in ra.ring_schedule(P, i, True):
+                if kind != "skip":
+                    ra.block_attn_bwd_step(qs[i], ds[i], ls[i], deltas[i], ks[j], vs[j], dqs[i], dks[j], dvs[j],
+                                           q_pos0=i * Sp, k_pos0=j * Sp, causal=True)
+
+    chain()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in dqs + dks + dvs + deltas]
+    g = capture(chain)
+    for rep in range(3):
+        for t in dqs + dks + dvs + deltas:
+            t.normal_()                        # garbage the graph must overwrite
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"backward replay {rep} ({dtype})")
+        for a, b in zip(dqs + dks + dvs + deltas, ref):
+            assert torch.equal(a, b), rep
+        other = ra.attn_bwd(q, k, v, o, lse, dout, causal=True)   # eager work between replays
+        torch.cuda.synchronize()
+        del other
+    del delta

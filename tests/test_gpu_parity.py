@@ -545,3 +545,30 @@ def test_calls_on_two_streams_match_the_default_stream(ra):
     torch.cuda.synchronize()
     for a, b, c in zip(ref, r1, r2):
         assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_on_two_side_streams(ra, dtype):
+    """The backward entry points issued on two side streams at once give results
+    bit-identical to the same calls on the default stream (bf16 and fp32)."""
+    B, Hq, Hkv, S, D = 1, 8, 2, 1000, 128
+    q, k, v = (to_dev(x, dtype) for x in prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=177, dtype="f32"))
+    dout = to_dev(randn_np((B, Hq, S, D), 178, "f32"), dtype)
+    o, lse = ra.ring_attn_fwd(q, k, v, P=2, causal=True)
+    torch.cuda.synchronize()
+
+    def work():
+        return ra.attn_bwd(q, k, v, o, lse, dout, causal=True)
+
+    ref = work()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        r1 = work()
+    with torch.cuda.stream(s2):
+        r2 = work()
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, r1, r2):
+        assert torch.equal(a, b) and torch.equal(a, c)
