@@ -1,6 +1,7 @@
 """The entry points under HIP graph capture: they enqueue kernels on the given stream
 and nothing else (no allocation, no synchronisation, no memset), so a captured ring
-of block steps and a captured no-allocation decode replay like the eager calls.
+of block steps, a captured no-allocation decode and a captured backward ring replay
+like the eager calls.
 
 Each graph is replayed several times, with other eager work and synchronisations
 between the replays, and every replay is compared bit for bit with the eager result
