@@ -450,7 +450,7 @@ def splitkv_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 
 
 def attn_bwd_preprocess(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None):
-    """delta [B,H,S] fp32 = rowsum(dout * o) for bf16 o, dout [B,H,S,Dv]."""
+    """delta [B,H,S] fp32 = rowsum(dout * o) for o, dout [B,H,S,Dv] (both bf16 or both fp32)."""
     lib = load_library()
     if o.shape != dout.shape or o.dtype != dout.dtype:
         raise RingAttnError(1, "o and dout must have one shape and dtype")
