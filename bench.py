@@ -466,13 +466,13 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (published, packed)
 
 
-def _f32_backward_workload():
+def _f32_wide_workload():
     from workloads import PrefillConfig
     return PrefillConfig(name="F32B", dtype="f32", causal=True, B=1, Hq=8, Hkv=2, Sp=2048, P=4, Dqk=128, Dv=128,
                          seed=1300, description="fp32, causal, GQA 8:2, S 8192 = 4 x 2048, d 128")
 
 
-F32_BWD = _f32_backward_workload()
+F32B = _f32_wide_workload()
 
 
 def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
@@ -640,10 +640,13 @@ def main():
             torch.cuda.empty_cache()
             if name == "C1" and not args.no_backward:
                 # C1 (one head, 1024 rows) is far too small to load the chip, so the
-                # fp32 backward is also timed on a GQA sequence of 8192 tokens
-                log(f"[bench] generating {F32_BWD.name} inputs ({F32_BWD.description})")
-                q, k, v = prefill_inputs_torch(F32_BWD, dev)
-                line["backward_f32"] = guarded("backward f32", run_backward, args, ra, torch, stream, F32_BWD, q,
+                # fp32 prefill and backward are also timed on a GQA sequence of 8192
+                # tokens
+                log(f"[bench] generating {F32B.name} inputs ({F32B.description})")
+                q, k, v = prefill_inputs_torch(F32B, dev)
+                line["prefill_other"][F32B.name] = guarded(F32B.name, prefill_line, args, ra, torch, stream,
+                                                              F32B, q, k, v, args.steps, max(args.warmup, 2))
+                line["backward_f32"] = guarded("backward f32", run_backward, args, ra, torch, stream, F32B, q,
                                                k, v)
                 del q, k, v
                 torch.cuda.empty_cache()

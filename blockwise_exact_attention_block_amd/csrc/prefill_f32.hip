@@ -8,10 +8,10 @@
 // this path exists for fp32 inputs, whose tolerance no bf16 matrix-core product
 // could meet.
 //
-// Workgroup: 256 threads (4 waves), 16 query rows, key tiles of 64. Small fp32
-// problems have few query rows, so a workgroup takes few of them (more
-// workgroups) and walks the keys in tiles of 64. Thread t works for query row
-// t / 16 (the 16 threads of a row sit in one wave):
+// A workgroup owns 16 query rows and walks the keys in tiles of 64, split over NS
+// groups of 256 threads ("key streams": 4 at D_qk = D_v = 64, 2 otherwise, what
+// fits 160 KB of LDS), each taking every NS-th tile. Thread t of a group works for
+// query row t / 16 (the 16 threads of a row sit in one wave):
 //   score phase: keys (t % 16) + 16 u, u = 0..3; each step reads four
 //                consecutive d of the row's query (one broadcast 16-byte LDS read)
 //                and of each of its keys (16-byte reads of padded K rows,
@@ -22,10 +22,10 @@
 //                FMAs.
 // The row's 16 threads exchange the tile's max and sum with xor-shuffles inside
 // their group of 16 lanes. The next K/V tile is fetched into registers while the
-// current one is computed, and written to the other LDS buffer after it.
-// A launch of fewer than 512 query tiles (two per CU) runs 2 or 4 such groups of
-// 256 threads per workgroup instead, each over its own share of the key tiles,
-// and merges their states at the end (prefill_f32_streams_kernel).
+// current one is computed. At the end the groups' states are merged in LDS. Several
+// streams keep 8 or 16 waves on a CU where one 256-thread workgroup with
+// double-buffered tiles (145 KB at D = 128) kept 4, and they split a small
+// launch's key range over more waves.
 #include "common.hpp"
 
 namespace ra {
@@ -106,192 +106,11 @@ struct F32Work {
   }
 };
 
-template <int DQK, int DV, int MODE>
-__global__ void __launch_bounds__(256)
-prefill_f32_kernel(PrefillArgs a) {
-  using C = F32Cfg<DQK, DV>;
-  constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV;
-  __shared__ __attribute__((aligned(16))) float qsm[BQ * DQK];
-  __shared__ __attribute__((aligned(16))) float ksm[2][BK * KS];
-  __shared__ __attribute__((aligned(16))) float vsm[2][BK * DV];
-  __shared__ __attribute__((aligned(16))) float psm[BQ * PS];
-
-  const int tid = threadIdx.x;
-  const int qi = tid >> 4;   // query row inside the tile
-  const int j = tid & 15;
-
-  F32Work<BQ, BK, MODE> w;
-  if (!w.init(a)) return;
-  const int bh = w.bh, row_base = w.row_base, row_end = w.row_end, ntiles = w.ntiles;
-  const long long pos_base = w.pos_base;
-  const float* q_head = (const float*)a.q + (size_t)bh * a.q_rows * DQK;
-  const float* k_head = (const float*)a.k + w.kvh * DQK;
-  const float* v_head = (const float*)a.v + w.kvh * DV;
-  auto tile_at = [&](int n, int& krow0, long long& kpos0, int& nvalid) { w.tile_at(n, krow0, kpos0, nvalid); };
-
-  // queries of the tile into LDS (zero past the end)
-  for (int e = tid; e < BQ * DQK / 4; e += C::THREADS) {
-    const int r = e / (DQK / 4), c4 = e % (DQK / 4);
-    const int row = row_base + r;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < row_end) x = *(const float4*)(q_head + (size_t)row * DQK + 4 * c4);
-    *(float4*)&qsm[r * DQK + 4 * c4] = x;
-  }
-
-  // K / V tiles: global -> registers (rows past the tile's valid keys read as zero),
-  // registers -> LDS
-  float4 kr[C::KCH], vr[C::VCH];
-  auto load_tile = [&](int krow0, int nvalid) {
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int e = it * C::THREADS + tid, r = e / (DQK / 4), c4 = e % (DQK / 4);
-      kr[it] = r < nvalid ? *(const float4*)(k_head + (size_t)(krow0 + r) * DQK + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VCH; ++it) {
-      const int e = it * C::THREADS + tid, r = e / (DV / 4), c4 = e % (DV / 4);
-      vr[it] = r < nvalid ? *(const float4*)(v_head + (size_t)(krow0 + r) * DV + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int e = it * C::THREADS + tid, r = e / (DQK / 4), c4 = e % (DQK / 4);
-      *(float4*)&ksm[buf][r * KS + 4 * c4] = kr[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VCH; ++it) {
-      const int e = it * C::THREADS + tid, r = e / (DV / 4), c4 = e % (DV / 4);
-      *(float4*)&vsm[buf][r * DV + 4 * c4] = vr[it];
-    }
-  };
-
-  const int my_row = row_base + qi;
-  const long long my_pos = pos_base + qi;
-  float4 acc[NV];
-  float m = kNegInf, l = 0.f;
-#pragma unroll
-  for (int e = 0; e < NV; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (MODE == F32_STEP && my_row < row_end) {
-    const size_t r = (size_t)bh * a.q_rows + my_row;
-    const float lin = a.lse_acc[r];
-    if (lin != kNegInf) {
-      m = lin * kLog2e;
-      l = 1.f;
-#pragma unroll
-      for (int e = 0; e < NV; ++e) acc[e] = *(const float4*)(a.o_acc + r * DV + 64 * e + 4 * j);
-    }
-  }
-
-  int krow0, nvalid;
-  long long kpos0;
-  tile_at(0, krow0, kpos0, nvalid);
-  load_tile(krow0, nvalid);
-  store_tile(0);
-  __syncthreads();   // Q and the first K/V tile are in LDS
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    const long long kpos_cur = kpos0;
-    const int nvalid_cur = nvalid;
-    if (n + 1 < ntiles) {
-      tile_at(n + 1, krow0, kpos0, nvalid);
-      load_tile(krow0, nvalid);   // lands while this tile is computed
-    }
-
-    // scores of keys j + 16 u
-    constexpr int KPT = C::KPT;
-    float s[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) s[u] = 0.f;
-#pragma unroll 8
-    for (int d4 = 0; d4 < DQK / 4; ++d4) {
-      const float4 qv = *(const float4*)&qsm[qi * DQK + 4 * d4];
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const float4 kv = *(const float4*)&ksm[buf][(j + 16 * u) * KS + 4 * d4];
-        s[u] = fmaf(qv.x, kv.x, s[u]);
-        s[u] = fmaf(qv.y, kv.y, s[u]);
-        s[u] = fmaf(qv.z, kv.z, s[u]);
-        s[u] = fmaf(qv.w, kv.w, s[u]);
-      }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = j + 16 * u;
-      const bool ok = key < nvalid_cur && (!a.causal || kpos_cur + key <= my_pos);
-      s[u] = ok ? s[u] : kNegInf;
-      mx = fmaxf(mx, s[u]);
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-    const float mnew = fmaxf(m, mx * a.scale_log2);
-    const float muse = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = exp2_hw(m - muse);
-    m = mnew;
-    float rs = 0.f;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const float p = exp2_hw(fmaf(s[u], a.scale_log2, -muse));
-      psm[qi * PS + j + 16 * u] = p;
-      rs += p;
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) rs += shfl_xor_f(rs, o);
-    l = l * alpha + rs;
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      acc[e].x *= alpha;
-      acc[e].y *= alpha;
-      acc[e].z *= alpha;
-      acc[e].w *= alpha;
-    }
-    __syncthreads();   // the row's probabilities are in LDS
-
-    // O += P V over the tile's keys, four keys per step
-#pragma unroll 4
-    for (int c4 = 0; c4 < BK / 4; ++c4) {
-      const float4 pv = *(const float4*)&psm[qi * PS + 4 * c4];
-      const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-#pragma unroll
-        for (int e = 0; e < NV; ++e) {
-          const float4 vv = *(const float4*)&vsm[buf][(4 * c4 + e4) * DV + 64 * e + 4 * j];
-          acc[e].x = fmaf(pk[e4], vv.x, acc[e].x);
-          acc[e].y = fmaf(pk[e4], vv.y, acc[e].y);
-          acc[e].z = fmaf(pk[e4], vv.z, acc[e].z);
-          acc[e].w = fmaf(pk[e4], vv.w, acc[e].w);
-        }
-      }
-    }
-    if (n + 1 < ntiles) store_tile(buf ^ 1);   // its last readers passed the previous barrier
-    __syncthreads();   // this tile fully consumed, the next one in LDS
-  }
-
-  if (my_row < row_end) {
-    const size_t r = (size_t)bh * a.q_rows + my_row;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? (m + log2_hw(l)) * kLn2 : kNegInf;
-    float* out = MODE == F32_RING ? (float*)a.o : a.o_acc;
-#pragma unroll
-    for (int e = 0; e < NV; ++e)
-      *(float4*)(out + r * DV + 64 * e + 4 * j) = make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
-    if (j == 0) {
-      if (MODE == F32_RING)
-        a.lse[r] = lse;
-      else
-        a.lse_acc[r] = lse;
-    }
-  }
-}
-
-// Key streams, for launches too small to fill the chip: NS groups of 256 threads
-// share one query tile, group s takes key tiles s, s + NS, s + 2 NS, ... with the
-// same per-tile work as above (single-buffered LDS, the next tile prefetched in
-// registers), and the groups' running states (m, l, O) meet in LDS at the end:
-// with M the largest m, l = sum l_s 2^(m_s - M) and O = sum O_s 2^(m_s - M), the
-// merge of partial softmax states over disjoint key sets.
+// NS groups of 256 threads ("key streams") share one query tile: group s takes key
+// tiles s, s + NS, s + 2 NS, ... (single-buffered LDS, the next tile prefetched in
+// registers), and the groups' running states (m, l, O) meet in LDS at the end: with
+// M the largest m, l = sum l_s 2^(m_s - M) and O = sum O_s 2^(m_s - M), the merge of
+// partial softmax states over disjoint key sets.
 template <int DQK, int DV>
 struct F32StreamCfg {
   using C = F32Cfg<DQK, DV>;
@@ -302,7 +121,7 @@ struct F32StreamCfg {
 
 template <int DQK, int DV, int MODE>
 __global__ void __launch_bounds__((F32StreamCfg<DQK, DV>::NS * 256))
-prefill_f32_streams_kernel(PrefillArgs a) {
+prefill_f32_kernel(PrefillArgs a) {
   using C = F32Cfg<DQK, DV>;
   using SC = F32StreamCfg<DQK, DV>;
   constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV, NS = SC::NS;
@@ -530,13 +349,8 @@ static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
   const long long tiles = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (tiles < 512) {
-    // fewer query tiles than two per CU: split each tile's keys over streams
-    hipLaunchKernelGGL((prefill_f32_streams_kernel<DQK, DV, MODE>), dim3((unsigned)tiles),
-                       dim3(F32StreamCfg<DQK, DV>::NS * C::THREADS), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles), dim3(C::THREADS), 0, st, a);
-  }
+  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles),
+                     dim3(F32StreamCfg<DQK, DV>::NS * C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 

@@ -406,7 +406,7 @@ def test_fp32_backward_workload_sampled_rows_keys_and_closed_form(ra):
     That sum runs over up to n = 32768 terms in fp32, so its rounding is about
     sqrt(n) 2^-24 ~ 1e-5 of each value: the mean gate there is 5e-5 of the mean
     |reference| (and max 1e-4 of the largest)."""
-    from bench import F32_BWD as cfg
+    from bench import F32B as cfg
     S = cfg.S
     q, k, v = prefill_inputs_torch(cfg, DEV)
     o, lse = run_prefill(ra, cfg, q, k, v)

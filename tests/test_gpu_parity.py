@@ -61,12 +61,9 @@ def test_fp32_ring_ragged(ra, dims, causal, Sp, P):
               seed=11 + Sp + P)
 
 
-# fp32 launches of fewer than 512 query tiles (16 rows each) split every tile's keys
-# over 2 or 4 streams of one workgroup; the cases above take that path. These have
-# enough tiles for one stream per workgroup, with ragged query and key tiles.
-
-F32_ONE_STREAM_TILES = 512
-
+# fp32 launches with more query tiles (16 rows each) than the chip holds at once
+# (one workgroup per CU), with ragged query and key tiles: the cases above fit in one
+# round.
 
 def f32_tiles(B, Hq, rows, nparts=1):
     return B * Hq * nparts * ((rows + 15) // 16)
@@ -75,9 +72,9 @@ def f32_tiles(B, Hq, rows, nparts=1):
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
-def test_fp32_ring_one_stream_ragged(ra, dims, causal, layout):
+def test_fp32_ring_large_grid_ragged(ra, dims, causal, layout):
     B, Hq, Hkv, Sp, P = 2, 8, 2, 263, 2
-    assert f32_tiles(B, Hq, Sp, P) >= F32_ONE_STREAM_TILES
+    assert f32_tiles(B, Hq, Sp, P) > 256
     case = ring_case if layout == "contiguous" else striped_case
     case(ra, dtype="f32", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
          seed=171 + dims[0] + dims[1])
@@ -85,12 +82,11 @@ def test_fp32_ring_one_stream_ragged(ra, dims, causal, layout):
 
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
 @pytest.mark.parametrize("Sq", [520, 40])
-def test_fp32_step_chain_both_paths(ra, dims, Sq):
-    """Two causal block steps from the empty state, queries after both blocks: 520
-    query rows run one key stream per workgroup, 40 rows split the keys."""
+def test_fp32_step_chain_two_grid_sizes(ra, dims, Sq):
+    """Two causal block steps from the empty state, queries after both blocks: 528
+    query tiles (more than one round of the chip) and 48."""
     B, Hq, Hkv, Sk = 2, 8, 2, 300
     Dqk, Dv = dims
-    assert (f32_tiles(B, Hq, Sq) >= F32_ONE_STREAM_TILES) == (Sq == 520)
     q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, 2 * Sk, Dqk, Dv, seed=181 + Sq, dtype="f32")
     q_pos0 = 2 * Sk - 20
     tq, tk, tv = (to_dev(x, torch.float32) for x in (q, k, v))
