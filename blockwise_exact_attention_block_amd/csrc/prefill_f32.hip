@@ -8,14 +8,14 @@
 // this path exists for fp32 inputs, whose tolerance no bf16 matrix-core product
 // could meet.
 //
-// A workgroup owns 16 query rows and walks the keys in tiles of 64, split over NS
-// groups of 256 threads ("key streams": 4 at D_qk = D_v = 64, 2 otherwise, what
-// fits 160 KB of LDS), each taking every NS-th tile. Thread t of a group works for
-// query row t / 16 (the 16 threads of a row sit in one wave):
-//   score phase: keys (t % 16) + 16 u, u = 0..3; each step reads four
+// A workgroup owns 16 query rows and walks the keys in tiles of 64 (32 when
+// D_qk + D_v > 128), split over NS groups of 256 threads ("key streams": 4, or 2
+// for large launches at D = 128), each taking every NS-th tile. Thread t of a
+// group works for query row t / 16 (the 16 threads of a row sit in one wave):
+//   score phase: keys (t % 16) + 16 u, u < BK / 16; each step reads four
 //                consecutive d of the row's query (one broadcast 16-byte LDS read)
 //                and of each of its keys (16-byte reads of padded K rows,
-//                conflict-free), then 16 FMAs;
+//                conflict-free), then 4 FMAs per key;
 //   PV phase:    output columns 4 (t % 16) .. + 3 (and + 64 when D_v = 128); each
 //                step reads four probabilities of the row (broadcast) and, per
 //                key, four consecutive V values (16-byte reads), then 16 (32)
@@ -23,7 +23,7 @@
 // The row's 16 threads exchange the tile's max and sum with xor-shuffles inside
 // their group of 16 lanes. The next K/V tile is fetched into registers while the
 // current one is computed. At the end the groups' states are merged in LDS. Several
-// streams keep 8 or 16 waves on a CU where one 256-thread workgroup with
+// streams keep 16 waves on a CU where one 256-thread workgroup with
 // double-buffered tiles (145 KB at D = 128) kept 4, and they split a small
 // launch's key range over more waves.
 #include "common.hpp"
@@ -34,9 +34,10 @@ enum { F32_RING = 0, F32_STEP = 1 };
 
 template <int DQK, int DV>
 struct F32Cfg {
-  // 64-key tiles (128-key tiles at D = 64 measured 25 % slower on the small
-  // workloads this path serves: more registers, no shorter critical path)
-  static constexpr int BQ = 16, BK = 64, THREADS = 256;
+  // 64-key tiles at D_qk = D_v = 64, 32-key tiles otherwise (measured: at D = 64,
+  // 32-key tiles are 10-15 % slower and 128-key tiles 25 % slower; at D = 128,
+  // 32-key tiles are 1.5x faster: half the LDS and 50 fewer registers per thread)
+  static constexpr int BQ = 16, BK = DQK + DV <= 128 ? 64 : 32, THREADS = 256;
   static constexpr int KPT = BK / 16;  // keys per thread in the score phase
   static constexpr int KS = DQK + 4;   // padded K rows: 16 consecutive rows start on 16 distinct 4-bank groups
   static constexpr int PS = BK + 4;
@@ -111,19 +112,20 @@ struct F32Work {
 // registers), and the groups' running states (m, l, O) meet in LDS at the end: with
 // M the largest m, l = sum l_s 2^(m_s - M) and O = sum O_s 2^(m_s - M), the merge of
 // partial softmax states over disjoint key sets.
-template <int DQK, int DV>
+template <int DQK, int DV, int NS_>
 struct F32StreamCfg {
   using C = F32Cfg<DQK, DV>;
-  static constexpr int NS = DQK + DV <= 128 ? 4 : 2;   // what fits 160 KB of LDS
+  static constexpr int NS = NS_;
   static constexpr int KV = C::BK * C::KS + C::BK * DV;  // one stream's K and V tile
   static_assert(C::BQ * DV <= KV, "a stream's partial output fits its K / V area");
+  static_assert((C::BQ * DQK + NS * (KV + C::BQ * C::PS)) * 4 <= 160 * 1024, "LDS");
 };
 
-template <int DQK, int DV, int MODE>
-__global__ void __launch_bounds__((F32StreamCfg<DQK, DV>::NS * 256))
+template <int DQK, int DV, int MODE, int NS_>
+__global__ void __launch_bounds__(NS_ * 256)
 prefill_f32_kernel(PrefillArgs a) {
   using C = F32Cfg<DQK, DV>;
-  using SC = F32StreamCfg<DQK, DV>;
+  using SC = F32StreamCfg<DQK, DV, NS_>;
   constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV, NS = SC::NS;
   constexpr int T = C::THREADS;
   __shared__ __attribute__((aligned(16))) float qsm[BQ * DQK];
@@ -349,8 +351,17 @@ static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
   const long long tiles = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE>), dim3((unsigned)tiles),
-                     dim3(F32StreamCfg<DQK, DV>::NS * C::THREADS), 0, st, a);
+  // four key streams at D = 64 (what fits 160 KB of LDS with 64-key tiles); at
+  // D = 128 four for launches of less than two query tiles per CU, where the key
+  // range is the longer path, and two otherwise (two workgroups per CU)
+  if constexpr (DQK + DV > 128) {
+    if (tiles >= 512) {
+      hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE, 2>), dim3((unsigned)tiles), dim3(2 * C::THREADS), 0, st,
+                         a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE, 4>), dim3((unsigned)tiles), dim3(4 * C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 
