@@ -61,10 +61,14 @@ struct F32BCfg {
   static constexpr int BK = DQK + DV >= 256 ? 32 : 64;
   static constexpr int NU = BK / 16;            // keys per thread in the dQ kernel's score pass
   static constexpr int BKEY = 32;               // keys per tile (dK/dV)
+  static constexpr int BQK = 32;                // query rows per tile (dK/dV)
+  static constexpr int KK = DQK / 32, KVV = DV / 32;   // keys per thread in the dK (dV) sums
+  static constexpr int QCH2 = BQK * DQK / 4 / THREADS, OCH2 = BQK * DV / 4 / THREADS;
   // every LDS row padded by 4 floats: 16-byte reads of up to 16 rows at one column
   // start on distinct 4-bank groups
   static constexpr int QS = DQK + 4, OS = DV + 4, KS = DQK + 4, VS = DV + 4;
   static constexpr int PS = BK + 4, PS2 = BKEY + 4;
+  static_assert(QCH2 * THREADS * 4 == BQK * DQK && OCH2 * THREADS * 4 == BQK * DV, "tile split");
   static constexpr int KCH = BK * DQK / 4 / THREADS, VCH = BK * DV / 4 / THREADS;
   static constexpr int QCH = BQ * DQK / 4 / THREADS, OCH = BQ * DV / 4 / THREADS;
   static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
@@ -228,29 +232,44 @@ bwd_dq_f32_kernel(BwdArgs a) {
 
 // ---- dK, dV ---------------------------------------------------------------------------
 // One 32-key tile of one (batch, KV head): dK, dV of its keys summed over the group's
-// query heads and the query tiles that see them, added into the accumulators. The
-// workgroup's two halves of 256 threads walk alternate (head, query tile) pairs, each
-// with its own Q / dO / P / dS tiles, and add their sums through LDS at the end.
+// query heads and the query tiles (32 rows) that see them, added into the
+// accumulators. The workgroup's two halves of 256 threads walk alternate (head,
+// query tile) pairs, each with its own Q / dO / P / dS tiles, and add their sums
+// through LDS at the end.
 template <int DQK, int DV>
 struct F32KvSmem {
   using C = F32BCfg<DQK, DV>;
   // K and V rows; at the end, the second half's partial sums
   float kv[C::BKEY * (C::KS + C::VS)];
-  float q[2][C::BQ * C::QS];
-  float o[2][C::BQ * C::OS];
-  float p[2][C::BQ * C::PS2];
-  float ds[2][C::BQ * C::PS2];
-  float l2[2][C::BQ];
-  float dl[2][C::BQ];
+  float q[2][C::BQK * C::QS];
+  float o[2][C::BQK * C::OS];
+  float p[2][C::BQK * C::PS2];
+  float ds[2][C::BQK * C::PS2];
+  float l2[2][C::BQK];
+  float dl[2][C::BQK];
 };
+
+template <int N>
+__device__ __forceinline__ void lds_n(float (&x)[N], const float* p) {
+  if constexpr (N == 4) {
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else if constexpr (N == 2) {
+    const float2 v = *(const float2*)p;
+    x[0] = v.x; x[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = p[i];
+  }
+}
 
 template <int DQK, int DV>
 __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, int kt, F32KvSmem<DQK, DV>& sm) {
   using C = F32BCfg<DQK, DV>;
-  constexpr int BQ = C::BQ, BKEY = C::BKEY, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS2 = C::PS2;
+  constexpr int BQ = C::BQK, BKEY = C::BKEY, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS2 = C::PS2;
   constexpr int T = C::THREADS;   // threads per half
-  constexpr int MK = DQK / 32, MV = DV / 32;
-  static_assert(T * (MK + MV) * 16 <= BKEY * (KS + VS) * 4, "partial sums fit the K / V area");
+  constexpr int KK = C::KK, KVV = C::KVV;
+  static_assert(T * (KK + KVV) * 16 <= BKEY * (KS + VS) * 4, "partial sums fit the K / V area");
   const int tid = threadIdx.x, half = tid / T, lt = tid % T;
   const int key_base = kt * BKEY;
   int q_first = 0;   // the first query that can see the tile's first key
@@ -283,26 +302,28 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
-  // phase 1: key kk1 = t % 32 against rows r1 and r1 + 8; phase 2: key kk2 = t / 8,
-  // columns 4 c2 + 32 m (t: the thread's index in its half)
-  const int kk1 = lt & 31, r1 = lt >> 5;
-  const int kk2 = lt >> 3, c2 = lt & 7;
-  const long long kpos1 = a.k_pos0 + key_base + kk1;
-  const bool key1_ok = key_base + kk1 < a.Sk;
-  float4 acck[MK], accv[MV];
+  // phase 1 (P, dS): keys kp, kp + 16 against rows rq, rq + 16, kp = t % 16,
+  // rq = t / 16. Phase 2: dK columns 4 (t % (DQK/4)) .. + 3 of keys KK (t / (DQK/4))
+  // .. + KK - 1, and dV likewise (t: the thread's index in its half).
+  const int kp = lt & 15, rq = lt >> 4;
+  const int cgk = lt % (DQK / 4), kgk = lt / (DQK / 4);
+  const int cgv = lt % (DV / 4), kgv = lt / (DV / 4);
+  const long long kpos_a = a.k_pos0 + key_base + kp;
+  const bool key_a_ok = key_base + kp < a.Sk, key_b_ok = key_base + kp + 16 < a.Sk;
+  float4 acck[KK], accv[KVV];
 #pragma unroll
-  for (int m = 0; m < MK; ++m) acck[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int m = 0; m < KK; ++m) acck[m] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int m = 0; m < MV; ++m) accv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int m = 0; m < KVV; ++m) accv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   // the half's next (head, query tile): rows and statistics fetched one step ahead
-  float4 qr[C::QCH], orr[C::OCH];
+  float4 qr[C::QCH2], orr[C::OCH2];
   float l2n = kNegInf, dln = 0.f;
   auto fetch = [&](int n) {
     const int hq = g * a.group + n / nqt, row0 = (qt0 + n % nqt) * BQ;
     const size_t bh = (size_t)b * a.Hq + hq;
-    load_rows<DQK, C::QCH, T>(qr, (const float*)a.q + bh * a.Sq * DQK, row0, a.Sq, lt);
-    load_rows<DV, C::OCH, T>(orr, (const float*)a.dout + bh * a.Sq * DV, row0, a.Sq, lt);
+    load_rows<DQK, C::QCH2, T>(qr, (const float*)a.q + bh * a.Sq * DQK, row0, a.Sq, lt);
+    load_rows<DV, C::OCH2, T>(orr, (const float*)a.dout + bh * a.Sq * DV, row0, a.Sq, lt);
     if (lt < BQ) {
       // -LSE * log2(e) of each row (-inf past the block or with no visible key: P = 0)
       const int row = row0 + lt;
@@ -322,8 +343,8 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
     const int row0 = (qt0 + n % nqt) * BQ;
     __syncthreads();   // the previous pair's rows, P and dS are consumed
     if (active) {
-      store_rows<DQK, C::QCH, T, QS>(qr, qsm, lt);
-      store_rows<DV, C::OCH, T, OS>(orr, osm, lt);
+      store_rows<DQK, C::QCH2, T, QS>(qr, qsm, lt);
+      store_rows<DV, C::OCH2, T, OS>(orr, osm, lt);
       if (lt < BQ) {
         sm.l2[half][lt] = l2n;
         sm.dl[half][lt] = dln;
@@ -332,38 +353,57 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
     __syncthreads();   // the pair's rows and statistics (and the K, V rows) are in LDS
     if (n + 2 < ntiles) fetch(n + 2);   // lands while this pair is computed
     if (active) {
-      float s0 = 0.f, s1 = 0.f, p0 = 0.f, p1 = 0.f;
+      float s00 = 0.f, s01 = 0.f, s10 = 0.f, s11 = 0.f;   // s[row][key]
 #pragma unroll 4
       for (int d4 = 0; d4 < DQK / 4; ++d4) {
-        const float4 kx = lds4(&ksm[kk1 * KS + 4 * d4]);
-        s0 = dot4(lds4(&qsm[r1 * QS + 4 * d4]), kx, s0);
-        s1 = dot4(lds4(&qsm[(r1 + 8) * QS + 4 * d4]), kx, s1);
+        const float4 k0 = lds4(&ksm[kp * KS + 4 * d4]), k1 = lds4(&ksm[(kp + 16) * KS + 4 * d4]);
+        const float4 q0 = lds4(&qsm[rq * QS + 4 * d4]), q1 = lds4(&qsm[(rq + 16) * QS + 4 * d4]);
+        s00 = dot4(q0, k0, s00);
+        s01 = dot4(q0, k1, s01);
+        s10 = dot4(q1, k0, s10);
+        s11 = dot4(q1, k1, s11);
       }
+      float p00 = 0.f, p01 = 0.f, p10 = 0.f, p11 = 0.f;   // dP[row][key]
 #pragma unroll 4
       for (int d4 = 0; d4 < DV / 4; ++d4) {
-        const float4 vx = lds4(&vsm[kk1 * VS + 4 * d4]);
-        p0 = dot4(lds4(&osm[r1 * OS + 4 * d4]), vx, p0);
-        p1 = dot4(lds4(&osm[(r1 + 8) * OS + 4 * d4]), vx, p1);
+        const float4 v0 = lds4(&vsm[kp * VS + 4 * d4]), v1 = lds4(&vsm[(kp + 16) * VS + 4 * d4]);
+        const float4 o0 = lds4(&osm[rq * OS + 4 * d4]), o1 = lds4(&osm[(rq + 16) * OS + 4 * d4]);
+        p00 = dot4(o0, v0, p00);
+        p01 = dot4(o0, v1, p01);
+        p10 = dot4(o1, v0, p10);
+        p11 = dot4(o1, v1, p11);
       }
-      const long long qpos = a.q_pos0 + row0 + r1;
-      const bool vis0 = key1_ok && (!a.causal || kpos1 <= qpos);
-      const bool vis1 = key1_ok && (!a.causal || kpos1 <= qpos + 8);
-      const float pa = vis0 ? exp2_hw(fmaf(s0, a.scale_log2, sm.l2[half][r1])) : 0.f;
-      const float pb = vis1 ? exp2_hw(fmaf(s1, a.scale_log2, sm.l2[half][r1 + 8])) : 0.f;
-      psm[r1 * PS2 + kk1] = pa;
-      psm[(r1 + 8) * PS2 + kk1] = pb;
-      dssm[r1 * PS2 + kk1] = pa * (p0 - sm.dl[half][r1]);
-      dssm[(r1 + 8) * PS2 + kk1] = pb * (p1 - sm.dl[half][r1 + 8]);
+      const long long qpos = a.q_pos0 + row0 + rq;
+      const float l0 = sm.l2[half][rq], l1 = sm.l2[half][rq + 16];
+      const float dl0 = sm.dl[half][rq], dl1 = sm.dl[half][rq + 16];
+      auto prob = [&](float sv, bool ok, long long kpos, long long qp, float l) {
+        return ok && (!a.causal || kpos <= qp) ? exp2_hw(fmaf(sv, a.scale_log2, l)) : 0.f;
+      };
+      const float pa0 = prob(s00, key_a_ok, kpos_a, qpos, l0), pb0 = prob(s01, key_b_ok, kpos_a + 16, qpos, l0);
+      const float pa1 = prob(s10, key_a_ok, kpos_a, qpos + 16, l1);
+      const float pb1 = prob(s11, key_b_ok, kpos_a + 16, qpos + 16, l1);
+      psm[rq * PS2 + kp] = pa0;
+      psm[rq * PS2 + kp + 16] = pb0;
+      psm[(rq + 16) * PS2 + kp] = pa1;
+      psm[(rq + 16) * PS2 + kp + 16] = pb1;
+      dssm[rq * PS2 + kp] = pa0 * (p00 - dl0);
+      dssm[rq * PS2 + kp + 16] = pb0 * (p01 - dl0);
+      dssm[(rq + 16) * PS2 + kp] = pa1 * (p10 - dl1);
+      dssm[(rq + 16) * PS2 + kp + 16] = pb1 * (p11 - dl1);
     }
     __syncthreads();   // P and dS of the pair are in LDS
     if (active) {
 #pragma unroll 2
       for (int rr = 0; rr < BQ; ++rr) {
-        const float p = psm[rr * PS2 + kk2], ds = dssm[rr * PS2 + kk2];
+        float ds[KK], p[KVV];
+        lds_n<KK>(ds, &dssm[rr * PS2 + KK * kgk]);
+        lds_n<KVV>(p, &psm[rr * PS2 + KVV * kgv]);
+        const float4 qx = lds4(&qsm[rr * QS + 4 * cgk]);
+        const float4 ox = lds4(&osm[rr * OS + 4 * cgv]);
 #pragma unroll
-        for (int m = 0; m < MV; ++m) axpy4(p, lds4(&osm[rr * OS + 32 * m + 4 * c2]), accv[m]);
+        for (int m = 0; m < KK; ++m) axpy4(ds[m], qx, acck[m]);
 #pragma unroll
-        for (int m = 0; m < MK; ++m) axpy4(ds, lds4(&qsm[rr * QS + 32 * m + 4 * c2]), acck[m]);
+        for (int m = 0; m < KVV; ++m) axpy4(p[m], ox, accv[m]);
       }
     }
   }
@@ -373,36 +413,41 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
   __syncthreads();   // every read of K and V is done
   if (half == 1) {
 #pragma unroll
-    for (int m = 0; m < MK; ++m) red[m * T + lt] = acck[m];
+    for (int m = 0; m < KK; ++m) red[m * T + lt] = acck[m];
 #pragma unroll
-    for (int m = 0; m < MV; ++m) red[(MK + m) * T + lt] = accv[m];
+    for (int m = 0; m < KVV; ++m) red[(KK + m) * T + lt] = accv[m];
   }
   __syncthreads();
-  const int key = key_base + kk2;
-  if (half == 0 && key < a.Sk) {
-    float* dkp = a.dk + (kvh + key) * DQK;
-    float* dvp = a.dv + (kvh + key) * DV;
+  if (half == 0) {
 #pragma unroll
-    for (int m = 0; m < MK; ++m) {
-      const float4 o2 = red[m * T + lt];
-      float4 sum = acck[m];
-      sum.x += o2.x;
-      sum.y += o2.y;
-      sum.z += o2.z;
-      sum.w += o2.w;
-      float4 cur = *(const float4*)(dkp + 32 * m + 4 * c2);
-      axpy4(a.scale, sum, cur);
-      *(float4*)(dkp + 32 * m + 4 * c2) = cur;
+    for (int m = 0; m < KK; ++m) {
+      const int key = key_base + KK * kgk + m;
+      if (key < a.Sk) {
+        const float4 o2 = red[m * T + lt];
+        float4 sum = acck[m];
+        sum.x += o2.x;
+        sum.y += o2.y;
+        sum.z += o2.z;
+        sum.w += o2.w;
+        float* dkp = a.dk + (kvh + key) * DQK + 4 * cgk;
+        float4 cur = *(const float4*)dkp;
+        axpy4(a.scale, sum, cur);
+        *(float4*)dkp = cur;
+      }
     }
 #pragma unroll
-    for (int m = 0; m < MV; ++m) {
-      const float4 o2 = red[(MK + m) * T + lt];
-      float4 cur = *(const float4*)(dvp + 32 * m + 4 * c2);
-      cur.x += accv[m].x + o2.x;
-      cur.y += accv[m].y + o2.y;
-      cur.z += accv[m].z + o2.z;
-      cur.w += accv[m].w + o2.w;
-      *(float4*)(dvp + 32 * m + 4 * c2) = cur;
+    for (int m = 0; m < KVV; ++m) {
+      const int key = key_base + KVV * kgv + m;
+      if (key < a.Sk) {
+        const float4 o2 = red[(KK + m) * T + lt];
+        float* dvp = a.dv + (kvh + key) * DV + 4 * cgv;
+        float4 cur = *(const float4*)dvp;
+        cur.x += accv[m].x + o2.x;
+        cur.y += accv[m].y + o2.y;
+        cur.z += accv[m].z + o2.z;
+        cur.w += accv[m].w + o2.w;
+        *(float4*)dvp = cur;
+      }
     }
   }
 }
