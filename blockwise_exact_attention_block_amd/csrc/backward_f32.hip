@@ -13,20 +13,22 @@
 //
 // Three kernels:
 //   * bwd_delta_f32_kernel: delta per query row, 16 lanes per row.
-//   * bwd_dq_f32_kernel (256 threads): 16 query rows of one (batch, head) per
-//     workgroup, key tiles of 64 (32 when D_qk + D_v = 256) in LDS, the next tile
-//     prefetched into registers. Thread t serves row t / 16: first the scores and dP
-//     of keys (t % 16) + 16 u, each Q and dO chunk read once for all of them, whose
-//     dS go to LDS; then dQ columns 64 e + 4 (t % 16) .. + 3 summed over the keys.
+//   * bwd_dq_f32_kernel (256 threads): 32 query rows of one (batch, head) per
+//     workgroup, key tiles of 64 (D_qk = D_v = 64) or 32 in LDS, the next tile
+//     prefetched into registers. Thread t first forms S and dP for keys t % 16 + 16 u
+//     against rows t / 16 and t / 16 + 16, then accumulates dQ for D_qk / 32 rows at
+//     one group of four columns, reading their dS (stored key-major) as one vector.
 //   * bwd_dkdv_f32_kernel (512 threads): key tiles of 32 of one (batch, KV head), the
 //     tile's K and V rows in LDS; it walks the group's query heads and the visible
-//     query tiles of 16 rows, the two halves of the workgroup taking alternate ones.
-//     Thread t of a half first computes P and dS for key t % 32 and rows t / 32 and
-//     t / 32 + 8, then dV and dK columns 4 (t % 8) + 32 m of key t / 8, summed over the
-//     tile's rows; the halves' sums meet in LDS at the end. Under a causal mask a
-//     workgroup takes key tiles kt and n - 1 - kt, which balances the work.
-// LDS rows are padded by 4 floats; every sum runs in a fixed order, so results are
-// reproducible run to run.
+//     query tiles of 32 rows, the two halves of the workgroup taking alternate ones.
+//     Thread t of a half first forms P and dS for keys t % 16, t % 16 + 16 against
+//     rows t / 16, t / 16 + 16, then accumulates dK (dV) for D_qk / 32 (D_v / 32) keys
+//     at one group of four columns, reading their dS (P) as one vector; the halves'
+//     sums meet in LDS at the end. Under a causal mask a workgroup takes key tiles kt
+//     and n - 1 - kt, which balances the work.
+// Each thread works on two rows by two or more keys, so every 16-byte LDS read
+// feeds 8 or more FMAs. LDS rows are padded by 4 floats; every sum runs in a fixed
+// order, so results are reproducible run to run.
 #include "common.hpp"
 
 namespace ra {
@@ -55,24 +57,22 @@ bwd_delta_f32_kernel(const float* o, const float* dout, float* delta, long long 
 template <int DQK, int DV>
 struct F32BCfg {
   static constexpr int THREADS = 256;
-  static constexpr int BQ = 16;                 // query rows per workgroup (dQ) / per tile (dK/dV)
-  // keys per tile (dQ): 32 when the head dims sum to 256, so that two workgroups
-  // fit a CU's LDS
-  static constexpr int BK = DQK + DV >= 256 ? 32 : 64;
+  static constexpr int BQK = 32;                // query rows per tile (both kernels)
+  // keys per tile in the dQ kernel: 32 unless D_qk = D_v = 64, so that two
+  // workgroups fit a CU's LDS
+  static constexpr int BK = DQK + DV > 128 ? 32 : 64;
   static constexpr int NU = BK / 16;            // keys per thread in the dQ kernel's score pass
   static constexpr int BKEY = 32;               // keys per tile (dK/dV)
-  static constexpr int BQK = 32;                // query rows per tile (dK/dV)
-  static constexpr int KK = DQK / 32, KVV = DV / 32;   // keys per thread in the dK (dV) sums
-  static constexpr int QCH2 = BQK * DQK / 4 / THREADS, OCH2 = BQK * DV / 4 / THREADS;
+  // keys per thread in the dK (dV) sums; also rows per thread in the dQ sums
+  static constexpr int KK = DQK / 32, KVV = DV / 32;
   // every LDS row padded by 4 floats: 16-byte reads of up to 16 rows at one column
   // start on distinct 4-bank groups
   static constexpr int QS = DQK + 4, OS = DV + 4, KS = DQK + 4, VS = DV + 4;
-  static constexpr int PS = BK + 4, PS2 = BKEY + 4;
-  static_assert(QCH2 * THREADS * 4 == BQK * DQK && OCH2 * THREADS * 4 == BQK * DV, "tile split");
+  static constexpr int PS2 = BKEY + 4;
   static constexpr int KCH = BK * DQK / 4 / THREADS, VCH = BK * DV / 4 / THREADS;
-  static constexpr int QCH = BQ * DQK / 4 / THREADS, OCH = BQ * DV / 4 / THREADS;
+  static constexpr int QCH2 = BQK * DQK / 4 / THREADS, OCH2 = BQK * DV / 4 / THREADS;
   static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
-  static_assert(QCH * THREADS * 4 == BQ * DQK && OCH * THREADS * 4 == BQ * DV, "tile split");
+  static_assert(QCH2 * THREADS * 4 == BQK * DQK && OCH2 * THREADS * 4 == BQK * DV, "tile split");
   static_assert(DQK % 64 == 0 && DV % 64 == 0, "64-column groups");
 };
 
@@ -111,20 +111,40 @@ __device__ __forceinline__ void store_rows(const float4 (&r)[CH], float* lds, in
   }
 }
 
+template <int N>
+__device__ __forceinline__ void lds_n(float (&x)[N], const float* p) {
+  if constexpr (N == 4) {
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else if constexpr (N == 2) {
+    const float2 v = *(const float2*)p;
+    x[0] = v.x; x[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = p[i];
+  }
+}
+
 // ---- dQ -------------------------------------------------------------------------------
+// 32 query rows of one (batch, head) per workgroup. Score pass: keys kp + 16 u
+// (u < BK / 16) against rows rq and rq + 16 (kp = t % 16, rq = t / 16), each K / V
+// chunk read once for both rows and each Q / dO chunk once for all the keys; dS goes
+// to LDS key-major. dQ pass: rows RQ (t / (DQK/4)) .. + RQ - 1 at columns
+// 4 (t % (DQK/4)) .. + 3, one vector read of their dS and one of K per key.
 template <int DQK, int DV>
 __global__ void __launch_bounds__(256)
 bwd_dq_f32_kernel(BwdArgs a) {
   using C = F32BCfg<DQK, DV>;
-  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS = C::PS;
-  constexpr int T = C::THREADS;
+  constexpr int BQ = C::BQK, BK = C::BK, NU = C::NU, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS;
+  constexpr int T = C::THREADS, RQ = C::KK, DSS = BQ + 4;
   __shared__ __attribute__((aligned(16))) float qsm[BQ * QS];
   __shared__ __attribute__((aligned(16))) float osm[BQ * OS];
   __shared__ __attribute__((aligned(16))) float ksm[BK * KS];
   __shared__ __attribute__((aligned(16))) float vsm[BK * VS];
-  __shared__ __attribute__((aligned(16))) float dssm[BQ * PS];
+  __shared__ __attribute__((aligned(16))) float dst[BK * DSS];   // dS, key-major
 
-  const int tid = threadIdx.x, r = tid >> 4, j = tid & 15;
+  const int tid = threadIdx.x, kp = tid & 15, rq = tid >> 4;
+  const int cg = tid % (DQK / 4), rg = tid / (DQK / 4);
   // workgroup -> (batch, head, query tile), the heaviest causal tiles first
   const int qt = a.n_tiles - 1 - (int)(blockIdx.x % a.n_tiles);
   const int bh = blockIdx.x / a.n_tiles;
@@ -143,28 +163,34 @@ bwd_dq_f32_kernel(BwdArgs a) {
   const float* v_head = (const float*)a.v + kvh * DV;
 
   {
-    float4 qr[C::QCH], orr[C::OCH];
-    load_rows<DQK, C::QCH, T>(qr, q_head, row_base, a.Sq, tid);
-    load_rows<DV, C::OCH, T>(orr, o_head, row_base, a.Sq, tid);
-    store_rows<DQK, C::QCH, T, QS>(qr, qsm, tid);
-    store_rows<DV, C::OCH, T, OS>(orr, osm, tid);
+    float4 qr[C::QCH2], orr[C::OCH2];
+    load_rows<DQK, C::QCH2, T>(qr, q_head, row_base, a.Sq, tid);
+    load_rows<DV, C::OCH2, T>(orr, o_head, row_base, a.Sq, tid);
+    store_rows<DQK, C::QCH2, T, QS>(qr, qsm, tid);
+    store_rows<DV, C::OCH2, T, OS>(orr, osm, tid);
   }
-  // the row's statistics: a row past the block, or with no visible key, gets P = 0
-  const int my_row = row_base + r;
-  const long long my_pos = a.q_pos0 + my_row;
-  float lse2 = __builtin_huge_valf(), dlt = 0.f;   // +inf: exp2(s - lse2) = 0
-  if (my_row < a.Sq) {
-    const float l = a.lse[(size_t)bh * a.Sq + my_row];
-    if (l != kNegInf) lse2 = l * kLog2e;
-    dlt = a.delta[(size_t)bh * a.Sq + my_row];
+  // statistics of rows rq and rq + 16: a row past the block, or with no visible key,
+  // gets P = 0
+  float lse2[2], dlt[2];
+  long long qpos[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = row_base + rq + 16 * h;
+    qpos[h] = a.q_pos0 + row;
+    lse2[h] = __builtin_huge_valf();   // +inf: exp2(s - lse2) = 0
+    dlt[h] = 0.f;
+    if (row < a.Sq) {
+      const float l = a.lse[(size_t)bh * a.Sq + row];
+      if (l != kNegInf) lse2[h] = l * kLog2e;
+      dlt[h] = a.delta[(size_t)bh * a.Sq + row];
+    }
   }
 
   // K / V tiles: global -> registers (one tile ahead) -> LDS
   float4 kr[C::KCH], vr[C::VCH];
-  constexpr int NE = DQK / 64;
-  float4 acc[NE];
+  float4 acc[RQ];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int e = 0; e < RQ; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   load_rows<DQK, C::KCH, T>(kr, k_head, 0, a.Sk, tid);
   load_rows<DV, C::VCH, T>(vr, v_head, 0, a.Sk, tid);
@@ -178,38 +204,48 @@ bwd_dq_f32_kernel(BwdArgs a) {
       load_rows<DQK, C::KCH, T>(kr, k_head, (n + 1) * BK, a.Sk, tid);
       load_rows<DV, C::VCH, T>(vr, v_head, (n + 1) * BK, a.Sk, tid);
     }
-    // scores and dP of keys j + 16 u against this thread's row: each Q (dO) chunk
-    // read once for all of them
-    constexpr int NU = C::NU;
-    float s[NU], dp[NU];
+    float s[2][NU], dp[2][NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) s[u] = dp[u] = 0.f;
-#pragma unroll 4
+    for (int u = 0; u < NU; ++u) s[0][u] = s[1][u] = dp[0][u] = dp[1][u] = 0.f;
+#pragma unroll 2
     for (int d4 = 0; d4 < DQK / 4; ++d4) {
-      const float4 x = lds4(&qsm[r * QS + 4 * d4]);
+      const float4 x0 = lds4(&qsm[rq * QS + 4 * d4]), x1 = lds4(&qsm[(rq + 16) * QS + 4 * d4]);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) s[u] = dot4(x, lds4(&ksm[(j + 16 * u) * KS + 4 * d4]), s[u]);
+      for (int u = 0; u < NU; ++u) {
+        const float4 kx = lds4(&ksm[(kp + 16 * u) * KS + 4 * d4]);
+        s[0][u] = dot4(x0, kx, s[0][u]);
+        s[1][u] = dot4(x1, kx, s[1][u]);
+      }
     }
-#pragma unroll 4
+#pragma unroll 2
     for (int d4 = 0; d4 < DV / 4; ++d4) {
-      const float4 x = lds4(&osm[r * OS + 4 * d4]);
+      const float4 x0 = lds4(&osm[rq * OS + 4 * d4]), x1 = lds4(&osm[(rq + 16) * OS + 4 * d4]);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) dp[u] = dot4(x, lds4(&vsm[(j + 16 * u) * VS + 4 * d4]), dp[u]);
+      for (int u = 0; u < NU; ++u) {
+        const float4 vx = lds4(&vsm[(kp + 16 * u) * VS + 4 * d4]);
+        dp[0][u] = dot4(x0, vx, dp[0][u]);
+        dp[1][u] = dot4(x1, vx, dp[1][u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int key = j + 16 * u;
-      const bool vis = key < nvalid && (!a.causal || kpos0 + key <= my_pos);
-      const float p = vis ? exp2_hw(fmaf(s[u], a.scale_log2, -lse2)) : 0.f;
-      dssm[r * PS + key] = p * (dp[u] - dlt);
+      const int key = kp + 16 * u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool vis = key < nvalid && (!a.causal || kpos0 + key <= qpos[h]);
+        const float p = vis ? exp2_hw(fmaf(s[h][u], a.scale_log2, -lse2[h])) : 0.f;
+        dst[key * DSS + rq + 16 * h] = p * (dp[h][u] - dlt[h]);
+      }
     }
     __syncthreads();   // the tile's dS is in LDS
-    // dQ columns 64 e + 4 j .. + 3 over the tile's keys
+    // dQ rows RQ rg .. + RQ - 1, columns 4 cg .. + 3, over the tile's keys
 #pragma unroll 4
     for (int kk = 0; kk < BK; ++kk) {
-      const float ds = dssm[r * PS + kk];
+      float ds[RQ];
+      lds_n<RQ>(ds, &dst[kk * DSS + RQ * rg]);
+      const float4 kx = lds4(&ksm[kk * KS + 4 * cg]);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) axpy4(ds, lds4(&ksm[kk * KS + 64 * e + 4 * j]), acc[e]);
+      for (int e = 0; e < RQ; ++e) axpy4(ds[e], kx, acc[e]);
     }
     __syncthreads();   // K, V and dS of this tile consumed
     if (n + 1 < ntiles) {
@@ -219,13 +255,14 @@ bwd_dq_f32_kernel(BwdArgs a) {
     }
   }
 
-  if (my_row < a.Sq) {
-    float* dqp = a.dq + ((size_t)bh * a.Sq + my_row) * DQK;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float4 cur = *(const float4*)(dqp + 64 * e + 4 * j);
+  for (int e = 0; e < RQ; ++e) {
+    const int row = row_base + RQ * rg + e;
+    if (row < a.Sq) {
+      float* dqp = a.dq + ((size_t)bh * a.Sq + row) * DQK + 4 * cg;
+      float4 cur = *(const float4*)dqp;
       axpy4(a.scale, acc[e], cur);
-      *(float4*)(dqp + 64 * e + 4 * j) = cur;
+      *(float4*)dqp = cur;
     }
   }
 }
@@ -248,20 +285,6 @@ struct F32KvSmem {
   float l2[2][C::BQK];
   float dl[2][C::BQK];
 };
-
-template <int N>
-__device__ __forceinline__ void lds_n(float (&x)[N], const float* p) {
-  if constexpr (N == 4) {
-    const float4 v = *(const float4*)p;
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  } else if constexpr (N == 2) {
-    const float2 v = *(const float2*)p;
-    x[0] = v.x; x[1] = v.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = p[i];
-  }
-}
 
 template <int DQK, int DV>
 __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, int kt, F32KvSmem<DQK, DV>& sm) {
@@ -495,7 +518,7 @@ static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(2 * C::THREADS), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  b.n_tiles = (a.Sq + C::BQ - 1) / C::BQ;
+  b.n_tiles = (a.Sq + C::BQK - 1) / C::BQK;
   grid = (long long)a.B * a.Hq * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid > 0)
