@@ -8,24 +8,27 @@
 // this path exists for fp32 inputs, whose tolerance no bf16 matrix-core product
 // could meet.
 //
-// A workgroup owns 16 query rows and walks the keys in tiles of 64 (32 when
-// D_qk + D_v > 128), split over NS groups of 256 threads ("key streams": 4, or 2
-// for large launches at D = 128), each taking every NS-th tile. Thread t of a
-// group works for query row t / 16 (the 16 threads of a row sit in one wave):
+// A workgroup owns 16 R query rows (R = 1, or 2 for launches of at least 1024
+// 16-row tiles) and walks the keys in tiles of 64 (32 when D_qk + D_v > 128),
+// split over NS groups of 256 threads ("key streams": 4 for R = 1; for R = 2, 3 at
+// D = 64 and 2 at D = 128), each taking every NS-th tile. Thread t of a group
+// works for rows t / 16 + 16 r, r < R (the 16 threads of a row group sit in one
+// wave):
 //   score phase: keys (t % 16) + 16 u, u < BK / 16; each step reads four
-//                consecutive d of the row's query (one broadcast 16-byte LDS read)
-//                and of each of its keys (16-byte reads of padded K rows,
-//                conflict-free), then 4 FMAs per key;
+//                consecutive d of the rows' queries (broadcast 16-byte LDS reads
+//                of padded rows) and of each of its keys (16-byte reads of padded
+//                K rows, conflict-free), then 4 R FMAs per key;
 //   PV phase:    output columns 4 (t % 16) .. + 3 (and + 64 when D_v = 128); each
-//                step reads four probabilities of the row (broadcast) and, per
-//                key, four consecutive V values (16-byte reads), then 16 (32)
-//                FMAs.
+//                step reads four probabilities of each row (broadcast) and, per
+//                key, four consecutive V values (16-byte reads), then 4 R FMAs per
+//                key and column group.
 // The row's 16 threads exchange the tile's max and sum with xor-shuffles inside
 // their group of 16 lanes. The next K/V tile is fetched into registers while the
 // current one is computed. At the end the groups' states are merged in LDS. Several
-// streams keep 16 waves on a CU where one 256-thread workgroup with
+// streams keep 8 to 16 waves on a CU where one 256-thread workgroup with
 // double-buffered tiles (145 KB at D = 128) kept 4, and they split a small
-// launch's key range over more waves.
+// launch's key range over more waves; two rows per thread halve the K and V reads
+// per FMA where the launch has the workgroups to spare.
 #include "common.hpp"
 
 namespace ra {
@@ -40,6 +43,7 @@ struct F32Cfg {
   static constexpr int BQ = 16, BK = DQK + DV <= 128 ? 64 : 32, THREADS = 256;
   static constexpr int KPT = BK / 16;  // keys per thread in the score phase
   static constexpr int KS = DQK + 4;   // padded K rows: 16 consecutive rows start on 16 distinct 4-bank groups
+  static constexpr int QS = DQK + 4;   // padded Q rows: a wave's four rows start on distinct 4-bank groups
   static constexpr int PS = BK + 4;
   static constexpr int NV = DV / 64;   // float4 output groups per thread
   static constexpr int KCH = BK * DQK / 4 / THREADS;   // float4 K loads per thread per tile
@@ -112,28 +116,32 @@ struct F32Work {
 // registers), and the groups' running states (m, l, O) meet in LDS at the end: with
 // M the largest m, l = sum l_s 2^(m_s - M) and O = sum O_s 2^(m_s - M), the merge of
 // partial softmax states over disjoint key sets.
-template <int DQK, int DV, int NS_>
+template <int DQK, int DV, int NS_, int R_>
 struct F32StreamCfg {
   using C = F32Cfg<DQK, DV>;
-  static constexpr int NS = NS_;
+  static constexpr int NS = NS_, R = R_;
+  static constexpr int BQ = 16 * R;                      // query rows per workgroup
   static constexpr int KV = C::BK * C::KS + C::BK * DV;  // one stream's K and V tile
-  static_assert(C::BQ * DV <= KV, "a stream's partial output fits its K / V area");
-  static_assert((C::BQ * DQK + NS * (KV + C::BQ * C::PS)) * 4 <= 160 * 1024, "LDS");
+  static_assert(BQ * DV <= KV, "a stream's partial output fits its K / V area");
+  static_assert((BQ * C::QS + NS * (KV + BQ * C::PS)) * 4 <= 160 * 1024, "LDS");
 };
 
-template <int DQK, int DV, int MODE, int NS_>
+// R rows per thread: the 16 threads of row group qi serve rows qi + 16 r, r < R, so
+// every K (V) chunk read from LDS feeds R rows.
+template <int DQK, int DV, int MODE, int NS_, int R_>
 __global__ void __launch_bounds__(NS_ * 256)
 prefill_f32_kernel(PrefillArgs a) {
   using C = F32Cfg<DQK, DV>;
-  using SC = F32StreamCfg<DQK, DV, NS_>;
-  constexpr int BQ = C::BQ, BK = C::BK, KS = C::KS, PS = C::PS, NV = C::NV, NS = SC::NS;
+  using SC = F32StreamCfg<DQK, DV, NS_, R_>;
+  constexpr int BK = C::BK, KS = C::KS, QS = C::QS, PS = C::PS, NV = C::NV, NS = SC::NS, R = SC::R;
+  constexpr int BQ = SC::BQ, KPT = C::KPT;
   constexpr int T = C::THREADS;
-  __shared__ __attribute__((aligned(16))) float qsm[BQ * DQK];
+  __shared__ __attribute__((aligned(16))) float qsm[BQ * QS];
   __shared__ __attribute__((aligned(16))) float kvsm[NS][SC::KV];
   __shared__ __attribute__((aligned(16))) float psm[NS][BQ * PS];
 
   const int tid = threadIdx.x, st = tid / T, lt = tid % T;
-  const int qi = lt >> 4;   // query row inside the tile
+  const int qi = lt >> 4;   // row group: rows qi + 16 r of the tile
   const int j = lt & 15;
   float* ksm = kvsm[st];
   float* vsm = kvsm[st] + BK * KS;
@@ -151,7 +159,7 @@ prefill_f32_kernel(PrefillArgs a) {
     const int row = row_base + r;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row < row_end) x = *(const float4*)(q_head + (size_t)row * DQK + 4 * c4);
-    *(float4*)&qsm[r * DQK + 4 * c4] = x;
+    *(float4*)&qsm[r * QS + 4 * c4] = x;
   }
 
   float4 kr[C::KCH], vr[C::VCH];
@@ -180,21 +188,27 @@ prefill_f32_kernel(PrefillArgs a) {
     }
   };
 
-  const int my_row = row_base + qi;
-  const long long my_pos = w.pos_base + qi;
-  float4 acc[NV];
-  float m = kNegInf, l = 0.f;
+  float4 acc[R][NV];
+  float m[R], l[R];
+  long long my_pos[R];
 #pragma unroll
-  for (int e = 0; e < NV; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (MODE == F32_STEP && st == 0 && my_row < row_end) {
-    // the running state enters through the first stream
-    const size_t r = (size_t)bh * a.q_rows + my_row;
-    const float lin = a.lse_acc[r];
-    if (lin != kNegInf) {
-      m = lin * kLog2e;
-      l = 1.f;
+  for (int h = 0; h < R; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+    my_pos[h] = w.pos_base + qi + 16 * h;
 #pragma unroll
-      for (int e = 0; e < NV; ++e) acc[e] = *(const float4*)(a.o_acc + r * DV + 64 * e + 4 * j);
+    for (int e = 0; e < NV; ++e) acc[h][e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int my_row = row_base + qi + 16 * h;
+    if (MODE == F32_STEP && st == 0 && my_row < row_end) {
+      // the running state enters through the first stream
+      const size_t r = (size_t)bh * a.q_rows + my_row;
+      const float lin = a.lse_acc[r];
+      if (lin != kNegInf) {
+        m[h] = lin * kLog2e;
+        l[h] = 1.f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[h][e] = *(const float4*)(a.o_acc + r * DV + 64 * e + 4 * j);
+      }
     }
   }
 
@@ -217,71 +231,94 @@ prefill_f32_kernel(PrefillArgs a) {
       w.tile_at(n + NS, krow0, kpos0, nvalid);
       load_tile(krow0, nvalid);   // lands while this tile is computed
     }
-    float alpha = 1.f;
-    if (active) {
-      constexpr int KPT = C::KPT;
-      float s[KPT];
+    float alpha[R];
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) s[u] = 0.f;
-#pragma unroll 8
+    for (int h = 0; h < R; ++h) alpha[h] = 1.f;
+    if (active) {
+      float s[R][KPT];
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) s[h][u] = 0.f;
+#pragma unroll 4
       for (int d4 = 0; d4 < DQK / 4; ++d4) {
-        const float4 qv = *(const float4*)&qsm[qi * DQK + 4 * d4];
+        float4 qv[R];
+#pragma unroll
+        for (int h = 0; h < R; ++h) qv[h] = *(const float4*)&qsm[(qi + 16 * h) * QS + 4 * d4];
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
           const float4 kv = *(const float4*)&ksm[(j + 16 * u) * KS + 4 * d4];
-          s[u] = fmaf(qv.x, kv.x, s[u]);
-          s[u] = fmaf(qv.y, kv.y, s[u]);
-          s[u] = fmaf(qv.z, kv.z, s[u]);
-          s[u] = fmaf(qv.w, kv.w, s[u]);
+#pragma unroll
+          for (int h = 0; h < R; ++h) {
+            s[h][u] = fmaf(qv[h].x, kv.x, s[h][u]);
+            s[h][u] = fmaf(qv[h].y, kv.y, s[h][u]);
+            s[h][u] = fmaf(qv[h].z, kv.z, s[h][u]);
+            s[h][u] = fmaf(qv[h].w, kv.w, s[h][u]);
+          }
         }
       }
-      float mx = kNegInf;
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int key = j + 16 * u;
-        const bool ok = key < nvalid_cur && (!a.causal || kpos_cur + key <= my_pos);
-        s[u] = ok ? s[u] : kNegInf;
-        mx = fmaxf(mx, s[u]);
+      for (int h = 0; h < R; ++h) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const int key = j + 16 * u;
+          const bool ok = key < nvalid_cur && (!a.causal || kpos_cur + key <= my_pos[h]);
+          s[h][u] = ok ? s[h][u] : kNegInf;
+          mx = fmaxf(mx, s[h][u]);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+        const float mnew = fmaxf(m[h], mx * a.scale_log2);
+        const float muse = mnew == kNegInf ? 0.f : mnew;
+        alpha[h] = exp2_hw(m[h] - muse);
+        m[h] = mnew;
+        float rs = 0.f;
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const float p = exp2_hw(fmaf(s[h][u], a.scale_log2, -muse));
+          prow[(qi + 16 * h) * PS + j + 16 * u] = p;
+          rs += p;
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) rs += shfl_xor_f(rs, o);
+        l[h] = l[h] * alpha[h] + rs;
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-      const float mnew = fmaxf(m, mx * a.scale_log2);
-      const float muse = mnew == kNegInf ? 0.f : mnew;
-      alpha = exp2_hw(m - muse);
-      m = mnew;
-      float rs = 0.f;
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const float p = exp2_hw(fmaf(s[u], a.scale_log2, -muse));
-        prow[qi * PS + j + 16 * u] = p;
-        rs += p;
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) rs += shfl_xor_f(rs, o);
-      l = l * alpha + rs;
     }
     __syncthreads();   // the rows' probabilities are in LDS
     if (active) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) {
-        acc[e].x *= alpha;
-        acc[e].y *= alpha;
-        acc[e].z *= alpha;
-        acc[e].w *= alpha;
-      }
-#pragma unroll 4
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          acc[h][e].x *= alpha[h];
+          acc[h][e].y *= alpha[h];
+          acc[h][e].z *= alpha[h];
+          acc[h][e].w *= alpha[h];
+        }
+#pragma unroll 2
       for (int c4 = 0; c4 < BK / 4; ++c4) {
-        const float4 pv = *(const float4*)&prow[qi * PS + 4 * c4];
-        const float pk[4] = {pv.x, pv.y, pv.z, pv.w};
+        float pk[R][4];
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          const float4 pv = *(const float4*)&prow[(qi + 16 * h) * PS + 4 * c4];
+          pk[h][0] = pv.x;
+          pk[h][1] = pv.y;
+          pk[h][2] = pv.z;
+          pk[h][3] = pv.w;
+        }
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
 #pragma unroll
           for (int e = 0; e < NV; ++e) {
             const float4 vv = *(const float4*)&vsm[(4 * c4 + e4) * DV + 64 * e + 4 * j];
-            acc[e].x = fmaf(pk[e4], vv.x, acc[e].x);
-            acc[e].y = fmaf(pk[e4], vv.y, acc[e].y);
-            acc[e].z = fmaf(pk[e4], vv.z, acc[e].z);
-            acc[e].w = fmaf(pk[e4], vv.w, acc[e].w);
+#pragma unroll
+            for (int h = 0; h < R; ++h) {
+              acc[h][e].x = fmaf(pk[h][e4], vv.x, acc[h][e].x);
+              acc[h][e].y = fmaf(pk[h][e4], vv.y, acc[h][e].y);
+              acc[h][e].z = fmaf(pk[h][e4], vv.z, acc[h][e].z);
+              acc[h][e].w = fmaf(pk[h][e4], vv.w, acc[h][e].w);
+            }
           }
         }
       }
@@ -293,76 +330,90 @@ prefill_f32_kernel(PrefillArgs a) {
   if (st > 0) {
     float* ob = kvsm[st];
 #pragma unroll
-    for (int e = 0; e < NV; ++e) *(float4*)&ob[qi * DV + 64 * e + 4 * j] = acc[e];
-    if (j == 0) {
-      psm[st][2 * qi] = m;
-      psm[st][2 * qi + 1] = l;
+    for (int h = 0; h < R; ++h) {
+      const int row = qi + 16 * h;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) *(float4*)&ob[row * DV + 64 * e + 4 * j] = acc[h][e];
+      if (j == 0) {
+        psm[st][2 * row] = m[h];
+        psm[st][2 * row + 1] = l[h];
+      }
     }
   }
   __syncthreads();
-  if (st == 0 && my_row < row_end) {
-    float M = m;
+  if (st == 0) {
 #pragma unroll
-    for (int t = 1; t < NS; ++t) M = fmaxf(M, psm[t][2 * qi]);
-    const float wown = m == kNegInf ? 0.f : exp2_hw(m - M);
-    l *= wown;
+    for (int h = 0; h < R; ++h) {
+      const int row = qi + 16 * h, my_row = row_base + row;
+      if (my_row >= row_end) continue;
+      float M = m[h];
 #pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      acc[e].x *= wown;
-      acc[e].y *= wown;
-      acc[e].z *= wown;
-      acc[e].w *= wown;
-    }
-#pragma unroll
-    for (int t = 1; t < NS; ++t) {
-      const float mt = psm[t][2 * qi];
-      const float wt = mt == kNegInf ? 0.f : exp2_hw(mt - M);
-      l = fmaf(psm[t][2 * qi + 1], wt, l);
+      for (int t = 1; t < NS; ++t) M = fmaxf(M, psm[t][2 * row]);
+      const float wown = m[h] == kNegInf ? 0.f : exp2_hw(m[h] - M);
+      float lt_sum = l[h] * wown;
+      float4 o4[NV];
 #pragma unroll
       for (int e = 0; e < NV; ++e) {
-        const float4 o = *(const float4*)&kvsm[t][qi * DV + 64 * e + 4 * j];
-        acc[e].x = fmaf(o.x, wt, acc[e].x);
-        acc[e].y = fmaf(o.y, wt, acc[e].y);
-        acc[e].z = fmaf(o.z, wt, acc[e].z);
-        acc[e].w = fmaf(o.w, wt, acc[e].w);
+        o4[e].x = acc[h][e].x * wown;
+        o4[e].y = acc[h][e].y * wown;
+        o4[e].z = acc[h][e].z * wown;
+        o4[e].w = acc[h][e].w * wown;
       }
-    }
-    const size_t r = (size_t)bh * a.q_rows + my_row;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? (M + log2_hw(l)) * kLn2 : kNegInf;
-    float* out = MODE == F32_RING ? (float*)a.o : a.o_acc;
 #pragma unroll
-    for (int e = 0; e < NV; ++e)
-      *(float4*)(out + r * DV + 64 * e + 4 * j) = make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
-    if (j == 0) {
-      if (MODE == F32_RING)
-        a.lse[r] = lse;
-      else
-        a.lse_acc[r] = lse;
+      for (int t = 1; t < NS; ++t) {
+        const float mt = psm[t][2 * row];
+        const float wt = mt == kNegInf ? 0.f : exp2_hw(mt - M);
+        lt_sum = fmaf(psm[t][2 * row + 1], wt, lt_sum);
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const float4 o = *(const float4*)&kvsm[t][row * DV + 64 * e + 4 * j];
+          o4[e].x = fmaf(o.x, wt, o4[e].x);
+          o4[e].y = fmaf(o.y, wt, o4[e].y);
+          o4[e].z = fmaf(o.z, wt, o4[e].z);
+          o4[e].w = fmaf(o.w, wt, o4[e].w);
+        }
+      }
+      const size_t r = (size_t)bh * a.q_rows + my_row;
+      const float inv = lt_sum > 0.f ? 1.f / lt_sum : 0.f;
+      const float lse = lt_sum > 0.f ? (M + log2_hw(lt_sum)) * kLn2 : kNegInf;
+      float* out = MODE == F32_RING ? (float*)a.o : a.o_acc;
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        *(float4*)(out + r * DV + 64 * e + 4 * j) = make_float4(o4[e].x * inv, o4[e].y * inv, o4[e].z * inv,
+                                                                o4[e].w * inv);
+      if (j == 0) {
+        if (MODE == F32_RING)
+          a.lse[r] = lse;
+        else
+          a.lse_acc[r] = lse;
+      }
     }
   }
 }
 
-template <int DQK, int DV, int MODE>
-static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
-  using C = F32Cfg<DQK, DV>;
+template <int DQK, int DV, int MODE, int NS, int R>
+static hipError_t launch_f32_as(PrefillArgs a, hipStream_t st) {
   const int rows_per_part = MODE == F32_RING ? a.Sp : a.q_rows;
-  a.n_qtiles = (rows_per_part + C::BQ - 1) / C::BQ;
+  a.n_qtiles = (rows_per_part + 16 * R - 1) / (16 * R);
   const long long tiles = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * a.n_qtiles;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  // four key streams at D = 64 (what fits 160 KB of LDS with 64-key tiles); at
-  // D = 128 four for launches of less than two query tiles per CU, where the key
-  // range is the longer path, and two otherwise (two workgroups per CU)
-  if constexpr (DQK + DV > 128) {
-    if (tiles >= 512) {
-      hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE, 2>), dim3((unsigned)tiles), dim3(2 * C::THREADS), 0, st,
-                         a);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE, 4>), dim3((unsigned)tiles), dim3(4 * C::THREADS), 0, st, a);
+  hipLaunchKernelGGL((prefill_f32_kernel<DQK, DV, MODE, NS, R>), dim3((unsigned)tiles), dim3(NS * 256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DQK, int DV, int MODE>
+static hipError_t launch_f32(PrefillArgs a, hipStream_t st) {
+  const int rows_per_part = MODE == F32_RING ? a.Sp : a.q_rows;
+  const long long tiles16 = (long long)a.B * a.Hq * (MODE == F32_RING ? a.nq : 1) * ((rows_per_part + 15) / 16);
+  // Launches of fewer than 1024 16-row tiles split each tile's keys over four
+  // streams; larger ones (two or more 32-row workgroups per CU) take two rows per
+  // thread with three streams at D = 64 and two at D = 128, what fits 160 KB of LDS.
+  if (tiles16 < 1024) return launch_f32_as<DQK, DV, MODE, 4, 1>(a, st);
+  if constexpr (DQK + DV <= 128)
+    return launch_f32_as<DQK, DV, MODE, 3, 2>(a, st);
+  else
+    return launch_f32_as<DQK, DV, MODE, 2, 2>(a, st);
 }
 
 hipError_t prefill_f32(const PrefillArgs& a, int dqk, int dv, int step_mode, hipStream_t st) {

@@ -61,9 +61,9 @@ def test_fp32_ring_ragged(ra, dims, causal, Sp, P):
               seed=11 + Sp + P)
 
 
-# fp32 launches with more query tiles (16 rows each) than the chip holds at once
-# (one workgroup per CU), with ragged query and key tiles: the cases above fit in one
-# round.
+# fp32 launches of at least 1024 16-row query tiles take two rows per thread (32-row
+# workgroups); smaller ones (the cases above) split the keys over four streams.
+# These have ragged 16- and 32-row tiles and ragged key tiles.
 
 def f32_tiles(B, Hq, rows, nparts=1):
     return B * Hq * nparts * ((rows + 15) // 16)
@@ -73,20 +73,22 @@ def f32_tiles(B, Hq, rows, nparts=1):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
 def test_fp32_ring_large_grid_ragged(ra, dims, causal, layout):
-    B, Hq, Hkv, Sp, P = 2, 8, 2, 263, 2
-    assert f32_tiles(B, Hq, Sp, P) > 256
+    B, Hq, Hkv, Sp, P = 2, 8, 2, 520, 2
+    assert f32_tiles(B, Hq, Sp, P) >= 1024
     case = ring_case if layout == "contiguous" else striped_case
     case(ra, dtype="f32", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
          seed=171 + dims[0] + dims[1])
 
 
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
-@pytest.mark.parametrize("Sq", [520, 40])
-def test_fp32_step_chain_two_grid_sizes(ra, dims, Sq):
-    """Two causal block steps from the empty state, queries after both blocks: 528
-    query tiles (more than one round of the chip) and 48."""
+@pytest.mark.parametrize("Sq", [1040, 520, 40])
+def test_fp32_step_chain_three_grid_sizes(ra, dims, Sq):
+    """Two causal block steps from the empty state, queries after both blocks: 1040,
+    528 and 48 16-row query tiles (two rows per thread, then four key streams over
+    more and fewer workgroups than the chip holds at once)."""
     B, Hq, Hkv, Sk = 2, 8, 2, 300
     Dqk, Dv = dims
+    assert (f32_tiles(B, Hq, Sq) >= 1024) == (Sq == 1040)
     q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, 2 * Sk, Dqk, Dv, seed=181 + Sq, dtype="f32")
     q_pos0 = 2 * Sk - 20
     tq, tk, tv = (to_dev(x, torch.float32) for x in (q, k, v))
