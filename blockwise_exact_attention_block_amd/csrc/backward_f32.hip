@@ -14,10 +14,12 @@
 // Three kernels:
 //   * bwd_delta_f32_kernel: delta per query row, 16 lanes per row.
 //   * bwd_dq_f32_kernel (256 threads): 32 query rows of one (batch, head) per
-//     workgroup, key tiles of 64 (D_qk = D_v = 64) or 32 in LDS, the next tile
-//     prefetched into registers. Thread t first forms S and dP for keys t % 16 + 16 u
-//     against rows t / 16 and t / 16 + 16, then accumulates dQ for D_qk / 32 rows at
-//     one group of four columns, reading their dS (stored key-major) as one vector.
+//     workgroup (16 in launches of fewer 32-row workgroups than CUs), key tiles of 64
+//     (D_qk = D_v = 64) or 32 in LDS, the next tile prefetched into registers. Thread
+//     t first forms S and dP for keys t % 16 + 16 u against rows t / 16 and
+//     t / 16 + 16, then accumulates dQ for D_qk / 32 rows (half that with 16-row
+//     workgroups) at one group of four columns, reading their dS (stored key-major)
+//     as one vector.
 //   * bwd_dkdv_f32_kernel (512 threads): key tiles of 32 of one (batch, KV head), the
 //     tile's K and V rows in LDS; it walks the group's query heads and the visible
 //     query tiles of 32 rows, the two halves of the workgroup taking alternate ones.
@@ -126,17 +128,20 @@ __device__ __forceinline__ void lds_n(float (&x)[N], const float* p) {
 }
 
 // ---- dQ -------------------------------------------------------------------------------
-// 32 query rows of one (batch, head) per workgroup. Score pass: keys kp + 16 u
-// (u < BK / 16) against rows rq and rq + 16 (kp = t % 16, rq = t / 16), each K / V
-// chunk read once for both rows and each Q / dO chunk once for all the keys; dS goes
-// to LDS key-major. dQ pass: rows RQ (t / (DQK/4)) .. + RQ - 1 at columns
+// 16 R query rows of one (batch, head) per workgroup (R = 2, or 1 for launches of
+// fewer 32-row workgroups than CUs). Score pass: keys kp + 16 u (u < BK / 16)
+// against rows rq + 16 h, h < R (kp = t % 16, rq = t / 16), each K / V chunk read
+// once for the R rows and each Q / dO chunk once for all the keys; dS goes to LDS
+// key-major. dQ pass: rows RQ (t / (DQK/4)) .. + RQ - 1 at columns
 // 4 (t % (DQK/4)) .. + 3, one vector read of their dS and one of K per key.
-template <int DQK, int DV>
+template <int DQK, int DV, int R>
 __global__ void __launch_bounds__(256)
 bwd_dq_f32_kernel(BwdArgs a) {
   using C = F32BCfg<DQK, DV>;
-  constexpr int BQ = C::BQK, BK = C::BK, NU = C::NU, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS;
-  constexpr int T = C::THREADS, RQ = C::KK, DSS = BQ + 4;
+  constexpr int BQ = 16 * R, BK = C::BK, NU = C::NU, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS;
+  constexpr int T = C::THREADS, RQ = BQ * DQK / 4 / T, DSS = BQ + 4;
+  constexpr int QCH = BQ * DQK / 4 / T, OCH = BQ * DV / 4 / T;
+  static_assert(RQ * T * 4 == BQ * DQK && QCH * T * 4 == BQ * DQK && OCH * T * 4 == BQ * DV, "tile split");
   __shared__ __attribute__((aligned(16))) float qsm[BQ * QS];
   __shared__ __attribute__((aligned(16))) float osm[BQ * OS];
   __shared__ __attribute__((aligned(16))) float ksm[BK * KS];
@@ -163,18 +168,18 @@ bwd_dq_f32_kernel(BwdArgs a) {
   const float* v_head = (const float*)a.v + kvh * DV;
 
   {
-    float4 qr[C::QCH2], orr[C::OCH2];
-    load_rows<DQK, C::QCH2, T>(qr, q_head, row_base, a.Sq, tid);
-    load_rows<DV, C::OCH2, T>(orr, o_head, row_base, a.Sq, tid);
-    store_rows<DQK, C::QCH2, T, QS>(qr, qsm, tid);
-    store_rows<DV, C::OCH2, T, OS>(orr, osm, tid);
+    float4 qr[QCH], orr[OCH];
+    load_rows<DQK, QCH, T>(qr, q_head, row_base, a.Sq, tid);
+    load_rows<DV, OCH, T>(orr, o_head, row_base, a.Sq, tid);
+    store_rows<DQK, QCH, T, QS>(qr, qsm, tid);
+    store_rows<DV, OCH, T, OS>(orr, osm, tid);
   }
-  // statistics of rows rq and rq + 16: a row past the block, or with no visible key,
-  // gets P = 0
-  float lse2[2], dlt[2];
-  long long qpos[2];
+  // statistics of rows rq + 16 h: a row past the block, or with no visible key, gets
+  // P = 0
+  float lse2[R], dlt[R];
+  long long qpos[R];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < R; ++h) {
     const int row = row_base + rq + 16 * h;
     qpos[h] = a.q_pos0 + row;
     lse2[h] = __builtin_huge_valf();   // +inf: exp2(s - lse2) = 0
@@ -204,34 +209,40 @@ bwd_dq_f32_kernel(BwdArgs a) {
       load_rows<DQK, C::KCH, T>(kr, k_head, (n + 1) * BK, a.Sk, tid);
       load_rows<DV, C::VCH, T>(vr, v_head, (n + 1) * BK, a.Sk, tid);
     }
-    float s[2][NU], dp[2][NU];
+    float s[R][NU], dp[R][NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) s[0][u] = s[1][u] = dp[0][u] = dp[1][u] = 0.f;
+    for (int h = 0; h < R; ++h)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) s[h][u] = dp[h][u] = 0.f;
 #pragma unroll 2
     for (int d4 = 0; d4 < DQK / 4; ++d4) {
-      const float4 x0 = lds4(&qsm[rq * QS + 4 * d4]), x1 = lds4(&qsm[(rq + 16) * QS + 4 * d4]);
+      float4 x[R];
+#pragma unroll
+      for (int h = 0; h < R; ++h) x[h] = lds4(&qsm[(rq + 16 * h) * QS + 4 * d4]);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const float4 kx = lds4(&ksm[(kp + 16 * u) * KS + 4 * d4]);
-        s[0][u] = dot4(x0, kx, s[0][u]);
-        s[1][u] = dot4(x1, kx, s[1][u]);
+#pragma unroll
+        for (int h = 0; h < R; ++h) s[h][u] = dot4(x[h], kx, s[h][u]);
       }
     }
 #pragma unroll 2
     for (int d4 = 0; d4 < DV / 4; ++d4) {
-      const float4 x0 = lds4(&osm[rq * OS + 4 * d4]), x1 = lds4(&osm[(rq + 16) * OS + 4 * d4]);
+      float4 x[R];
+#pragma unroll
+      for (int h = 0; h < R; ++h) x[h] = lds4(&osm[(rq + 16 * h) * OS + 4 * d4]);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const float4 vx = lds4(&vsm[(kp + 16 * u) * VS + 4 * d4]);
-        dp[0][u] = dot4(x0, vx, dp[0][u]);
-        dp[1][u] = dot4(x1, vx, dp[1][u]);
+#pragma unroll
+        for (int h = 0; h < R; ++h) dp[h][u] = dot4(x[h], vx, dp[h][u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int key = kp + 16 * u;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < R; ++h) {
         const bool vis = key < nvalid && (!a.causal || kpos0 + key <= qpos[h]);
         const float p = vis ? exp2_hw(fmaf(s[h][u], a.scale_log2, -lse2[h])) : 0.f;
         dst[key * DSS + rq + 16 * h] = p * (dp[h][u] - dlt[h]);
@@ -518,11 +529,18 @@ static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(2 * C::THREADS), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  b.n_tiles = (a.Sq + C::BQK - 1) / C::BQK;
+  // 32-row dQ workgroups (two rows per thread), or 16-row ones when there are fewer
+  // 32-row workgroups than CUs
+  const bool two_rows = (long long)a.B * a.Hq * ((a.Sq + 31) / 32) >= 256;
+  b.n_tiles = two_rows ? (a.Sq + 31) / 32 : (a.Sq + 15) / 16;
   grid = (long long)a.B * a.Hq * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (grid > 0)
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  if (grid > 0) {
+    if (two_rows)
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 2>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+    else
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 1>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
+  }
   return hipGetLastError();
 }
 

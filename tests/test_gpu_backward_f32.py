@@ -84,6 +84,35 @@ def test_f32_bwd_step_against_oracle(ra, dims, causal, q_pos0, k_pos0, Sq, Sk):
     grad_close(dv, gv, "dv")
 
 
+@pytest.mark.parametrize("dims", DIMS)
+@pytest.mark.parametrize("causal,q_pos0,k_pos0", [(False, 0, 0), (True, 900, 0), (True, 100, 180)])
+def test_f32_bwd_step_two_row_dq(ra, dims, causal, q_pos0, k_pos0):
+    """A launch of at least 256 32-row dQ workgroups takes two query rows per thread
+    (the cases above have fewer and take one): 2 x 8 heads x 1040 rows (33 ragged
+    32-row tiles), 300 keys."""
+    B, Hq, Hkv, Sq, Sk = 2, 8, 2, 1040, 300
+    D, Dv = dims
+    assert B * Hq * ((Sq + 31) // 32) >= 256
+    say(f"block_attn_bwd_step f32 two-row dQ D{D}/{Dv} causal={causal} q_pos0={q_pos0} k_pos0={k_pos0}")
+    q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=1540 + D + Dv + q_pos0, dtype="f32")
+    do = randn_np((B, Hq, Sq, Dv), 1640 + D + Dv, "f32")
+    scale = 1 / math.sqrt(D)
+    kf, vf = (np.concatenate([x, x[:, :, :7]], axis=2) for x in (k, v))
+    kpos = np.concatenate([k_pos0 + np.arange(Sk), k_pos0 + Sk + np.arange(7)])
+    _, _, _, lse, delta = oracle.attention_bwd(q, kf, vf, do, scale=scale, causal=causal, q_pos0=q_pos0,
+                                               k_pos=kpos)
+    gq, gk, gv = oracle.block_bwd(q, k, v, do, lse, delta, scale=scale, causal=causal, q_pos0=q_pos0,
+                                  k_pos0=k_pos0)
+    dq, dk, dv = zeros(B, Hq, Sq, D), zeros(B, Hkv, Sk, D), zeros(B, Hkv, Sk, Dv)
+    ra.block_attn_bwd_step(to_dev(q), to_dev(do), to_dev(np.where(np.isfinite(lse), lse, -np.inf)),
+                           to_dev(delta), to_dev(k), to_dev(v), dq, dk, dv, q_pos0=q_pos0, k_pos0=k_pos0,
+                           causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    grad_close(dq, gq, "dq")
+    grad_close(dk, gk, "dk")
+    grad_close(dv, gv, "dv")
+
+
 def test_f32_bwd_step_accumulates(ra):
     """The step adds into the accumulators: two calls give twice one call."""
     B, Hq, Hkv, S, D = 1, 2, 1, 200, 128
