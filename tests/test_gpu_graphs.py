@@ -49,12 +49,13 @@ def capture(fn):
     return g
 
 
-def test_ring_of_block_steps_in_a_graph(ra):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ring_of_block_steps_in_a_graph(ra, dtype):
     """Partition 2 of a causal ring of 4 (GQA 4:1, D 128): its three visible block
-    steps in ring order, captured with the state reset."""
+    steps in ring order, captured with the state reset (bf16 and fp32 kernels)."""
     B, Hq, Hkv, Sp, P, D = 1, 8, 2, 384, 4, 128
     S, i = Sp * P, 2
-    q, k, v = (to_dev(x) for x in prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=181, dtype="bf16"))
+    q, k, v = (to_dev(x, dtype) for x in prefill_inputs_np(B, Hq, Hkv, S, S, D, D, seed=181, dtype="f32"))
     qi = q[:, :, i * Sp:(i + 1) * Sp].contiguous()
     blocks = [(j, k[:, :, j * Sp:(j + 1) * Sp].contiguous(), v[:, :, j * Sp:(j + 1) * Sp].contiguous())
               for j, kind in ra.ring_schedule(P, i, True) if kind != "skip"]

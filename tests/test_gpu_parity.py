@@ -545,6 +545,36 @@ def test_calls_on_two_streams_match_the_default_stream(ra):
         assert torch.equal(a, b) and torch.equal(a, c)
 
 
+def test_fp32_forward_on_two_side_streams(ra):
+    """The fp32 ring prefill (two-row layout at 1040 tiles, and the four-stream one)
+    and an fp32 block step on two side streams at once: bit-identical to the default
+    stream."""
+    q, k, v = (to_dev(x, torch.float32) for x in prefill_inputs_np(2, 8, 2, 1040, 1040, 128, 128, seed=175,
+                                                                      dtype="f32"))
+
+    def work():
+        o, lse = ra.ring_attn_fwd(q, k, v, P=2, causal=True)
+        o1, l1 = ra.ring_attn_fwd(q[:1, :2].contiguous(), k[:1, :1].contiguous(), v[:1, :1].contiguous(), P=2,
+                                  causal=True)
+        oa, la = ra.init_state(q[:, :, :520].contiguous(), 128)
+        ra.block_attn_step(q[:, :, :520].contiguous(), k[:, :, 300:800].contiguous(), v[:, :, 300:800].contiguous(),
+                           oa, la, q_pos0=520, k_pos0=300, causal=True)
+        return o, lse, o1, l1, oa, la
+
+    ref = work()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        r1 = work()
+    with torch.cuda.stream(s2):
+        r2 = work()
+    torch.cuda.synchronize()
+    for a, b, c in zip(ref, r1, r2):
+        assert torch.equal(a, b) and torch.equal(a, c)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_backward_on_two_side_streams(ra, dtype):
     """The backward entry points issued on two side streams at once give results
