@@ -199,8 +199,12 @@ def test_random_backward_step(ra, c):
     dt = c["dt"]
     q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=c["seed"], dtype=dt)
     do = randn_np((B, Hq, Sq, Dv), c["seed"] + 3, dt)
-    extra = np.arange(7) % Sk                     # 7 more keys after the block (repeats when Sk < 7)
-    kf, vf = (np.concatenate([x, x[:, :, extra]], axis=2) for x in (k, v))
+    # 7 more keys of their own after the block. (Copies of the block's keys would,
+    # for a one-key block, make every visible key of a row identical: then dS is
+    # exactly zero and the kernels' rounding has nothing to be relative to.)
+    kx = randn_np((B, Hkv, 7, D), c["seed"] + 4, dt)
+    vx = randn_np((B, Hkv, 7, Dv), c["seed"] + 5, dt)
+    kf, vf = np.concatenate([k, kx], axis=2), np.concatenate([v, vx], axis=2)
     kpos = np.concatenate([c["k_pos0"] + np.arange(Sk), c["k_pos0"] + Sk + np.arange(7)])
     _, _, _, lse, delta = oracle.attention_bwd(q, kf, vf, do, scale=scale, causal=c["causal"], q_pos0=c["q_pos0"],
                                                k_pos=kpos)
