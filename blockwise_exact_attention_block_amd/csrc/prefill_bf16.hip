@@ -43,6 +43,10 @@
 
 namespace ra {
 
+// Query tiles per block when workgroups are dealt to the XCDs in blocks (see the
+// workgroup mapping in prefill_bf16_kernel).
+constexpr int kXcdTiles = 4;
+
 enum { MODE_RING = 0, MODE_STEP = 1 };
 
 // Largest lead (log2 units) of a score over its row's reference shift before the
@@ -98,17 +102,32 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int h = lane >> 5;
 
   // Workgroup -> (batch, head, query partition, query tile), XCD-aware. Workgroups
-  // are dealt to the 8 XCDs round-robin, so XCD x runs ids x, x+8, ...; those ids
-  // take the x-th contiguous eighth of the work list, ordered (batch, KV head,
-  // query tile, query head of the group). The ~32 workgroups an XCD runs at once
-  // are then the query heads of one KV head on a few adjacent query tiles, which
-  // stream the same K/V blocks at the same time through that XCD's L2. Inside a
-  // KV head the heaviest causal tiles go first.
+  // are dealt to the 8 XCDs round-robin, so XCD x runs ids x, x+8, ...; the work
+  // list is ordered (batch, KV head, query tile, query head of the group), the
+  // heaviest causal tiles of a KV head first. When the KV heads (times batch) are a
+  // multiple of 8, XCD x takes the x-th contiguous eighth of the list: whole KV
+  // heads, so the ~32 workgroups it runs at once are the query heads of one KV head
+  // on a few adjacent query tiles, streaming the same K/V blocks through its L2.
+  // Otherwise an eighth would hold part of a KV head's tiles (with two KV heads, XCD
+  // 0 its heaviest quarter and XCD 3 its lightest), so the list is cut into blocks
+  // of kXcdTiles query tiles (with all query heads of the group), dealt in rounds of
+  // eight, one block per XCD, in serpentine order (round r deals blocks 8 r .. 8 r + 7
+  // to XCDs 0 .. 7 when r is even and 7 .. 0 when it is odd): as the weights of
+  // heavy-first causal tiles fall about linearly, every XCD's sum comes out even,
+  // and its concurrent workgroups still read one KV head.
   const int tiles_per_head = (MODE == MODE_RING ? a.nq : 1) * a.n_qtiles;
   const int n_items = a.B * a.Hq * tiles_per_head;
-  const int per_xcd = (n_items + 7) >> 3;
-  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (u >= n_items) return;  // padding of the last XCD's share: no work, no barrier
+  int u;
+  if (((a.B * a.Hkv) & 7) == 0) {
+    const int per_xcd = (n_items + 7) >> 3;
+    u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  } else {
+    const int bs = kXcdTiles * a.group;   // items per dealt block
+    const int x = (int)(blockIdx.x & 7), j = (int)(blockIdx.x >> 3);
+    const int r = j / bs;                 // the round: one block per XCD
+    u = (8 * r + ((r & 1) ? 7 - x : x)) * bs + j % bs;
+  }
+  if (u >= n_items) return;  // padding of the last round: no work, no barrier
   const int w = u % a.group;
   const int rest = u / a.group;
   const int gt = tiles_per_head - 1 - rest % tiles_per_head;
@@ -606,7 +625,13 @@ static hipError_t launch_cfg(PrefillArgs a, hipStream_t st) {
   const long long tiles = prefill_items(a, MODE, C::BQ, a.n_qtiles);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
-  const long long grid = 8 * ((tiles + 7) / 8);   // whole rounds of the 8 XCDs
+  // whole rounds of the 8 XCDs (and, when blocks are dealt, of whole blocks)
+  long long grid = 8 * ((tiles + 7) / 8);
+  if ((a.B * a.Hkv) % 8 != 0) {
+    const long long bs = (long long)kXcdTiles * (a.Hq / a.Hkv);
+    grid = 8 * ((tiles + 8 * bs - 1) / (8 * bs)) * bs;
+  }
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_bf16_kernel<DQK, DV, NQ, NW, MODE, SPLIT>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
