@@ -463,7 +463,7 @@ def run_decode(args, ra, torch, dev, stream, dcfg, decode_inputs_torch):
     }
 
 
-PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (published, packed)
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 (published: dense matrix, and vector with packed math)
 
 
 def _f32_wide_workload():
@@ -501,8 +501,9 @@ def prefill_line(args, ra, torch, stream, cfg, q, k, v, steps, warmup):
         roof = {"kernel": f"prefill_bf16_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "mfma",
                 "peak": PEAK_BF16_TFLOPS, "traffic": recorded_traffic("prefill", cfg.name)}
     else:
-        # fp32 inputs run on the vector ALUs (fp32 FMAs, not packed)
-        roof = {"kernel": f"prefill_f32_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "alu",
+        # fp32 inputs run on the fp32 matrix cores (v_mfma_f32_32x32x2_f32 or
+        # 16x16x4, by launch size), whose dense peak is the fp32 figure
+        roof = {"kernel": f"prefill_f32_kernel<{cfg.Dqk},{cfg.Dv},ring>", "bound": "mfma",
                 "peak": PEAK_FP32_TFLOPS, "traffic": None}
     roof.update({"achieved": round(achieved, 3), "unit": "TFLOP/s", "frac": round(achieved / roof["peak"], 4),
                  "algorithmic_flops_per_launch": flops, "launch_ms": round(ev_ms, 5),

@@ -61,20 +61,22 @@ def test_fp32_ring_ragged(ra, dims, causal, Sp, P):
               seed=11 + Sp + P)
 
 
-# fp32 launches of at least 1024 16-row query tiles take two rows per thread (32-row
-# workgroups); smaller ones (the cases above) split the keys over four streams.
-# These have ragged 16- and 32-row tiles and ragged key tiles.
+# fp32 launches with at least 512 workgroups of 32 x 32 products (128 query rows, 64
+# at D_qk = D_v = 64) use that shape; smaller ones (the cases above) take 16 x 16
+# products in workgroups of 32 or 16 rows. These have ragged row and key tiles.
 
-def f32_tiles(B, Hq, rows, nparts=1):
-    return B * Hq * nparts * ((rows + 15) // 16)
+def f32_wide(B, Hq, rows, nparts, Dqk, Dv):
+    """Whether an fp32 launch takes the 32 x 32 product shape."""
+    bq = 64 if Dqk + Dv <= 128 else 128
+    return B * Hq * nparts * ((rows + bq - 1) // bq) >= 512
 
 
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("layout", ["contiguous", "striped"])
 def test_fp32_ring_large_grid_ragged(ra, dims, causal, layout):
-    B, Hq, Hkv, Sp, P = 2, 8, 2, 520, 2
-    assert f32_tiles(B, Hq, Sp, P) >= 1024
+    B, Hq, Hkv, Sp, P = (2, 8, 2, 1040, 2) if dims == (64, 64) else (2, 16, 4, 1040, 2)
+    assert f32_wide(B, Hq, Sp, P, *dims)
     case = ring_case if layout == "contiguous" else striped_case
     case(ra, dtype="f32", B=B, Hq=Hq, Hkv=Hkv, Sp=Sp, P=P, Dqk=dims[0], Dv=dims[1], causal=causal,
          seed=171 + dims[0] + dims[1])
@@ -83,12 +85,12 @@ def test_fp32_ring_large_grid_ragged(ra, dims, causal, layout):
 @pytest.mark.parametrize("dims", [(64, 64), (128, 128)])
 @pytest.mark.parametrize("Sq", [1040, 520, 40])
 def test_fp32_step_chain_three_grid_sizes(ra, dims, Sq):
-    """Two causal block steps from the empty state, queries after both blocks: 1040,
-    528 and 48 16-row query tiles (two rows per thread, then four key streams over
-    more and fewer workgroups than the chip holds at once)."""
-    B, Hq, Hkv, Sk = 2, 8, 2, 300
+    """Two causal block steps from the empty state, queries after both blocks: the
+    32 x 32 product shape at 1040 rows, then the 16 x 16 one over more and fewer
+    workgroups than the chip holds at once."""
     Dqk, Dv = dims
-    assert (f32_tiles(B, Hq, Sq) >= 1024) == (Sq == 1040)
+    B, Hq, Hkv, Sk = 2, 16 if Dqk == 64 else 32, 4, 300
+    assert f32_wide(B, Hq, Sq, 1, Dqk, Dv) == (Sq == 1040)
     q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, 2 * Sk, Dqk, Dv, seed=181 + Sq, dtype="f32")
     q_pos0 = 2 * Sk - 20
     tq, tk, tv = (to_dev(x, torch.float32) for x in (q, k, v))
@@ -546,11 +548,12 @@ def test_calls_on_two_streams_match_the_default_stream(ra):
 
 
 def test_fp32_forward_on_two_side_streams(ra):
-    """The fp32 ring prefill (two-row layout at 1040 tiles, and the four-stream one)
-    and an fp32 block step on two side streams at once: bit-identical to the default
-    stream."""
-    q, k, v = (to_dev(x, torch.float32) for x in prefill_inputs_np(2, 8, 2, 1040, 1040, 128, 128, seed=175,
+    """The fp32 ring prefill (32 x 32 products at 2 x 32 heads, and 16 x 16 ones on
+    one head) and an fp32 block step on two side streams at once: bit-identical to
+    the default stream."""
+    q, k, v = (to_dev(x, torch.float32) for x in prefill_inputs_np(2, 32, 8, 1040, 1040, 128, 128, seed=175,
                                                                       dtype="f32"))
+    assert f32_wide(2, 32, 520, 2, 128, 128) and not f32_wide(1, 2, 520, 2, 128, 128)
 
     def work():
         o, lse = ra.ring_attn_fwd(q, k, v, P=2, causal=True)

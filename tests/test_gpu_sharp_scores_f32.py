@@ -121,9 +121,9 @@ def test_f32_ring_sharp(ra, kind, dims, causal, layout):
 @pytest.mark.parametrize("Sp", [160, 1040])
 def test_f32_step_chain_from_empty_sharp(ra, kind, dims, Sp):
     """Every partition's ring as block steps from the empty state (O = 0, LSE = -inf),
-    causal: small launches (four key streams) and, at 2 x 8 heads x 1040 rows, the
-    two-rows-per-thread layout."""
-    B, Hq, Hkv, P = (1, 4, 2, 3) if Sp == 160 else (2, 8, 2, 2)
+    causal: small launches (16 x 16 products) and, at 2 x 32 heads x 1040 rows, the
+    32 x 32 product shape."""
+    B, Hq, Hkv, P = (1, 4, 2, 3) if Sp == 160 else (2, 32, 8, 2)
     Dqk, Dv = dims
     S = Sp * P
     say(f"block_attn_step fp32 from empty, {kind} D{Dqk}/{Dv} Sp {Sp}")
