@@ -1,5 +1,5 @@
-// Backward pass of blockwise exact attention for fp32 inputs on gfx950, on the
-// vector ALUs.
+// Backward pass of blockwise exact attention for fp32 inputs on gfx950, on the fp32
+// matrix cores.
 //
 // The same gradients as the bf16 backward (the exact gradients of O = softmax(scale *
 // Q K^T) V over the visible keys, page "长上下文的第一性挑战", §挑战 1, eq.
@@ -11,26 +11,32 @@
 // Everything stays in fp32: no product rounds P or dS, so this path meets the fp32
 // tolerance that the bf16 kernels cannot.
 //
+// Every product runs on v_mfma_f32_16x16x4_f32 (a 16 x 4 by 4 x 16 fp32 block into a
+// 16 x 16 fp32 accumulator, 64 FLOP per clock per SIMD). Lane L of a wave works for
+// row (or key) L % 16 of its 16 x 16 block and lane group g = L / 16: an operand
+// "stationary" in a lane holds dimensions g D / 4 .. g D / 4 + D / 4 - 1 of that row,
+// and an accumulator gives the lane column L % 16 and rows 4 g .. 4 g + 3.
+//
 // Three kernels:
 //   * bwd_delta_f32_kernel: delta per query row, 16 lanes per row.
-//   * bwd_dq_f32_kernel (256 threads): 32 query rows of one (batch, head) per
-//     workgroup (16 in launches of fewer 32-row workgroups than CUs), key tiles of 64
-//     (D_qk = D_v = 64) or 32 in LDS, the next tile prefetched into registers. Thread
-//     t first forms S and dP for keys t % 16 + 16 u against rows t / 16 and
-//     t / 16 + 16, then accumulates dQ for D_qk / 32 rows (half that with 16-row
-//     workgroups) at one group of four columns, reading their dS (stored key-major)
-//     as one vector.
-//   * bwd_dkdv_f32_kernel (512 threads): key tiles of 32 of one (batch, KV head), the
-//     tile's K and V rows in LDS; it walks the group's query heads and the visible
-//     query tiles of 32 rows, the two halves of the workgroup taking alternate ones.
-//     Thread t of a half first forms P and dS for keys t % 16, t % 16 + 16 against
-//     rows t / 16, t / 16 + 16, then accumulates dK (dV) for D_qk / 32 (D_v / 32) keys
-//     at one group of four columns, reading their dS (P) as one vector; the halves'
-//     sums meet in LDS at the end. Under a causal mask a workgroup takes key tiles kt
-//     and n - 1 - kt, which balances the work.
-// Each thread works on two rows by two or more keys, so every 16-byte LDS read
-// feeds 8 or more FMAs. LDS rows are padded by 4 floats; every sum runs in a fixed
-// order, so results are reproducible run to run.
+//   * bwd_dq_f32_kernel (8 waves): 64 query rows of one (batch, head) = 4 row blocks
+//     x 2 key streams; K / V tiles of 32 keys go from HBM into LDS (direct loads,
+//     double-buffered). A wave keeps its 16 rows' Q and dO stationary, forms
+//     Sᵀ = K Qᵀ and dPᵀ = V dOᵀ for 16 keys (lane: row L % 16, keys 4 g + v), P and
+//     dS in registers, then dQᵀ += Kᵀ dSᵀ with the lane's dS values as the B operand
+//     and K read back from LDS as A. The streams' sums meet in LDS at the end.
+//   * bwd_dkdv_f32_kernel (8 waves): 32 keys of one (batch, KV head) = 2 key blocks
+//     x 4 query streams. A wave keeps its 16 keys' K and V stationary; it walks the
+//     group's query heads and the query tiles of 64 rows that can see them (Q, dO,
+//     LSE and delta in LDS, double-buffered), forms S = Q Kᵀ and dP = dO Vᵀ (lane:
+//     key L % 16, rows 4 g + v), P and dS, then dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS with
+//     dO and Q read back from LDS. Under a causal mask a workgroup takes key tiles
+//     kt and n - 1 - kt, which balances the work. The query streams' sums meet in
+//     LDS at the end.
+// LDS rows are padded by 4 floats, so the 16-byte operand reads of 16 rows at one
+// column and the 4-byte reads of rows 4 apart at 16 consecutive columns are both
+// free of bank conflicts. Every sum runs in a fixed order, so results repeat bit for
+// bit.
 #include "common.hpp"
 
 namespace ra {
@@ -56,104 +62,66 @@ bwd_delta_f32_kernel(const float* o, const float* dout, float* delta, long long 
   if (row < rows && L == 0) delta[row] = acc;
 }
 
-template <int DQK, int DV>
-struct F32BCfg {
-  static constexpr int THREADS = 256;
-  static constexpr int BQK = 32;                // query rows per tile (both kernels)
-  // keys per tile in the dQ kernel: 32 unless D_qk = D_v = 64, so that two
-  // workgroups fit a CU's LDS
-  static constexpr int BK = DQK + DV > 128 ? 32 : 64;
-  static constexpr int NU = BK / 16;            // keys per thread in the dQ kernel's score pass
-  static constexpr int BKEY = 32;               // keys per tile (dK/dV)
-  // keys per thread in the dK (dV) sums; also rows per thread in the dQ sums
-  static constexpr int KK = DQK / 32, KVV = DV / 32;
-  // every LDS row padded by 4 floats: 16-byte reads of up to 16 rows at one column
-  // start on distinct 4-bank groups
-  static constexpr int QS = DQK + 4, OS = DV + 4, KS = DQK + 4, VS = DV + 4;
-  static constexpr int PS2 = BKEY + 4;
-  static constexpr int KCH = BK * DQK / 4 / THREADS, VCH = BK * DV / 4 / THREADS;
-  static constexpr int QCH2 = BQK * DQK / 4 / THREADS, OCH2 = BQK * DV / 4 / THREADS;
-  static_assert(KCH * THREADS * 4 == BK * DQK && VCH * THREADS * 4 == BK * DV, "tile split");
-  static_assert(QCH2 * THREADS * 4 == BQK * DQK && OCH2 * THREADS * 4 == BQK * DV, "tile split");
-  static_assert(DQK % 64 == 0 && DV % 64 == 0, "64-column groups");
-};
-
-__device__ __forceinline__ float dot4(float4 x, float4 y, float acc) {
-  acc = fmaf(x.x, y.x, acc);
-  acc = fmaf(x.y, y.y, acc);
-  acc = fmaf(x.z, y.z, acc);
-  return fmaf(x.w, y.w, acc);
-}
-__device__ __forceinline__ void axpy4(float s, float4 x, float4& acc) {
-  acc.x = fmaf(s, x.x, acc.x);
-  acc.y = fmaf(s, x.y, acc.y);
-  acc.z = fmaf(s, x.z, acc.z);
-  acc.w = fmaf(s, x.w, acc.w);
-}
-__device__ __forceinline__ float4 lds4(const float* p) { return *(const float4*)p; }
-
-// Rows [row0, row0 + rows) of a [n, D] fp32 matrix, 16-byte chunks dealt round-robin
-// over the workgroup's threads (chunk e = it * THREADS + tid); rows at or past
-// `limit` read as zero.
-template <int D, int CH, int THREADS>
-__device__ __forceinline__ void load_rows(float4 (&r)[CH], const float* base, int row0, int limit, int tid) {
-#pragma unroll
-  for (int it = 0; it < CH; ++it) {
-    const int e = it * THREADS + tid, rr = e / (D / 4), c4 = e % (D / 4);
-    r[it] = row0 + rr < limit ? *(const float4*)(base + (size_t)(row0 + rr) * D + 4 * c4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-template <int D, int CH, int THREADS, int STRIDE>
-__device__ __forceinline__ void store_rows(const float4 (&r)[CH], float* lds, int tid) {
-#pragma unroll
-  for (int it = 0; it < CH; ++it) {
-    const int e = it * THREADS + tid, rr = e / (D / 4), c4 = e % (D / 4);
-    *(float4*)&lds[rr * STRIDE + 4 * c4] = r[it];
-  }
+__device__ __forceinline__ f32x4 mma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// D / 4 consecutive floats from global memory (zero when !ok) into registers
 template <int N>
-__device__ __forceinline__ void lds_n(float (&x)[N], const float* p) {
-  if constexpr (N == 4) {
-    const float4 v = *(const float4*)p;
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  } else if constexpr (N == 2) {
-    const float2 v = *(const float2*)p;
-    x[0] = v.x; x[1] = v.y;
-  } else {
+__device__ __forceinline__ void load_vec(float (&x)[N], const float* p, bool ok) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = p[i];
+  for (int c = 0; c < N / 4; ++c) {
+    const float4 v = ok ? *(const float4*)(p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    x[4 * c] = v.x;
+    x[4 * c + 1] = v.y;
+    x[4 * c + 2] = v.z;
+    x[4 * c + 3] = v.w;
   }
+}
+
+// acc += A B over N steps: A from LDS (16-byte reads, four steps each), B stationary
+template <int N>
+__device__ __forceinline__ f32x4 chain(const float* lds, const float (&b)[N], f32x4 acc) {
+#pragma unroll
+  for (int c = 0; c < N / 4; ++c) {
+    const float4 x = *(const float4*)(lds + 4 * c);
+    acc = mma16_f32(x.x, b[4 * c], acc);
+    acc = mma16_f32(x.y, b[4 * c + 1], acc);
+    acc = mma16_f32(x.z, b[4 * c + 2], acc);
+    acc = mma16_f32(x.w, b[4 * c + 3], acc);
+  }
+  return acc;
 }
 
 // ---- dQ -------------------------------------------------------------------------------
-// 16 R query rows of one (batch, head) per workgroup (R = 2, or 1 for launches of
-// fewer 32-row workgroups than CUs). Score pass: keys kp + 16 u (u < BK / 16)
-// against rows rq + 16 h, h < R (kp = t % 16, rq = t / 16), each K / V chunk read
-// once for the R rows and each Q / dO chunk once for all the keys; dS goes to LDS
-// key-major. dQ pass: rows RQ (t / (DQK/4)) .. + RQ - 1 at columns
-// 4 (t % (DQK/4)) .. + 3, one vector read of their dS and one of K per key.
-template <int DQK, int DV, int R>
-__global__ void __launch_bounds__(256)
-bwd_dq_f32_kernel(BwdArgs a) {
-  using C = F32BCfg<DQK, DV>;
-  constexpr int BQ = 16 * R, BK = C::BK, NU = C::NU, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS;
-  constexpr int T = C::THREADS, RQ = BQ * DQK / 4 / T, DSS = BQ + 4;
-  constexpr int QCH = BQ * DQK / 4 / T, OCH = BQ * DV / 4 / T;
-  static_assert(RQ * T * 4 == BQ * DQK && QCH * T * 4 == BQ * DQK && OCH * T * 4 == BQ * DV, "tile split");
-  __shared__ __attribute__((aligned(16))) float qsm[BQ * QS];
-  __shared__ __attribute__((aligned(16))) float osm[BQ * OS];
-  __shared__ __attribute__((aligned(16))) float ksm[BK * KS];
-  __shared__ __attribute__((aligned(16))) float vsm[BK * VS];
-  __shared__ __attribute__((aligned(16))) float dst[BK * DSS];   // dS, key-major
+template <int DQK, int DV>
+struct F32DqCfg {
+  static constexpr int NR = 4, NS = 2;                // 16-row blocks x key streams
+  static constexpr int BQ = 16 * NR, BK = 16 * NS;    // query rows per workgroup, keys per tile
+  static constexpr int KS = DQK + 4, VS = DV + 4;
+  static constexpr int K_TILE = padded_tile_bytes(BK, KS * 4) / 4;   // floats per buffer
+  static constexpr int V_TILE = padded_tile_bytes(BK, VS * 4) / 4;
+  static constexpr int DT = DQK / 16;                 // dQ output tiles of 16 columns
+  static constexpr int MERGE = 16 * DQK;              // one wave's dQ partial sums
+  static_assert(NR * NS == 8, "eight waves");
+  static_assert((NS - 1) * NR * MERGE <= 2 * (K_TILE + V_TILE), "merge area");
+};
 
-  const int tid = threadIdx.x, kp = tid & 15, rq = tid >> 4;
-  const int cg = tid % (DQK / 4), rg = tid / (DQK / 4);
-  // workgroup -> (batch, head, query tile), the heaviest causal tiles first
-  const int qt = a.n_tiles - 1 - (int)(blockIdx.x % a.n_tiles);
-  const int bh = blockIdx.x / a.n_tiles;
-  const int b = bh / a.Hq, hq = bh - b * a.Hq, g = hq / a.group;
+template <int DQK, int DV>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_f32_kernel(BwdArgs a) {
+  using C = F32DqCfg<DQK, DV>;
+  constexpr int NR = C::NR, NS = C::NS, BQ = C::BQ, BK = C::BK, KS = C::KS, VS = C::VS, DT = C::DT;
+  __shared__ __attribute__((aligned(1024))) float smem[2 * (C::K_TILE + C::V_TILE)];
+  const int lane = threadIdx.x & 63, lm = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int rb = wave % NR, stream = wave / NR;
+
+  // workgroup x: head x % (B Hq) and the (x / (B Hq))-th heaviest of its query tiles
+  const int nbh = a.B * a.Hq;
+  const int bh = blockIdx.x % nbh;
+  const int qt = a.n_tiles - 1 - (int)(blockIdx.x / nbh);
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, kvg = hq / a.group;
   const int row_base = qt * BQ;
   const int last_row = min(row_base + BQ, a.Sq) - 1;
   long long kmax = a.Sk;
@@ -161,328 +129,304 @@ bwd_dq_f32_kernel(BwdArgs a) {
   if (kmax <= 0) return;   // no key of the block is visible to this tile
   const int ntiles = (int)((kmax + BK - 1) / BK);
 
-  const float* q_head = (const float*)a.q + (size_t)bh * a.Sq * DQK;
-  const float* o_head = (const float*)a.dout + (size_t)bh * a.Sq * DV;
-  const size_t kvh = (size_t)(b * a.Hkv + g) * a.Sk;
-  const float* k_head = (const float*)a.k + kvh * DQK;
-  const float* v_head = (const float*)a.v + kvh * DV;
+  const int wrow0 = row_base + 16 * rb;
+  const int wrows = min(16, a.Sq - wrow0);
+  const long long wpos0 = a.q_pos0 + wrow0;
+  const int row = wrow0 + lm;
+  const bool row_ok = lm < wrows;
+  const long long qpos = wpos0 + lm;
 
-  {
-    float4 qr[QCH], orr[OCH];
-    load_rows<DQK, QCH, T>(qr, q_head, row_base, a.Sq, tid);
-    load_rows<DV, OCH, T>(orr, o_head, row_base, a.Sq, tid);
-    store_rows<DQK, QCH, T, QS>(qr, qsm, tid);
-    store_rows<DV, OCH, T, OS>(orr, osm, tid);
+  float q[DQK / 4], dout[DV / 4];
+  load_vec(q, (const float*)a.q + ((size_t)bh * a.Sq + row) * DQK + g * (DQK / 4), row_ok);
+  load_vec(dout, (const float*)a.dout + ((size_t)bh * a.Sq + row) * DV + g * (DV / 4), row_ok);
+  // a row past the block, or with no visible key, gets P = 0 (exp2(s - inf))
+  float lse2 = __builtin_huge_valf(), dl = 0.f;
+  if (row_ok) {
+    const float l = a.lse[(size_t)bh * a.Sq + row];
+    if (l != kNegInf) lse2 = l * kLog2e;
+    dl = a.delta[(size_t)bh * a.Sq + row];
   }
-  // statistics of rows rq + 16 h: a row past the block, or with no visible key, gets
-  // P = 0
-  float lse2[R], dlt[R];
-  long long qpos[R];
+  f32x4 dq[DT];
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const int row = row_base + rq + 16 * h;
-    qpos[h] = a.q_pos0 + row;
-    lse2[h] = __builtin_huge_valf();   // +inf: exp2(s - lse2) = 0
-    dlt[h] = 0.f;
-    if (row < a.Sq) {
-      const float l = a.lse[(size_t)bh * a.Sq + row];
-      if (l != kNegInf) lse2[h] = l * kLog2e;
-      dlt[h] = a.delta[(size_t)bh * a.Sq + row];
-    }
-  }
+  for (int t = 0; t < DT; ++t) dq[t] = f32x4{};
 
-  // K / V tiles: global -> registers (one tile ahead) -> LDS
-  float4 kr[C::KCH], vr[C::VCH];
-  float4 acc[RQ];
-#pragma unroll
-  for (int e = 0; e < RQ; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const size_t kvh = (size_t)(b * a.Hkv + kvg) * a.Sk;
+  const u32x4 kdesc = raw_desc((const float*)a.k + kvh * DQK, (unsigned)((size_t)a.Sk * DQK * 4));
+  const u32x4 vdesc = raw_desc((const float*)a.v + kvh * DV, (unsigned)((size_t)a.Sk * DV * 4));
+  const unsigned k_last = (unsigned)((size_t)a.Sk * DQK * 4 - 16), v_last = (unsigned)((size_t)a.Sk * DV * 4 - 16);
+  const unsigned k_lds = lds_addr(smem), v_lds = lds_addr(smem + 2 * C::K_TILE);
+  PaddedTileDma<BK, DQK * 4, KS * 4, 8> kpad;
+  PaddedTileDma<BK, DV * 4, VS * 4, 8> vpad;
+  kpad.init(wave, lane);
+  vpad.init(wave, lane);
+  auto dma = [&](int n, int buf) __attribute__((always_inline)) {
+    kpad.issue(wave, k_lds + (unsigned)(buf * C::K_TILE * 4), (unsigned)(n * BK) * (DQK * 4), k_last, kdesc);
+    vpad.issue(wave, v_lds + (unsigned)(buf * C::V_TILE * 4), (unsigned)(n * BK) * (DV * 4), v_last, vdesc);
+  };
 
-  load_rows<DQK, C::KCH, T>(kr, k_head, 0, a.Sk, tid);
-  load_rows<DV, C::VCH, T>(vr, v_head, 0, a.Sk, tid);
-  store_rows<DQK, C::KCH, T, KS>(kr, ksm, tid);
-  store_rows<DV, C::VCH, T, VS>(vr, vsm, tid);
-  __syncthreads();   // Q, dO and the first K / V tile are in LDS
+  dma(0, 0);
+  wait_vmem();
+  __syncthreads();
   for (int n = 0; n < ntiles; ++n) {
-    const long long kpos0 = a.k_pos0 + (long long)n * BK;
-    const int nvalid = min(BK, a.Sk - n * BK);
-    if (n + 1 < ntiles) {   // lands while this tile is computed
-      load_rows<DQK, C::KCH, T>(kr, k_head, (n + 1) * BK, a.Sk, tid);
-      load_rows<DV, C::VCH, T>(vr, v_head, (n + 1) * BK, a.Sk, tid);
-    }
-    float s[R][NU], dp[R][NU];
+    const int buf = n & 1;
+    if (n + 1 < ntiles) dma(n + 1, buf ^ 1);
+    const int kb = 16 * stream;
+    const int nv = min(BK, a.Sk - n * BK) - kb;   // valid keys of this sub-block
+    const long long kpos = a.k_pos0 + (long long)n * BK + kb;
+    bool skip = nv <= 0 || wrows <= 0;
+    if (a.causal) skip = skip || kpos > wpos0 + wrows - 1;
+    const bool need_mask = nv < 16 || (a.causal && kpos + 15 > wpos0);
+    if (!skip) {
+      const float* kt = smem + buf * C::K_TILE;
+      const float* vt = smem + 2 * C::K_TILE + buf * C::V_TILE;
+      // Sᵀ and dPᵀ: lane holds row lm against keys 4 g + v
+      const f32x4 s = chain(kt + (kb + lm) * KS + g * (DQK / 4), q, f32x4{});
+      const f32x4 dp = chain(vt + (kb + lm) * VS + g * (DV / 4), dout, f32x4{});
+      float ds[4];
 #pragma unroll
-    for (int h = 0; h < R; ++h)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) s[h][u] = dp[h][u] = 0.f;
-#pragma unroll 2
-    for (int d4 = 0; d4 < DQK / 4; ++d4) {
-      float4 x[R];
-#pragma unroll
-      for (int h = 0; h < R; ++h) x[h] = lds4(&qsm[(rq + 16 * h) * QS + 4 * d4]);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const float4 kx = lds4(&ksm[(kp + 16 * u) * KS + 4 * d4]);
-#pragma unroll
-        for (int h = 0; h < R; ++h) s[h][u] = dot4(x[h], kx, s[h][u]);
+      for (int v = 0; v < 4; ++v) {
+        const int key = 4 * g + v;
+        const bool vis = !need_mask || (key < nv && (!a.causal || kpos + key <= qpos));
+        const float p = vis ? exp2_hw(fmaf(s[v], a.scale_log2, -lse2)) : 0.f;
+        ds[v] = p * (dp[v] - dl);
       }
+      // dQᵀ += Kᵀ dSᵀ: product t takes key 4 g + t, K read at column 16 dt + lm
+      const float* kc = kt + (kb + 4 * g) * KS + lm;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int d = 0; d < DT; ++d) dq[d] = mma16_f32(kc[t * KS + 16 * d], ds[t], dq[d]);
     }
-#pragma unroll 2
-    for (int d4 = 0; d4 < DV / 4; ++d4) {
-      float4 x[R];
-#pragma unroll
-      for (int h = 0; h < R; ++h) x[h] = lds4(&osm[(rq + 16 * h) * OS + 4 * d4]);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const float4 vx = lds4(&vsm[(kp + 16 * u) * VS + 4 * d4]);
-#pragma unroll
-        for (int h = 0; h < R; ++h) dp[h][u] = dot4(x[h], vx, dp[h][u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int key = kp + 16 * u;
-#pragma unroll
-      for (int h = 0; h < R; ++h) {
-        const bool vis = key < nvalid && (!a.causal || kpos0 + key <= qpos[h]);
-        const float p = vis ? exp2_hw(fmaf(s[h][u], a.scale_log2, -lse2[h])) : 0.f;
-        dst[key * DSS + rq + 16 * h] = p * (dp[h][u] - dlt[h]);
-      }
-    }
-    __syncthreads();   // the tile's dS is in LDS
-    // dQ rows RQ rg .. + RQ - 1, columns 4 cg .. + 3, over the tile's keys
-#pragma unroll 4
-    for (int kk = 0; kk < BK; ++kk) {
-      float ds[RQ];
-      lds_n<RQ>(ds, &dst[kk * DSS + RQ * rg]);
-      const float4 kx = lds4(&ksm[kk * KS + 4 * cg]);
-#pragma unroll
-      for (int e = 0; e < RQ; ++e) axpy4(ds[e], kx, acc[e]);
-    }
-    __syncthreads();   // K, V and dS of this tile consumed
-    if (n + 1 < ntiles) {
-      store_rows<DQK, C::KCH, T, KS>(kr, ksm, tid);
-      store_rows<DV, C::VCH, T, VS>(vr, vsm, tid);
-      __syncthreads();
-    }
+    wait_vmem();   // this wave's loads of tile n + 1 have landed
+    __syncthreads();
   }
 
+  // the key streams' sums meet in LDS (the tile buffers are free after the last barrier)
+  if constexpr (NS > 1) {
+    if (stream > 0) {
+      float* mb = smem + ((stream - 1) * NR + rb) * C::MERGE;
 #pragma unroll
-  for (int e = 0; e < RQ; ++e) {
-    const int row = row_base + RQ * rg + e;
-    if (row < a.Sq) {
-      float* dqp = a.dq + ((size_t)bh * a.Sq + row) * DQK + 4 * cg;
-      float4 cur = *(const float4*)dqp;
-      axpy4(a.scale, acc[e], cur);
-      *(float4*)dqp = cur;
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mb[(4 * d + v) * 64 + lane] = dq[d][v];
     }
+    __syncthreads();
+    if (stream > 0) return;
+#pragma unroll
+    for (int s2 = 1; s2 < NS; ++s2) {
+      const float* mb = smem + ((s2 - 1) * NR + rb) * C::MERGE;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dq[d][v] += mb[(4 * d + v) * 64 + lane];
+    }
+  }
+  if (!row_ok) return;
+  float* dqp = a.dq + ((size_t)bh * a.Sq + row) * DQK + 4 * g;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) {
+    float4 cur = *(const float4*)(dqp + 16 * d);
+    cur.x = fmaf(a.scale, dq[d][0], cur.x);
+    cur.y = fmaf(a.scale, dq[d][1], cur.y);
+    cur.z = fmaf(a.scale, dq[d][2], cur.z);
+    cur.w = fmaf(a.scale, dq[d][3], cur.w);
+    *(float4*)(dqp + 16 * d) = cur;
   }
 }
 
 // ---- dK, dV ---------------------------------------------------------------------------
-// One 32-key tile of one (batch, KV head): dK, dV of its keys summed over the group's
-// query heads and the query tiles (32 rows) that see them, added into the
-// accumulators. The workgroup's two halves of 256 threads walk alternate (head,
-// query tile) pairs, each with its own Q / dO / P / dS tiles, and add their sums
-// through LDS at the end.
 template <int DQK, int DV>
-struct F32KvSmem {
-  using C = F32BCfg<DQK, DV>;
-  // K and V rows; at the end, the second half's partial sums
-  float kv[C::BKEY * (C::KS + C::VS)];
-  float q[2][C::BQK * C::QS];
-  float o[2][C::BQK * C::OS];
-  float p[2][C::BQK * C::PS2];
-  float ds[2][C::BQK * C::PS2];
-  float l2[2][C::BQK];
-  float dl[2][C::BQK];
+struct F32DkvCfg {
+  static constexpr int NK = 2, NQS = 4;               // 16-key blocks x query streams
+  static constexpr int BKEY = 16 * NK, BQ = 16 * NQS; // keys per tile, query rows per query tile
+  static constexpr int QS = DQK + 4, OS = DV + 4;
+  static constexpr int Q_TILE = padded_tile_bytes(BQ, QS * 4) / 4;
+  static constexpr int O_TILE = padded_tile_bytes(BQ, OS * 4) / 4;
+  static constexpr int BUF = Q_TILE + O_TILE + 2 * BQ;   // Q, dO, LSE (log2 units), delta
+  static constexpr int KT = DQK / 16, VT = DV / 16;      // dK, dV output tiles of 16 columns
+  static constexpr int MERGE = 16 * (DQK + DV);          // one wave's dK, dV partial sums
+  static_assert(NK * NQS == 8, "eight waves");
+  static_assert(BQ == 64, "one wave loads a query tile's LSE and delta, one row per lane");
+  static_assert(2 * BUF * 4 <= 160 * 1024, "LDS");
+  static_assert((NQS - 1) * NK * MERGE <= 2 * BUF, "merge area");
 };
 
+// Key tile kt (BKEY keys) of one (batch, KV head): its dK, dV summed over the group's
+// query heads and the query tiles that see it, added into the accumulators.
 template <int DQK, int DV>
-__device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, int kt, F32KvSmem<DQK, DV>& sm) {
-  using C = F32BCfg<DQK, DV>;
-  constexpr int BQ = C::BQK, BKEY = C::BKEY, QS = C::QS, OS = C::OS, KS = C::KS, VS = C::VS, PS2 = C::PS2;
-  constexpr int T = C::THREADS;   // threads per half
-  constexpr int KK = C::KK, KVV = C::KVV;
-  static_assert(T * (KK + KVV) * 16 <= BKEY * (KS + VS) * 4, "partial sums fit the K / V area");
-  const int tid = threadIdx.x, half = tid / T, lt = tid % T;
+__device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int kvg, int kt, float* smem) {
+  using C = F32DkvCfg<DQK, DV>;
+  constexpr int NK = C::NK, NQS = C::NQS, BKEY = C::BKEY, BQ = C::BQ, QS = C::QS, OS = C::OS;
+  constexpr int KT = C::KT, VT = C::VT;
+  const int lane = threadIdx.x & 63, lm = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int kblk = wave % NK, qs = wave / NK;
   const int key_base = kt * BKEY;
   int q_first = 0;   // the first query that can see the tile's first key
   if (a.causal) {
     const long long f = a.k_pos0 + key_base - a.q_pos0;
     q_first = (int)max(0LL, min(f, (long long)a.Sq));
   }
-  if (q_first >= a.Sq) return;   // no query of the block sees these keys
-  const int qt0 = q_first / BQ;
-  const int nqt = (a.Sq + BQ - 1) / BQ - qt0;
+  if (q_first >= a.Sq) return;   // no query of the block sees these keys (workgroup-uniform)
+  const int nqt = (a.Sq - q_first + BQ - 1) / BQ;
   const int ntiles = a.group * nqt;   // (query head of the group, query tile) pairs
-  const int niter = (ntiles + 1) / 2; // half h takes pairs 2 i + h
 
-  float* ksm = sm.kv;
-  float* vsm = sm.kv + BKEY * KS;
-  float* qsm = sm.q[half];
-  float* osm = sm.o[half];
-  float* psm = sm.p[half];
-  float* dssm = sm.ds[half];
-  const size_t kvh = (size_t)(b * a.Hkv + g) * a.Sk;
-  __syncthreads();   // the previous tile's K, V and partial sums are consumed
-  for (int e = tid; e < BKEY * DQK / 4; e += 2 * T) {
-    const int rr = e / (DQK / 4), c4 = e % (DQK / 4), key = key_base + rr;
-    *(float4*)&ksm[rr * KS + 4 * c4] = key < a.Sk ? *(const float4*)((const float*)a.k + (kvh + key) * DQK + 4 * c4)
-                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int e = tid; e < BKEY * DV / 4; e += 2 * T) {
-    const int rr = e / (DV / 4), c4 = e % (DV / 4), key = key_base + rr;
-    *(float4*)&vsm[rr * VS + 4 * c4] = key < a.Sk ? *(const float4*)((const float*)a.v + (kvh + key) * DV + 4 * c4)
-                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-
-  // phase 1 (P, dS): keys kp, kp + 16 against rows rq, rq + 16, kp = t % 16,
-  // rq = t / 16. Phase 2: dK columns 4 (t % (DQK/4)) .. + 3 of keys KK (t / (DQK/4))
-  // .. + KK - 1, and dV likewise (t: the thread's index in its half).
-  const int kp = lt & 15, rq = lt >> 4;
-  const int cgk = lt % (DQK / 4), kgk = lt / (DQK / 4);
-  const int cgv = lt % (DV / 4), kgv = lt / (DV / 4);
-  const long long kpos_a = a.k_pos0 + key_base + kp;
-  const bool key_a_ok = key_base + kp < a.Sk, key_b_ok = key_base + kp + 16 < a.Sk;
-  float4 acck[KK], accv[KVV];
+  // stationary K and V of key lm of this wave's block (zero past the block)
+  const int key = key_base + 16 * kblk + lm;
+  const bool key_ok = key < a.Sk;
+  const size_t kvh = (size_t)(b * a.Hkv + kvg) * a.Sk;
+  float kreg[DQK / 4], vreg[DV / 4];
+  load_vec(kreg, (const float*)a.k + (kvh + key) * DQK + g * (DQK / 4), key_ok);
+  load_vec(vreg, (const float*)a.v + (kvh + key) * DV + g * (DV / 4), key_ok);
+  const long long kpos = a.k_pos0 + key;
+  const long long wk0 = a.k_pos0 + key_base + 16 * kblk;   // the wave's first key position
+  f32x4 dk[KT], dv[VT];
 #pragma unroll
-  for (int m = 0; m < KK; ++m) acck[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int t = 0; t < KT; ++t) dk[t] = f32x4{};
 #pragma unroll
-  for (int m = 0; m < KVV; ++m) accv[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int t = 0; t < VT; ++t) dv[t] = f32x4{};
 
-  // the half's next (head, query tile): rows and statistics fetched one step ahead
-  float4 qr[C::QCH2], orr[C::OCH2];
-  float l2n = kNegInf, dln = 0.f;
-  auto fetch = [&](int n) {
-    const int hq = g * a.group + n / nqt, row0 = (qt0 + n % nqt) * BQ;
-    const size_t bh = (size_t)b * a.Hq + hq;
-    load_rows<DQK, C::QCH2, T>(qr, (const float*)a.q + bh * a.Sq * DQK, row0, a.Sq, lt);
-    load_rows<DV, C::OCH2, T>(orr, (const float*)a.dout + bh * a.Sq * DV, row0, a.Sq, lt);
-    if (lt < BQ) {
-      // -LSE * log2(e) of each row (-inf past the block or with no visible key: P = 0)
-      const int row = row0 + lt;
-      l2n = kNegInf;
-      dln = 0.f;
-      if (row < a.Sq) {
-        const float l = a.lse[bh * a.Sq + row];
-        if (l != kNegInf) l2n = -l * kLog2e;
-        dln = a.delta[bh * a.Sq + row];
-      }
+  PaddedTileDma<BQ, DQK * 4, QS * 4, 8> qpad;
+  PaddedTileDma<BQ, DV * 4, OS * 4, 8> opad;
+  qpad.init(wave, lane);
+  opad.init(wave, lane);
+  const unsigned q_last = (unsigned)((size_t)a.Sq * DQK * 4 - 16), o_last = (unsigned)((size_t)a.Sq * DV * 4 - 16);
+  auto tile_rows = [&](int n, int& bh, int& r0) __attribute__((always_inline)) {
+    const int hh = n / nqt;
+    bh = b * a.Hq + kvg * a.group + hh;
+    r0 = q_first + (n - hh * nqt) * BQ;
+  };
+  auto dma = [&](int n, int buf) __attribute__((always_inline)) {
+    int bh, r0;
+    tile_rows(n, bh, r0);
+    float* base = smem + buf * C::BUF;
+    qpad.issue(wave, lds_addr(base), (unsigned)r0 * (DQK * 4), q_last,
+               raw_desc((const float*)a.q + (size_t)bh * a.Sq * DQK, (unsigned)((size_t)a.Sq * DQK * 4)));
+    opad.issue(wave, lds_addr(base + C::Q_TILE), (unsigned)r0 * (DV * 4), o_last,
+               raw_desc((const float*)a.dout + (size_t)bh * a.Sq * DV, (unsigned)((size_t)a.Sq * DV * 4)));
+  };
+  // LSE (log2 units; +inf past the block or for a row with no visible key, so P = 0)
+  // and delta of the tile's rows: wave 0, one row per lane
+  auto stats = [&](int n, float& l2, float& dl) __attribute__((always_inline)) {
+    int bh, r0;
+    tile_rows(n, bh, r0);
+    const int r = r0 + lane;
+    l2 = __builtin_huge_valf();
+    dl = 0.f;
+    if (r < a.Sq) {
+      const float l = a.lse[(size_t)bh * a.Sq + r];
+      if (l != kNegInf) l2 = l * kLog2e;
+      dl = a.delta[(size_t)bh * a.Sq + r];
     }
   };
-  if (half < ntiles) fetch(half);
-  for (int it = 0; it < niter; ++it) {
-    const int n = 2 * it + half;
-    const bool active = n < ntiles;   // the second half idles on an odd count's last step
-    const int row0 = (qt0 + n % nqt) * BQ;
-    __syncthreads();   // the previous pair's rows, P and dS are consumed
-    if (active) {
-      store_rows<DQK, C::QCH2, T, QS>(qr, qsm, lt);
-      store_rows<DV, C::OCH2, T, OS>(orr, osm, lt);
-      if (lt < BQ) {
-        sm.l2[half][lt] = l2n;
-        sm.dl[half][lt] = dln;
-      }
+  auto put_stats = [&](int buf, float l2, float dl) __attribute__((always_inline)) {
+    float* st = smem + buf * C::BUF + C::Q_TILE + C::O_TILE;
+    st[lane] = l2;
+    st[BQ + lane] = dl;
+  };
+
+  __syncthreads();   // the previous key tile's buffers and partial sums are consumed
+  dma(0, 0);
+  if (wave == 0) {
+    float l2, dl;
+    stats(0, l2, dl);
+    put_stats(0, l2, dl);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    float l2n = 0.f, dln = 0.f;
+    if (n + 1 < ntiles) {
+      dma(n + 1, buf ^ 1);
+      if (wave == 0) stats(n + 1, l2n, dln);
     }
-    __syncthreads();   // the pair's rows and statistics (and the K, V rows) are in LDS
-    if (n + 2 < ntiles) fetch(n + 2);   // lands while this pair is computed
-    if (active) {
-      float s00 = 0.f, s01 = 0.f, s10 = 0.f, s11 = 0.f;   // s[row][key]
-#pragma unroll 4
-      for (int d4 = 0; d4 < DQK / 4; ++d4) {
-        const float4 k0 = lds4(&ksm[kp * KS + 4 * d4]), k1 = lds4(&ksm[(kp + 16) * KS + 4 * d4]);
-        const float4 q0 = lds4(&qsm[rq * QS + 4 * d4]), q1 = lds4(&qsm[(rq + 16) * QS + 4 * d4]);
-        s00 = dot4(q0, k0, s00);
-        s01 = dot4(q0, k1, s01);
-        s10 = dot4(q1, k0, s10);
-        s11 = dot4(q1, k1, s11);
-      }
-      float p00 = 0.f, p01 = 0.f, p10 = 0.f, p11 = 0.f;   // dP[row][key]
-#pragma unroll 4
-      for (int d4 = 0; d4 < DV / 4; ++d4) {
-        const float4 v0 = lds4(&vsm[kp * VS + 4 * d4]), v1 = lds4(&vsm[(kp + 16) * VS + 4 * d4]);
-        const float4 o0 = lds4(&osm[rq * OS + 4 * d4]), o1 = lds4(&osm[(rq + 16) * OS + 4 * d4]);
-        p00 = dot4(o0, v0, p00);
-        p01 = dot4(o0, v1, p01);
-        p10 = dot4(o1, v0, p10);
-        p11 = dot4(o1, v1, p11);
-      }
-      const long long qpos = a.q_pos0 + row0 + rq;
-      const float l0 = sm.l2[half][rq], l1 = sm.l2[half][rq + 16];
-      const float dl0 = sm.dl[half][rq], dl1 = sm.dl[half][rq + 16];
-      auto prob = [&](float sv, bool ok, long long kpos, long long qp, float l) {
-        return ok && (!a.causal || kpos <= qp) ? exp2_hw(fmaf(sv, a.scale_log2, l)) : 0.f;
-      };
-      const float pa0 = prob(s00, key_a_ok, kpos_a, qpos, l0), pb0 = prob(s01, key_b_ok, kpos_a + 16, qpos, l0);
-      const float pa1 = prob(s10, key_a_ok, kpos_a, qpos + 16, l1);
-      const float pb1 = prob(s11, key_b_ok, kpos_a + 16, qpos + 16, l1);
-      psm[rq * PS2 + kp] = pa0;
-      psm[rq * PS2 + kp + 16] = pb0;
-      psm[(rq + 16) * PS2 + kp] = pa1;
-      psm[(rq + 16) * PS2 + kp + 16] = pb1;
-      dssm[rq * PS2 + kp] = pa0 * (p00 - dl0);
-      dssm[rq * PS2 + kp + 16] = pb0 * (p01 - dl0);
-      dssm[(rq + 16) * PS2 + kp] = pa1 * (p10 - dl1);
-      dssm[(rq + 16) * PS2 + kp + 16] = pb1 * (p11 - dl1);
-    }
-    __syncthreads();   // P and dS of the pair are in LDS
-    if (active) {
-#pragma unroll 2
-      for (int rr = 0; rr < BQ; ++rr) {
-        float ds[KK], p[KVV];
-        lds_n<KK>(ds, &dssm[rr * PS2 + KK * kgk]);
-        lds_n<KVV>(p, &psm[rr * PS2 + KVV * kgv]);
-        const float4 qx = lds4(&qsm[rr * QS + 4 * cgk]);
-        const float4 ox = lds4(&osm[rr * OS + 4 * cgv]);
+    int bh, r0;
+    tile_rows(n, bh, r0);
+    const int rs = 16 * qs;                          // this stream's rows of the tile
+    const long long qp0 = a.q_pos0 + r0 + rs;        // their first position
+    bool skip = r0 + rs >= a.Sq;
+    if (a.causal) skip = skip || qp0 + 15 < wk0;
+    const bool need_mask = a.causal && qp0 < wk0 + 15;
+    if (!skip) {
+      const float* base = smem + buf * C::BUF;
+      const float* qt = base;
+      const float* ot = base + C::Q_TILE;
+      const float* st = base + C::Q_TILE + C::O_TILE;
+      // S and dP: lane holds key lm against rows rs + 4 g + v
+      const f32x4 s = chain(qt + (rs + lm) * QS + g * (DQK / 4), kreg, f32x4{});
+      const f32x4 dp = chain(ot + (rs + lm) * OS + g * (DV / 4), vreg, f32x4{});
+      const float4 l4 = *(const float4*)(st + rs + 4 * g);
+      const float4 d4 = *(const float4*)(st + BQ + rs + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      float p[4], ds[4];
 #pragma unroll
-        for (int m = 0; m < KK; ++m) axpy4(ds[m], qx, acck[m]);
+      for (int v = 0; v < 4; ++v) {
+        const bool vis = !need_mask || kpos <= qp0 + 4 * g + v;
+        p[v] = vis ? exp2_hw(fmaf(s[v], a.scale_log2, -lv[v])) : 0.f;
+        ds[v] = p[v] * (dp[v] - dv4[v]);
+      }
+      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS: product t takes row rs + 4 g + t
+      const float* oc = ot + (rs + 4 * g) * OS + lm;
+      const float* qc = qt + (rs + 4 * g) * QS + lm;
 #pragma unroll
-        for (int m = 0; m < KVV; ++m) axpy4(p[m], ox, accv[m]);
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int d = 0; d < VT; ++d) dv[d] = mma16_f32(oc[t * OS + 16 * d], p[t], dv[d]);
+#pragma unroll
+        for (int d = 0; d < KT; ++d) dk[d] = mma16_f32(qc[t * QS + 16 * d], ds[t], dk[d]);
       }
     }
+    if (wave == 0 && n + 1 < ntiles) put_stats(buf ^ 1, l2n, dln);
+    wait_vmem();   // this wave's loads of tile n + 1 have landed
+    __syncthreads();
   }
 
-  // the second half's sums join the first half's through the K / V area
-  float4* red = (float4*)sm.kv;
-  __syncthreads();   // every read of K and V is done
-  if (half == 1) {
+  // the query streams' sums meet in LDS (the tile buffers are free after the last barrier)
+  if (qs > 0) {
+    float* mb = smem + ((qs - 1) * NK + kblk) * C::MERGE;
 #pragma unroll
-    for (int m = 0; m < KK; ++m) red[m * T + lt] = acck[m];
+    for (int d = 0; d < KT; ++d)
 #pragma unroll
-    for (int m = 0; m < KVV; ++m) red[(KK + m) * T + lt] = accv[m];
+      for (int v = 0; v < 4; ++v) mb[(4 * d + v) * 64 + lane] = dk[d][v];
+#pragma unroll
+    for (int d = 0; d < VT; ++d)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mb[(4 * (KT + d) + v) * 64 + lane] = dv[d][v];
   }
   __syncthreads();
-  if (half == 0) {
+  if (qs > 0 || !key_ok) return;
 #pragma unroll
-    for (int m = 0; m < KK; ++m) {
-      const int key = key_base + KK * kgk + m;
-      if (key < a.Sk) {
-        const float4 o2 = red[m * T + lt];
-        float4 sum = acck[m];
-        sum.x += o2.x;
-        sum.y += o2.y;
-        sum.z += o2.z;
-        sum.w += o2.w;
-        float* dkp = a.dk + (kvh + key) * DQK + 4 * cgk;
-        float4 cur = *(const float4*)dkp;
-        axpy4(a.scale, sum, cur);
-        *(float4*)dkp = cur;
-      }
-    }
+  for (int s2 = 1; s2 < NQS; ++s2) {
+    const float* mb = smem + ((s2 - 1) * NK + kblk) * C::MERGE;
 #pragma unroll
-    for (int m = 0; m < KVV; ++m) {
-      const int key = key_base + KVV * kgv + m;
-      if (key < a.Sk) {
-        const float4 o2 = red[(KK + m) * T + lt];
-        float* dvp = a.dv + (kvh + key) * DV + 4 * cgv;
-        float4 cur = *(const float4*)dvp;
-        cur.x += accv[m].x + o2.x;
-        cur.y += accv[m].y + o2.y;
-        cur.z += accv[m].z + o2.z;
-        cur.w += accv[m].w + o2.w;
-        *(float4*)dvp = cur;
-      }
-    }
+    for (int d = 0; d < KT; ++d)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dk[d][v] += mb[(4 * d + v) * 64 + lane];
+#pragma unroll
+    for (int d = 0; d < VT; ++d)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dv[d][v] += mb[(4 * (KT + d) + v) * 64 + lane];
+  }
+  float* dkp = a.dk + (kvh + key) * DQK + 4 * g;
+#pragma unroll
+  for (int d = 0; d < KT; ++d) {
+    float4 cur = *(const float4*)(dkp + 16 * d);
+    cur.x = fmaf(a.scale, dk[d][0], cur.x);
+    cur.y = fmaf(a.scale, dk[d][1], cur.y);
+    cur.z = fmaf(a.scale, dk[d][2], cur.z);
+    cur.w = fmaf(a.scale, dk[d][3], cur.w);
+    *(float4*)(dkp + 16 * d) = cur;
+  }
+  float* dvp = a.dv + (kvh + key) * DV + 4 * g;
+#pragma unroll
+  for (int d = 0; d < VT; ++d) {
+    float4 cur = *(const float4*)(dvp + 16 * d);
+    cur.x += dv[d][0];
+    cur.y += dv[d][1];
+    cur.z += dv[d][2];
+    cur.w += dv[d][3];
+    *(float4*)(dvp + 16 * d) = cur;
   }
 }
 
@@ -493,19 +437,16 @@ __device__ __forceinline__ void dkdv_f32_tile(const BwdArgs& a, int b, int g, in
 // (heaviest) tile. Without a mask every tile has the same work and a workgroup
 // takes one.
 template <int DQK, int DV>
-// Two waves per SIMD: one workgroup per CU, with the registers to keep more LDS
-// reads in flight (at D = 128 the compiler otherwise holds the kernel to the 128
-// registers of two workgroups per CU and serialises the reads).
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_f32_kernel(BwdArgs a) {
-  using C = F32BCfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) F32KvSmem<DQK, DV> sm;
+  using C = F32DkvCfg<DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) float smem[2 * C::BUF];
   const int nkt = (a.Sk + C::BKEY - 1) / C::BKEY;
   const int kt = (int)(blockIdx.x % a.n_tiles);   // a.n_tiles: ceil(nkt / 2) causal, nkt otherwise
   const int bg = blockIdx.x / a.n_tiles;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  dkdv_f32_tile<DQK, DV>(a, b, g, kt, sm);
-  if (a.causal && nkt - 1 - kt != kt) dkdv_f32_tile<DQK, DV>(a, b, g, nkt - 1 - kt, sm);
+  dkdv_f32_tile<DQK, DV>(a, b, g, kt, smem);
+  if (a.causal && nkt - 1 - kt != kt) dkdv_f32_tile<DQK, DV>(a, b, g, nkt - 1 - kt, smem);
 }
 
 // ---- launchers ------------------------------------------------------------------------
@@ -519,28 +460,20 @@ hipError_t bwd_delta_f32(const float* o, const float* dout, float* delta, long l
 
 template <int DQK, int DV>
 static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
-  using C = F32BCfg<DQK, DV>;
+  using CK = F32DkvCfg<DQK, DV>;
+  using CQ = F32DqCfg<DQK, DV>;
   BwdArgs b = a;
-  const int nkt = (a.Sk + C::BKEY - 1) / C::BKEY;
+  const int nkt = (a.Sk + CK::BKEY - 1) / CK::BKEY;
   b.n_tiles = a.causal ? (nkt + 1) / 2 : nkt;   // causal: pairs of key tiles
   long long grid = (long long)a.B * a.Hkv * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (grid > 0)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(2 * C::THREADS), 0, st, b);
+  if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(512), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 32-row dQ workgroups (two rows per thread), or 16-row ones when there are fewer
-  // 32-row workgroups than CUs
-  const bool two_rows = (long long)a.B * a.Hq * ((a.Sq + 31) / 32) >= 256;
-  b.n_tiles = two_rows ? (a.Sq + 31) / 32 : (a.Sq + 15) / 16;
+  b.n_tiles = (a.Sq + CQ::BQ - 1) / CQ::BQ;
   grid = (long long)a.B * a.Hq * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (grid > 0) {
-    if (two_rows)
-      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 2>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
-    else
-      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 1>), dim3((unsigned)grid), dim3(C::THREADS), 0, st, b);
-  }
+  if (grid > 0) hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(512), 0, st, b);
   return hipGetLastError();
 }
 
