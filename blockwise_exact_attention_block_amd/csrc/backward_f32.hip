@@ -20,7 +20,8 @@
 // Three kernels:
 //   * bwd_delta_f32_kernel: delta per query row, 16 lanes per row.
 //   * bwd_dq_f32_kernel (8 waves): 64 query rows of one (batch, head) = 4 row blocks
-//     x 2 key streams; K / V tiles of 32 keys go from HBM into LDS (direct loads,
+//     x 2 key streams (32 rows = 2 x 4 in launches of fewer 64-row workgroups than
+//     CUs); K / V tiles of 16 keys per stream go from HBM into LDS (direct loads,
 //     double-buffered). A wave keeps its 16 rows' Q and dO stationary, forms
 //     Sᵀ = K Qᵀ and dPᵀ = V dOᵀ for 16 keys (lane: row L % 16, keys 4 g + v), P and
 //     dS in registers, then dQᵀ += Kᵀ dSᵀ with the lane's dS values as the B operand
@@ -94,9 +95,9 @@ __device__ __forceinline__ f32x4 chain(const float* lds, const float (&b)[N], f3
 }
 
 // ---- dQ -------------------------------------------------------------------------------
-template <int DQK, int DV>
+template <int DQK, int DV, int NR_>
 struct F32DqCfg {
-  static constexpr int NR = 4, NS = 2;                // 16-row blocks x key streams
+  static constexpr int NR = NR_, NS = 8 / NR_;        // 16-row blocks x key streams
   static constexpr int BQ = 16 * NR, BK = 16 * NS;    // query rows per workgroup, keys per tile
   static constexpr int KS = DQK + 4, VS = DV + 4;
   static constexpr int K_TILE = padded_tile_bytes(BK, KS * 4) / 4;   // floats per buffer
@@ -107,10 +108,10 @@ struct F32DqCfg {
   static_assert((NS - 1) * NR * MERGE <= 2 * (K_TILE + V_TILE), "merge area");
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NR_>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_f32_kernel(BwdArgs a) {
-  using C = F32DqCfg<DQK, DV>;
+  using C = F32DqCfg<DQK, DV, NR_>;
   constexpr int NR = C::NR, NS = C::NS, BQ = C::BQ, BK = C::BK, KS = C::KS, VS = C::VS, DT = C::DT;
   __shared__ __attribute__((aligned(1024))) float smem[2 * (C::K_TILE + C::V_TILE)];
   const int lane = threadIdx.x & 63, lm = lane & 15, g = lane >> 4;
@@ -461,7 +462,7 @@ hipError_t bwd_delta_f32(const float* o, const float* dout, float* delta, long l
 template <int DQK, int DV>
 static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
   using CK = F32DkvCfg<DQK, DV>;
-  using CQ = F32DqCfg<DQK, DV>;
+  using CQ = F32DqCfg<DQK, DV, 4>;
   BwdArgs b = a;
   const int nkt = (a.Sk + CK::BKEY - 1) / CK::BKEY;
   b.n_tiles = a.causal ? (nkt + 1) / 2 : nkt;   // causal: pairs of key tiles
@@ -470,10 +471,20 @@ static hipError_t bwd_f32_launch(BwdArgs a, hipStream_t st) {
   if (grid > 0) hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(512), 0, st, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  b.n_tiles = (a.Sq + CQ::BQ - 1) / CQ::BQ;
+  // 64-row dQ workgroups (4 row blocks x 2 key streams), or 32-row ones (2 x 4) when
+  // there are fewer 64-row workgroups than CUs (measured on one head of 1024 rows:
+  // 86 against 112 us for the whole step; slightly slower on large launches)
+  const bool wide = (long long)a.B * a.Hq * ((a.Sq + CQ::BQ - 1) / CQ::BQ) >= 256;
+  const int bq = wide ? CQ::BQ : CQ::BQ / 2;
+  b.n_tiles = (a.Sq + bq - 1) / bq;
   grid = (long long)a.B * a.Hq * b.n_tiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (grid > 0) hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV>), dim3((unsigned)grid), dim3(512), 0, st, b);
+  if (grid > 0) {
+    if (wide)
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 4>), dim3((unsigned)grid), dim3(512), 0, st, b);
+    else
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DQK, DV, 2>), dim3((unsigned)grid), dim3(512), 0, st, b);
+  }
   return hipGetLastError();
 }
 

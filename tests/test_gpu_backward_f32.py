@@ -86,14 +86,14 @@ def test_f32_bwd_step_against_oracle(ra, dims, causal, q_pos0, k_pos0, Sq, Sk):
 
 @pytest.mark.parametrize("dims", DIMS)
 @pytest.mark.parametrize("causal,q_pos0,k_pos0", [(False, 0, 0), (True, 900, 0), (True, 100, 180)])
-def test_f32_bwd_step_two_row_dq(ra, dims, causal, q_pos0, k_pos0):
-    """A launch of at least 256 32-row dQ workgroups takes two query rows per thread
-    (the cases above have fewer and take one): 2 x 8 heads x 1040 rows (33 ragged
-    32-row tiles), 300 keys."""
+def test_f32_bwd_step_wide_dq(ra, dims, causal, q_pos0, k_pos0):
+    """A launch of at least 256 64-row dQ workgroups takes them (4 row blocks x 2 key
+    streams; the cases above have fewer and take 32-row ones): 2 x 8 heads x 1040
+    rows (17 tiles, the last ragged), 300 keys."""
     B, Hq, Hkv, Sq, Sk = 2, 8, 2, 1040, 300
     D, Dv = dims
-    assert B * Hq * ((Sq + 31) // 32) >= 256
-    say(f"block_attn_bwd_step f32 two-row dQ D{D}/{Dv} causal={causal} q_pos0={q_pos0} k_pos0={k_pos0}")
+    assert B * Hq * ((Sq + 63) // 64) >= 256
+    say(f"block_attn_bwd_step f32 wide dQ D{D}/{Dv} causal={causal} q_pos0={q_pos0} k_pos0={k_pos0}")
     q, k, v = prefill_inputs_np(B, Hq, Hkv, Sq, Sk, D, Dv, seed=1540 + D + Dv + q_pos0, dtype="f32")
     do = randn_np((B, Hq, Sq, Dv), 1640 + D + Dv, "f32")
     scale = 1 / math.sqrt(D)
