@@ -251,7 +251,7 @@ int ra_attn_bwd_preprocess(int dtype, const void* o, const void* dout, long long
  * order, with dk_acc / dv_acc travelling with their block. Two launches (dK/dV,
  * then dQ) on the stream. Supported: RA_BF16 with (Dqk, Dv) in {(64,64),
  * (128,128), (192,128)} (matrix cores; P and dS rounded to bf16 for the products)
- * and RA_F32 with Dqk, Dv in {64, 128} (vector ALUs, fp32 throughout). Errors as
+ * and RA_F32 with Dqk, Dv in {64, 128} (fp32 matrix cores, fp32 throughout). Errors as
  * ra_block_attn_step. The accumulators must not overlap the inputs or each other. */
 int ra_block_attn_bwd_step(int dtype, const void* q, const void* dout, const float* lse, const float* delta,
                            long long q_pos0, int Sq, const void* k_blk, const void* v_blk, long long k_pos0, int Sk,
