@@ -87,10 +87,11 @@ struct F32Cfg {
   static constexpr int THREADS = 512;
   static constexpr int BQ = M * NR, BK = M * NS;    // query rows, keys per tile
   // padded LDS rows (floats): 16 consecutive K rows start 4 banks apart, so the
-  // 16-byte reads of a quarter wave (16 rows, same columns) are conflict-free; V
-  // rows 4 apart start 32 banks apart, so the 32-bit reads of the lane groups
-  // (rows 4 g + const, M consecutive columns) of a half wave hit distinct banks
-  static constexpr int KS = DQK + 4, VS = DV + 8;
+  // 16-byte reads of a quarter wave (16 rows, same columns) are conflict-free. The
+  // 32-bit V reads of a wave take M consecutive columns in each of G rows 4 apart
+  // (rows 4 g + const): rows 4 apart start 32 banks apart when M = 32 and 16 banks
+  // apart when M = 16, so the wave's 64 reads hit 64 distinct banks
+  static constexpr int KS = DQK + 4, VS = DV + (M == 32 ? 8 : 4);
   static constexpr int K_TILE = padded_tile_bytes(BK, KS * 4) / 4;   // floats per buffer
   static constexpr int V_TILE = padded_tile_bytes(BK, VS * 4) / 4;
   static constexpr int DS = DQK / G;      // score products per sub-block

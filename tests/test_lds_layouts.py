@@ -13,8 +13,9 @@ against two properties:
     conflicted, which the counters showed as 38-40 % of LDS-active cycles.
 The layouts checked: the prefill's XOR-swizzled 256-byte rows (prefill_bf16.hip,
 D = 128, and V at D_qk = 192), its 384-byte K rows at D_qk = 192, its padded rows
-at D = 64, and the backward's (D + 8)-element rows read in the perm16 row order
-(backward_bf16.hip)."""
+at D = 64, the backward's (D + 8)-element rows read in the perm16 row order
+(backward_bf16.hip), and the fp32 kernels' padded rows (prefill_f32.hip,
+backward_f32.hip), whose 4-byte operand reads are served 64 lanes per pass."""
 import pytest
 
 
@@ -86,6 +87,10 @@ def padded_tile_dma_map(rows, row_bytes, stride, nw):
     (96, 384, 400),                      # a tile that is not whole KB (37.5 KB): slack
     (128, 256, 272),                     # dQ kernel D = 128: K and V
     (64, 256, 272), (64, 128, 144),      # dK/dV kernel Q and dO, D = 128 and 64
+    # fp32 kernels (4-byte elements): prefill 32 x 32 shape, K and V at D = 128 and 64
+    (64, 512, 528), (64, 512, 544), (128, 256, 272), (128, 256, 288),
+    # prefill 16 x 16 shape (V padded by 4), backward dQ tiles and dK/dV query tiles
+    (128, 256, 272), (32, 512, 528), (64, 512, 528),
 ])
 def test_padded_tile_dma_places_every_chunk(rows, row_bytes, stride):
     """Every 16-byte chunk of every row lands at its row's LDS offset."""
@@ -214,3 +219,49 @@ def test_backward_mask_offsets_match_perm16():
         for i in range(16):
             rho = 8 * (i >> 2) + 4 * h + (i & 3)
             assert perm16(rho) == 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1) + h
+
+
+# ---- fp32 kernels: rows padded by 4 floats (V by 8 with 32 x 32 products) --------
+
+def f32_row_read_passes(M, stride, d):
+    """16-byte operand reads of the fp32 products: lane L reads floats g d / G + 4 c
+    .. + 3 of row L % M (G = 64 / M lane groups, g = L / M); passes of 16 lanes."""
+    G = 64 // M
+    for c in range(d // G // 4):
+        for p in range(4):
+            yield [4 * ((lane % M) * stride + (lane // M) * (d // G) + 4 * c) for lane in range(16 * p, 16 * p + 16)]
+
+
+def f32_col_read_lanes(M, stride, d, step):
+    """4-byte operand reads of the second products: lane L reads column L % M (+ M
+    per output tile) of row 4 (L / M) + (step / 4) 4 G + step % 4; one pass of 64."""
+    G = 64 // M
+    for mt in range(d // M):
+        row = lambda lane: 4 * (lane // M) + (step >> 2) * 4 * G + (step & 3)
+        yield [4 * (row(lane) * stride + lane % M + M * mt) for lane in range(64)]
+
+
+@pytest.mark.parametrize("M", [32, 16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_prefill_reads_are_conflict_free(M, d):
+    ks, vs = d + 4, d + (8 if M == 32 else 4)
+    assert max(banks_max(p, 16) for p in f32_row_read_passes(M, ks, d)) == 1
+    for step in range(M * M // 64):
+        assert max(banks_max(p, 4) for p in f32_col_read_lanes(M, vs, d, step)) == 1
+
+
+def test_f32_prefill_v_padding_must_follow_the_shape():
+    """Rows padded by 8 with 16 x 16 products (lane groups 32 banks apart, four of
+    them) or by 4 with 32 x 32 ones (two groups 16 banks apart, 32 columns each)
+    would be 2-way conflicted."""
+    assert max(banks_max(p, 4) for p in f32_col_read_lanes(16, 136, 128, 0)) == 2
+    assert max(banks_max(p, 4) for p in f32_col_read_lanes(32, 132, 128, 0)) == 2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_backward_reads_are_conflict_free(d):
+    """backward_f32.hip: 16 x 16 products only, every tile padded by 4 floats; the
+    16-byte reads (S, dP) and the 4-byte reads (dQ from K; dV, dK from dO and Q)."""
+    assert max(banks_max(p, 16) for p in f32_row_read_passes(16, d + 4, d)) == 1
+    for step in range(4):
+        assert max(banks_max(p, 4) for p in f32_col_read_lanes(16, d + 4, d, step)) == 1
