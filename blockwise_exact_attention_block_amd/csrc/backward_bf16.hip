@@ -15,9 +15,10 @@
 //
 // Three kernels:
 //   * bwd_delta_kernel: delta = rowsum(dO o O) per query row.
-//   * Scores are exact fp32 products of the bf16 inputs; P = exp2(scale * log2(e) * s
+//   * Scores are fp32 products of the bf16 inputs; P = exp2(scale * log2(e) * s
 //     - LSE * log2(e)). The dP products start from -delta (their C operand), so they
-//     come out as dP - delta.
+//     come out as dP - delta. In the dK/dV kernel the S products likewise start from
+//     -LSE / scale, so P = exp2(scale * log2(e) * (S - LSE / scale)).
 //   * bwd_dq_kernel: one workgroup per 256 query rows of one (batch, head), 8 waves
 //     of 32 rows. Q and dO rows stay in VGPRs as B operands (lane = query column;
 //     at D_qk = 192 the dO rows wait in a lane-private LDS area instead); K and V
@@ -31,7 +32,8 @@
 //     dP = dO V^T (lane = key column; at D_qk = 192 the K rows wait in a
 //     lane-private LDS area instead). dV^T += dO^T P and dK^T += Q^T dS take dO^T
 //     and Q^T through ds_read_b64_tr_b16. Rows past the query block carry
-//     LSE = +inf, so their P and dS are exactly 0 with no row mask.
+//     LSE = +inf (their S products start from -inf), so their P and dS are
+//     exactly 0 with no row mask.
 #include "common.hpp"
 
 namespace ra {
@@ -423,7 +425,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   // Q / dO tiles go straight from HBM into the padded LDS rows (rows past the block
   // re-read the slab's last 16 bytes: finite values whose P is 0); the rows' LSE and
   // delta go through a register of threads 0..127
-  float rowv = 0.f;   // threads 0..63: -LSE * log2(e) of a row; 64..127: -delta
+  float rowv = 0.f;   // threads 0..BQ-1: -LSE / scale of a row; BQ..2BQ-1: -delta
   static_assert(C::THREADS >= 2 * BQ, "threads 0 .. 2 BQ - 1 carry the rows' LSE and delta");
   PaddedTileDma<BQ, DQK * 2, QS * 2, NW> qdma;
   PaddedTileDma<BQ, DV * 2, OS * 2, NW> odma;
@@ -442,7 +444,7 @@ bwd_dkdv_kernel(BwdArgs a) {
         rowv = kNegInf;   // rows past the block, or with no visible key: P = 0
         if (r < a.Sq) {
           const float l = a.lse[bh * a.Sq + r];
-          if (l != kNegInf) rowv = -l * kLog2e;
+          if (l != kNegInf) rowv = -l / a.scale;
         }
       } else {
         rowv = r < a.Sq ? -a.delta[bh * a.Sq + r] : 0.f;
@@ -469,15 +471,23 @@ bwd_dkdv_kernel(BwdArgs a) {
       const bool need_mask = a.causal && qpos_s < wave_kpos0 + 31;
       const int qrow = qs * 32 + perm16(l32);   // the query of accumulator row l32
       // S = Q K^T and dP = dO V^T: lane = key column, accumulator rows 8*(i/4) + 4*h +
-      // i%4 (their queries at perm16 of that). dP starts from the rows' -delta, so it
-      // comes out as dP - delta.
-      f32x16 st = f32x16{}, dpt;
+      // i%4 (their queries at perm16 of that). S starts from the rows' -LSE / scale
+      // and dP from their -delta, so they come out as S - LSE / scale and dP - delta:
+      // P = exp2(scale * log2(e) * (S - LSE / scale)) needs one multiply per score,
+      // and the rows' LSE is read before the products instead of between them and
+      // the exps. The offset costs the fp32 accumulation a few ulps of |S - LSE /
+      // scale|, far below the bf16 rounding of P.
+      f32x16 st, dpt;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
+        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
+        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
         const f32x4 d0 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 4 * h];
         const f32x4 d1 = *(const f32x4*)&dsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          st[8 * t2 + e] = l0[e];
+          st[8 * t2 + 4 + e] = l1[e];
           dpt[8 * t2 + e] = d0[e];
           dpt[8 * t2 + 4 + e] = d1[e];
         }
@@ -504,14 +514,11 @@ bwd_dkdv_kernel(BwdArgs a) {
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        // the rows' -LSE * log2(e)
-        const f32x4 l0 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 4 * h];
-        const f32x4 l1 = *(const f32x4*)&lsm[buf][qs * 32 + 16 * t2 + 8 + 4 * h];
         f32x8 p, ds;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * t2 + e;
-          p[e] = exp2_hw(fmaf(st[i], a.scale_log2, e < 4 ? l0[e] : l1[e - 4]));
+          p[e] = exp2_hw(st[i] * a.scale_log2);
           ds[e] = p[e] * dpt[i];
         }
         pb[t2] = to_bf16x8(p);
